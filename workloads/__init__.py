@@ -1,0 +1,220 @@
+"""Seeded synthetic inputs for the paged decode path.
+
+This module is shared by the test suite, the benchmark and the smoke check.
+It draws random numbers and builds input *structure* (sequence lengths,
+shuffled physical block ids, block tables, slot lists for given positions,
+pool contents); it holds none of the attention or block-manager arithmetic.
+
+Workloads are shaped after the setups on the pages (OPT-13B / 66B and
+LLaMA-13B models, request lengths drawn from a distribution rather than a
+dataset); no dataset item is reproduced.  Values are N(0, 1) drawn in fp32 and
+rounded to the storage dtype (round-to-nearest-even).
+
+Pool layout (shapes only; the index formula is documented in include/pa.h):
+  K: [num_blocks][Hkv][BS][D]
+  V: [num_blocks][Hkv][BS/VS][D][VS],  VS = min(BS, 16)
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+def v_slab(block_size: int) -> int:
+    return block_size if block_size < 16 else 16
+
+
+def k_pool_shape(num_blocks, num_kv_heads, block_size, head_dim):
+    return (num_blocks, num_kv_heads, block_size, head_dim)
+
+
+def v_pool_shape(num_blocks, num_kv_heads, block_size, head_dim):
+    vs = v_slab(block_size)
+    return (num_blocks, num_kv_heads, block_size // vs, head_dim, vs)
+
+
+@dataclass(frozen=True)
+class Spec:
+    """One workload family.  ``lengths`` is (kind, *params)."""
+    name: str
+    dtype: str
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    num_seqs: int
+    lengths: tuple
+    pool_factor: float = 1.25
+    pool_blocks: int | None = None  # fixed pool size overrides pool_factor
+    partition_size: int = 0         # 0 = library default
+    seed: int = 118_000
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim)
+
+    def with_(self, **kw) -> "Spec":
+        d = dict(self.__dict__)
+        d.update(kw)
+        return Spec(**d)
+
+
+# The five workload families (the first is the tiny worked example).
+TINY = Spec("tiny", "f32", 2, 2, 16, 4, 2, ("fixed", (5, 9)), pool_blocks=8, seed=118_000)
+OPT13B = Spec("opt13b_decode", "f16", 40, 40, 128, 16, 64, ("lognormal", 350.0, 1.0, 16, 2048),
+              seed=118_001)
+LLAMA13B_SHARE = Spec("llama13b_prefix_share", "bf16", 40, 40, 128, 16, 256,
+                      ("share", 8, 512, 1, 512), seed=118_002)
+GQA_LONG = Spec("gqa_long", "bf16", 64, 8, 128, 32, 32, ("uniform", 16384, 32768),
+                partition_size=512, seed=118_003)
+OPT66B_SWEEP = Spec("opt66b_sweep", "f16", 72, 72, 128, 16, 128, ("uniform", 1, 8192),
+                    seed=118_004)
+SPECS = {s.name: s for s in (TINY, OPT13B, LLAMA13B_SHARE, GQA_LONG, OPT66B_SWEEP)}
+
+
+def draw_lengths(spec: Spec, rng: np.random.Generator) -> np.ndarray:
+    kind = spec.lengths[0]
+    if kind == "fixed":
+        lens = np.array(spec.lengths[1], dtype=np.int64)
+    elif kind == "lognormal":  # median m, sigma s, clipped to [lo, hi]
+        _, m, s, lo, hi = spec.lengths
+        z = rng.standard_normal(spec.num_seqs)
+        lens = np.clip(np.rint(np.exp(math.log(m) + s * z)), lo, hi).astype(np.int64)
+    elif kind == "uniform":  # inclusive integer range
+        _, lo, hi = spec.lengths
+        lens = rng.integers(lo, hi + 1, size=spec.num_seqs)
+    else:
+        raise ValueError(kind)
+    return lens.astype(np.int32)
+
+
+def blocks_needed(length: int, block_size: int) -> int:
+    return -(-int(length) // block_size)
+
+
+def shuffled_tables(lens, block_size, rng, pool_factor=1.25, num_blocks=None, max_blocks=None):
+    """Random block tables: each sequence gets ceil(L / BS) distinct physical
+    ids drawn from a shuffled pool of ``num_blocks`` (default pool_factor x the
+    blocks required).  Unused entries are -1."""
+    need = [blocks_needed(L, block_size) for L in lens]
+    total = int(sum(need))
+    if num_blocks is None:
+        num_blocks = max(1, int(math.ceil(pool_factor * total)))
+    if total > num_blocks:
+        raise ValueError("pool too small")
+    if max_blocks is None:
+        max_blocks = max(1, max(need) if need else 1)
+    perm = rng.permutation(num_blocks)
+    tables = np.full((len(lens), max_blocks), -1, dtype=np.int32)
+    cursor = 0
+    for i, n in enumerate(need):
+        tables[i, :n] = perm[cursor:cursor + n]
+        cursor += n
+    return tables, int(num_blocks)
+
+
+def slots_for_positions(tables: np.ndarray, seq_pos, block_size: int) -> np.ndarray:
+    """Slot of each (seq, position) pair: physical block * BS + offset."""
+    out = np.empty(len(seq_pos), dtype=np.int64)
+    for i, (s, p) in enumerate(seq_pos):
+        out[i] = int(tables[s, p // block_size]) * block_size + p % block_size
+    return out
+
+
+def randn(shape, dtype: str, gen: torch.Generator, device) -> torch.Tensor:
+    """N(0, 1) in fp32, rounded to ``dtype``; filled in chunks to bound memory."""
+    out = torch.empty(shape, dtype=TORCH_DTYPE[dtype], device=device)
+    flat = out.view(-1)
+    chunk = 1 << 26
+    for s in range(0, flat.numel(), chunk):
+        e = min(flat.numel(), s + chunk)
+        flat[s:e] = torch.randn(e - s, generator=gen, device=device, dtype=torch.float32)
+    return out
+
+
+def make_generator(seed: int, device) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    return g
+
+
+def poison_unused(k_cache, v_cache, tables, lens, block_size):
+    """Set every pool position that holds no valid token to NaN: blocks no
+    table references and the unfilled tail of each sequence's last block."""
+    nb = k_cache.shape[0]
+    used = np.zeros(nb, dtype=bool)
+    vs = v_slab(block_size)
+    for i, L in enumerate(lens):
+        n = blocks_needed(L, block_size)
+        used[tables[i, :n]] = True
+    unused = torch.from_numpy(np.nonzero(~used)[0]).to(k_cache.device)
+    if unused.numel():
+        k_cache[unused] = float("nan")
+        v_cache[unused] = float("nan")
+    for i, L in enumerate(lens):
+        n = blocks_needed(L, block_size)
+        if n == 0:
+            continue
+        blk = int(tables[i, n - 1])
+        for off in range(int(L) - (n - 1) * block_size, block_size):
+            k_cache[blk, :, off, :] = float("nan")
+            v_cache[blk, :, off // vs, :, off % vs] = float("nan")
+
+
+@dataclass
+class DecodeCase:
+    spec: Spec
+    lens: np.ndarray            # int32 [B]
+    tables: np.ndarray          # int32 [B][max_blocks], -1 padded
+    num_blocks: int
+    q: torch.Tensor             # [B][Hq][D]
+    k_cache: torch.Tensor       # K pool shape
+    v_cache: torch.Tensor       # V pool shape
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def max_context_len(self) -> int:
+        return int(self.lens.max()) if len(self.lens) else 0
+
+
+def make_decode_case(spec: Spec, device="cpu", poison=True, lens=None, seed=None,
+                     num_blocks=None) -> DecodeCase:
+    """Pool pre-filled with N(0, 1) K/V, random shuffled tables, random q."""
+    seed = spec.seed if seed is None else seed
+    rng = np.random.default_rng(seed)
+    if lens is None:
+        lens = draw_lengths(spec, rng)
+    lens = np.asarray(lens, dtype=np.int32)
+    if num_blocks is None:
+        num_blocks = spec.pool_blocks
+    tables, nb = shuffled_tables(lens, spec.block_size, rng, spec.pool_factor, num_blocks)
+    gen = make_generator(seed, device)
+    B, hq, hkv, D, bs = spec.num_seqs, spec.num_q_heads, spec.num_kv_heads, spec.head_dim, \
+        spec.block_size
+    B = len(lens)
+    q = randn((B, hq, D), spec.dtype, gen, device)
+    k = randn(k_pool_shape(nb, hkv, bs, D), spec.dtype, gen, device)
+    v = randn(v_pool_shape(nb, hkv, bs, D), spec.dtype, gen, device)
+    if poison:
+        poison_unused(k, v, tables, lens, bs)
+    return DecodeCase(spec, lens, tables, nb, q, k, v)
+
+
+def to_numpy_bits(t: torch.Tensor) -> np.ndarray:
+    """Host copy for the oracle: fp32 as float32, 16-bit types as uint16 bits."""
+    t = t.detach().contiguous().cpu()
+    if t.dtype == torch.float32:
+        return t.numpy()
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def new_token_rows(num_tokens, num_kv_heads, head_dim, dtype, gen, device):
+    """K and V rows [T][Hkv][D] for tokens about to be written."""
+    k = randn((num_tokens, num_kv_heads, head_dim), dtype, gen, device)
+    v = randn((num_tokens, num_kv_heads, head_dim), dtype, gen, device)
+    return k, v
