@@ -1,0 +1,396 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged decode hot path on one MI355X.
+
+One step = one decode iteration of a batch: write each sequence's new token
+into its slot (pa_reshape_and_cache), run copy-on-write block copies when the
+workload has shared tail blocks (pa_copy_blocks), then single-query paged
+attention over every sequence (pa_decode).  All inputs (pools, q, new rows,
+slots, tables, lengths, copy pairs) are resident in HBM before timing starts;
+the host block allocator's per-step cost is timed separately and reported.
+
+To keep the 256 MB last-level cache from serving re-reads, the pools are
+replicated and consecutive steps use different replicas (the working set of
+back-to-back steps is several GB).
+
+Prints one JSON line (see --help for workloads).  The metric is the KV bytes
+the decode must read (valid tokens only, K and V) per second of step time.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="opt13b_decode",
+                    choices=["opt13b_decode", "gqa_long", "llama13b_prefix_share",
+                             "opt66b_sweep"])
+    ap.add_argument("--block-size", type=int, default=None, help="override (66B sweep)")
+    ap.add_argument("--partition", type=int, default=None,
+                    help="tokens per split partition (0 = library choice, -1 = never)")
+    ap.add_argument("--replicas", type=int, default=0, help="0 = enough for >= 2 GB")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (counter calibration)")
+    return ap.parse_args()
+
+
+# ----------------------------------------------------------------- workloads --
+class Workload:
+    """Resident inputs of one workload and its step."""
+
+    def __init__(self, args, dev):
+        import torch
+
+        import paged_kv_cache_118_amd as pa
+        import workloads as W
+        self.torch, self.pa, self.W, self.dev = torch, pa, W, dev
+        self.args = args
+        name = args.workload
+        spec = {"opt13b_decode": W.OPT13B, "gqa_long": W.GQA_LONG,
+                "llama13b_prefix_share": W.LLAMA13B_SHARE, "opt66b_sweep": W.OPT66B_SWEEP}[name]
+        if args.block_size:
+            spec = spec.with_(block_size=args.block_size)
+        self.spec = spec
+        self.dtype = spec.dtype
+        self.part = spec.partition_size if args.partition is None else args.partition
+        self.pairs_dev = None
+        if name == "llama13b_prefix_share":
+            self._build_share()
+        elif name == "opt66b_sweep":
+            self._build_mixed()
+        else:
+            self._build_decode()
+        self._finish()
+
+    # -- host allocator: every workload takes its slots / tables from it ----
+    def _alloc_step(self, build, step):
+        """Run the allocator set-up, then time the per-step allocator work
+        (append + copy-on-write detection + table export) on fresh copies."""
+        times = []
+        for rep in range(3):
+            a = build()
+            t = time.perf_counter()
+            out = step(a)
+            times.append(time.perf_counter() - t)
+        self.host_alloc_us = round(1e6 * min(times), 1)
+        return a, out
+
+    def _build_decode(self):
+        pa, W, torch, dev = self.pa, self.W, self.torch, self.dev
+        sp = self.spec
+        rng = np.random.default_rng(sp.seed)
+        lens = W.draw_lengths(sp, rng)
+        bs, B = sp.block_size, sp.num_seqs
+        nb = int(math.ceil(1.25 * sum(W.blocks_needed(L, bs) for L in lens)))
+        maxb = max(W.blocks_needed(L, bs) for L in lens)
+
+        def build():
+            a = pa.BlockAllocator(nb, bs, shuffle_seed=sp.seed)
+            for b, L in enumerate(lens):
+                a.add_seq(b, int(L) - 1)  # history before this step's token
+            return a
+
+        def step(a):
+            slots = np.concatenate([a.append(b, 1)[0] for b in range(B)])
+            tables, lens_now = a.block_tables(np.arange(B), maxb)
+            return slots, tables, lens_now
+
+        _, (slots, tables, lens_now) = self._alloc_step(build, step)
+        self.lens, self.tables, self.slots, self.nb = lens_now, tables, slots, nb
+        self.decode_idx = None
+        self.config = {"workload": sp.name, "num_seqs": B, "q_heads": sp.num_q_heads,
+                       "kv_heads": sp.num_kv_heads, "head_dim": sp.head_dim,
+                       "block_size": bs, "lengths": list(sp.lengths),
+                       "mean_context": float(np.mean(lens)), "max_context": int(lens.max()),
+                       "pool_blocks": nb}
+
+    def _build_share(self):
+        pa, W = self.pa, self.W
+        sp = self.spec
+        _, gsize, prefix, lo, hi = sp.lengths
+        groups = sp.num_seqs // gsize
+        rng = np.random.default_rng(sp.seed)
+        tails = rng.integers(lo, hi + 1, size=sp.num_seqs)
+        bs, B = sp.block_size, sp.num_seqs
+        need = groups * (prefix // bs) + sum(W.blocks_needed(int(t), bs) + 1 for t in tails)
+        nb = int(math.ceil(1.25 * need))
+        maxb = W.blocks_needed(prefix + hi, bs)
+
+        def build():
+            a = pa.BlockAllocator(nb, bs, shuffle_seed=sp.seed)
+            for g in range(groups):
+                a.add_seq(100_000 + g, prefix)
+            for c in range(B):
+                a.fork(100_000 + c // gsize, c)
+                a.append(c, int(tails[c]) - 1)
+                a.fork(c, 200_000 + c)  # beam parent keeps the partial tail shared
+            return a
+
+        def step(a):
+            slots, pairs = [], []
+            for c in range(B):
+                s, pair = a.append(c, 1)
+                slots.append(s)
+                if pair:
+                    pairs.append(pair)
+            tables, lens_now = a.block_tables(np.arange(B), maxb)
+            return np.concatenate(slots), np.array(pairs, dtype=np.int64).reshape(-1, 2), \
+                tables, lens_now
+
+        _, (slots, pairs, tables, lens_now) = self._alloc_step(build, step)
+        self.lens, self.tables, self.slots, self.nb = lens_now, tables, slots, nb
+        self.pairs = pairs
+        self.decode_idx = None
+        uniq_tokens = groups * prefix + int(np.sum(lens_now - prefix))
+        self.unique_kv_bytes = uniq_tokens * self._tok_bytes()
+        self.config = {"workload": sp.name, "num_seqs": B, "groups": groups, "prefix": prefix,
+                       "q_heads": sp.num_q_heads, "kv_heads": sp.num_kv_heads,
+                       "head_dim": sp.head_dim, "block_size": bs, "tails": [lo, hi],
+                       "cow_pairs": int(len(pairs)), "pool_blocks": nb}
+
+    def _build_mixed(self):
+        pa, W = self.pa, self.W
+        sp = self.spec
+        rng = np.random.default_rng(sp.seed)
+        lens = W.draw_lengths(sp, rng)  # context after this step
+        bs, B = sp.block_size, sp.num_seqs
+        n_chunk, chunk = 16, 256
+        writers = np.arange(n_chunk)
+        dec = np.arange(n_chunk, B)
+        need = sum(W.blocks_needed(int(L) + (chunk if i < n_chunk else 0), bs)
+                   for i, L in enumerate(lens))
+        nb = int(math.ceil(1.25 * need))
+        maxb = max(W.blocks_needed(int(L) + chunk, bs) for L in lens)
+
+        def build():
+            a = pa.BlockAllocator(nb, bs, shuffle_seed=sp.seed)
+            for b, L in enumerate(lens):
+                a.add_seq(b, int(L) if b < n_chunk else int(L) - 1)
+            return a
+
+        def step(a):
+            slots = [a.append(b, chunk)[0] for b in writers] + [a.append(b, 1)[0] for b in dec]
+            tables, lens_now = a.block_tables(dec, maxb)
+            return np.concatenate(slots), tables, lens_now
+
+        _, (slots, tables, lens_now) = self._alloc_step(build, step)
+        self.lens, self.tables, self.slots, self.nb = lens_now, tables, slots, nb
+        self.decode_idx = dec
+        self.config = {"workload": sp.name, "num_seqs": B, "chunk_writers": n_chunk,
+                       "chunk_tokens": chunk, "decode_seqs": int(len(dec)),
+                       "q_heads": sp.num_q_heads, "kv_heads": sp.num_kv_heads,
+                       "head_dim": sp.head_dim, "block_size": bs, "lengths": list(sp.lengths),
+                       "pool_blocks": nb}
+
+    def _tok_bytes(self):
+        sp = self.spec
+        es = 4 if sp.dtype == "f32" else 2
+        return 2 * sp.num_kv_heads * sp.head_dim * es
+
+    def _finish(self):
+        torch, W, dev, sp = self.torch, self.W, self.dev, self.spec
+        es = 4 if sp.dtype == "f32" else 2
+        B = len(self.lens)
+        T = len(self.slots)
+        self.kv_read_bytes = int(np.sum(self.lens.astype(np.int64))) * self._tok_bytes()
+        q_bytes = B * sp.num_q_heads * sp.head_dim * es
+        self.decode_alg_bytes = (self.kv_read_bytes + 2 * q_bytes + self.tables.nbytes +
+                                 self.lens.nbytes)
+        self.decode_seqs = B
+        self.roofline_kernel = "pa_decode"
+        per_step = self.kv_read_bytes + 2 * T * self._tok_bytes()
+        self.replicas = self.args.replicas or max(1, int(math.ceil(2e9 / per_step)))
+        gen = W.make_generator(sp.seed, dev)
+        self.k, self.v, self.q = [], [], []
+        base_k = W.randn(W.k_pool_shape(self.nb, sp.num_kv_heads, sp.block_size, sp.head_dim),
+                         sp.dtype, gen, dev)
+        base_v = W.randn(W.v_pool_shape(self.nb, sp.num_kv_heads, sp.block_size, sp.head_dim),
+                         sp.dtype, gen, dev)
+        # host copies for the CPU baseline are taken before any kernel runs
+        self._host_pools = None
+        for r in range(self.replicas):
+            self.k.append(base_k if r == 0 else base_k.clone())
+            self.v.append(base_v if r == 0 else base_v.clone())
+            self.q.append(W.randn((B, sp.num_q_heads, sp.head_dim), sp.dtype, gen, dev))
+        self.k_new, self.v_new = W.new_token_rows(T, sp.num_kv_heads, sp.head_dim, sp.dtype, gen,
+                                                  dev)
+        self.out = torch.empty_like(self.q[0])
+        self.slots_dev = torch.from_numpy(self.slots).to(dev)
+        self.tables_dev = torch.from_numpy(self.tables).to(dev)
+        self.lens_dev = torch.from_numpy(self.lens).to(dev)
+        if getattr(self, "pairs", None) is not None and len(self.pairs):
+            self.pairs_dev = torch.from_numpy(self.pairs).to(dev)
+        self.max_ctx = int(self.lens.max())
+        ws = self.pa.pa_decode_workspace_bytes(B, sp.num_q_heads, sp.num_kv_heads, sp.head_dim,
+                                               sp.block_size, self.max_ctx, self.part,
+                                               W.TORCH_DTYPE[sp.dtype])
+        self.ws = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
+        self.config["partition"] = self.pa.pa_decode_partition_size(
+            B, sp.num_q_heads, sp.num_kv_heads, sp.head_dim, sp.block_size, self.max_ctx,
+            self.part, W.TORCH_DTYPE[sp.dtype])
+        self.config["replicas"] = self.replicas
+        self.config["kv_read_bytes_per_step"] = self.kv_read_bytes
+        if hasattr(self, "unique_kv_bytes"):
+            self.config["unique_kv_bytes_per_step"] = self.unique_kv_bytes
+        self._snapshot_for_oracle()
+
+    def _snapshot_for_oracle(self):
+        """Host copies of the sample the CPU baseline decodes, taken now --
+        before any libpa kernel has touched the pools."""
+        if self.args.no_cpu_baseline:
+            return
+        W, torch = self.W, self.torch
+        sp = self.spec
+        bs = sp.block_size
+        tok_heads = np.cumsum(self.lens.astype(np.int64)) * sp.num_q_heads
+        # sample size: about cpu_seconds of oracle work at ~0.1 M token-heads/s/thread
+        threads = max(1, len(os.sched_getaffinity(0)))
+        budget = self.args.cpu_seconds * 0.15e6 * threads
+        k = int(np.searchsorted(tok_heads, budget)) + 1
+        k = max(1, min(k, len(self.lens)))
+        seqs = list(range(k))
+        used = sorted({int(b) for s in seqs for b in self.tables[s, :W.blocks_needed(
+            int(self.lens[s]), bs)]})
+        remap = {b: i for i, b in enumerate(used)}
+        t = np.full((k, self.tables.shape[1]), -1, dtype=np.int32)
+        for i, s in enumerate(seqs):
+            n = W.blocks_needed(int(self.lens[s]), bs)
+            t[i, :n] = [remap[int(b)] for b in self.tables[s, :n]]
+        idx = torch.tensor(used, dtype=torch.long, device=self.dev)
+        qsel = self.q[0] if self.decode_idx is None else self.q[0]
+        self._host = dict(
+            q=W.to_numpy_bits(qsel[:k]), k=W.to_numpy_bits(self.k[0].index_select(0, idx)),
+            v=W.to_numpy_bits(self.v[0].index_select(0, idx)), tables=t,
+            lens=self.lens[:k].copy(), seqs=k)
+
+    # -- the timed step ----------------------------------------------------
+    def step(self, r, ev=None):
+        pa, sp = self.pa, self.spec
+        if self.pairs_dev is not None:
+            pa.pa_copy_blocks(self.k[r], self.v[r], self.pairs_dev, sp.block_size)
+        pa.pa_reshape_and_cache(self.k_new, self.v_new, self.k[r], self.v[r], self.slots_dev,
+                                sp.block_size)
+        if ev is not None:
+            ev[0].record()
+        pa.pa_decode(self.out, self.q[r], self.k[r], self.v[r], self.tables_dev, self.lens_dev,
+                     sp.scale, sp.block_size, sp.num_kv_heads, self.max_ctx,
+                     partition_size=self.part, workspace=self.ws)
+        if ev is not None:
+            ev[1].record()
+
+    # -- CPU baseline --------------------------------------------------------
+    def cpu_baseline(self, seconds):
+        import oracle
+        h = self._host
+        sp = self.spec
+        threads = max(1, len(os.sched_getaffinity(0)))
+        orc = oracle.get()
+        t = time.perf_counter()
+        orc.decode(h["q"], h["k"], h["v"], h["tables"], h["lens"], sp.scale, sp.block_size,
+                   sp.num_kv_heads, sp.dtype, nthreads=threads)
+        dt = time.perf_counter() - t
+        kv = int(np.sum(h["lens"].astype(np.int64))) * self._tok_bytes()
+        return {"value": round(kv / 1e9 / dt, 4), "unit": "GB/s", "cores": threads,
+                "kind": "oracle", "seconds": round(dt, 3),
+                "sample": f"fp64 oracle decode of the first {h['seqs']} of {len(self.lens)} "
+                          f"sequences ({kv / 1e6:.1f} MB of K/V), all q heads"}
+
+
+def build_workload(args, dev):
+    return Workload(args, dev)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; use --gpus 1"}))
+        sys.exit(2)
+    import torch
+
+    if args.calib_copy_mb:
+        n = args.calib_copy_mb << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_copy_bytes": n, "launches": 5}))
+        return
+
+    dev = torch.device("cuda:0")
+    wl = build_workload(args, dev)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    # host allocator cost per step (its outputs are the resident inputs below)
+    for i in range(args.warmup):
+        wl.step(i % wl.replicas)
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        wl.step(i % wl.replicas, ev[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    dec_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+    kv_gb = wl.kv_read_bytes / 1e9
+    value = kv_gb / (ms_step / 1e3)
+    achieved = wl.decode_alg_bytes / 1e9 / (dec_ms / 1e3)
+    rec = {
+        "metric": "paged_decode_kv_read_GBps",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": wl.config,
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "seq_per_s": round(wl.decode_seqs / (ms_step / 1e3), 1),
+        "decode_kernel_ms": round(dec_ms, 5),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "kernel": wl.roofline_kernel,
+        },
+        "host_alloc_us_per_step": wl.host_alloc_us,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = wl.cpu_baseline(args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,205 @@
+/*
+ * pa.h -- C ABI of libpa: paged decode attention, KV-cache write, block copy
+ * and a host block allocator, for AMD Instinct MI355X (gfx950).
+ *
+ * Sources (web pages on PagedAttention):
+ *  [P5] wq-win.github.io, "079 | vLLM 与 PagedAttention" (digest of Kwon et al.,
+ *       SOSP 2023): section 二 (the Z / o equations, copy-on-write, tail
+ *       waste), section 三 (per-iteration block management).
+ *  [P1] gitcode.csdn.net, "vLLM 推理引擎：PagedAttention 与 KVCache 管理":
+ *       section 1 (block data structures), section 3 (the forward signature
+ *       query / key_cache / value_cache / block_tables / context_lens).
+ *  [P3] deepinsea.top, "PagedAttention 内存管理深度解析", section
+ *       "分页机制设计" (free list, all-or-nothing allocation).
+ *  [P4] vkads.cloudxian.cn, "vLLM PagedAttention源码：KV Cache", kernel
+ *       pseudocode (flat slot numbering of a block).
+ *
+ * Conventions for every call
+ *  - Device pointers are caller-owned (e.g. torch tensors); libpa never
+ *    allocates or frees device memory.  The decode split path uses the
+ *    caller's workspace.
+ *  - Calls return a pa_status and never abort or throw.  GPU calls are
+ *    asynchronous on `stream` (a hipStream_t; NULL = the null stream) and run
+ *    in issue order; a launch failure is PA_EHIP.
+ *  - Host-visible arguments are checked (null pointers, sizes, alignment,
+ *    supported dtype / head_dim / block_size, workspace size).  Device data
+ *    (block ids, slots, lengths) is not checked on the hot path; kernels
+ *    clamp or skip out-of-range ids so that a bad id never faults, but the
+ *    result for that sequence / token is then undefined.  With the
+ *    environment variable PA_VALIDATE=1, the GPU calls first copy the index
+ *    arrays to the host, synchronise `stream`, and return PA_EVALIDATE on an
+ *    out-of-range id, a duplicate slot or an overlapping copy pair.
+ *
+ * KV pool layout (one layer).  BS = block_size, D = head_dim, Hkv = kv heads,
+ * VS = min(BS, 16).  Element (physical block b, kv head h, offset o, dim d):
+ *   K:  k_cache[((b*Hkv + h)*BS + o)*D + d]
+ *   V:  v_cache[(((b*Hkv + h)*(BS/VS) + o/VS)*D + d)*VS + o%VS]
+ *  K stores token rows; V stores slabs of VS tokens, each slab [D][VS]
+ *  (token index fastest), so that one wavefront reads a whole 16-token slab
+ *  of either pool with contiguous 16-byte loads.  A token's slot is
+ *  b*BS + o ([P4]).  BS must be 1, 2, 4, 8, 16 or a multiple of 16.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_EINVAL = -1,    /* bad argument (null pointer, size, alignment) */
+  PA_ENOTSUP = -2,   /* valid but unsupported dtype / head_dim / block_size */
+  PA_ENOMEM = -3,    /* allocator: not enough free blocks (nothing changed) */
+  PA_EHIP = -4,      /* a HIP runtime call or kernel launch failed */
+  PA_EVALIDATE = -5, /* PA_VALIDATE=1 found a bad index in device data */
+  PA_ENOENT = -6     /* allocator: unknown sequence id, or id already used */
+} pa_status;
+
+typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+
+/* Message for a status code (static storage). */
+const char* pa_strerror(pa_status s);
+
+/* ------------------------------------------------------------------------
+ * pa_decode -- single-query paged attention for every (sequence, q head).
+ *
+ * Computes, for sequence b with L = context_lens[b] valid positions and q
+ * head h reading kv head g = h / (num_q_heads / num_kv_heads):
+ *   s_u = scale * q[b,h,:] . K[u],  o = sum_u exp(s_u) V[u] / sum_u exp(s_u)
+ * over u = 0 .. L-1, with one denominator shared by all blocks and the
+ * unfilled tail of the last block excluded ([P5] section 二, the Z / o
+ * equations).  Position u lives in physical block block_tables[b][u / BS] at
+ * offset u % BS ([P1] section 3).  L = 0 gives a zero row.  fp32 accumulation;
+ * the output is rounded to nearest-even in `dtype`.
+ *
+ *  out          [num_seqs][num_q_heads][head_dim] of dtype (device, written)
+ *  q            [num_seqs][num_q_heads][head_dim] of dtype (device)
+ *  k_cache      K pool, layout above, num_blocks blocks (device)
+ *  v_cache      V pool, layout above (device)
+ *  block_tables [num_seqs][max_blocks_per_seq] int32 (device); entries past
+ *               ceil(L / BS) are never read (padding is conventionally -1)
+ *  context_lens [num_seqs] int32 (device).  Must satisfy
+ *               L <= max_context_len and L <= max_blocks_per_seq * BS;
+ *               positions beyond either bound are ignored.
+ *  scale        score scale (1/sqrt(head_dim) for standard attention)
+ *  partition_size  tokens per work item: 0 = library choice, -1 = never
+ *               split a sequence, > 0 = that many (a multiple of 256).  Split
+ *               sequences are merged by a second kernel from per-partition
+ *               fp32 (max, sum, unnormalised output).
+ *  workspace    device scratch of at least pa_decode_workspace_bytes(...)
+ *               bytes (may be NULL when that size is 0); contents need no
+ *               initialisation and are clobbered.
+ * Requirements: num_q_heads % num_kv_heads == 0; head_dim in {16, 32, 64,
+ * 128, 256}; q, out and the pools 16-byte aligned.
+ * ---------------------------------------------------------------------- */
+pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* context_lens, float scale,
+                    int32_t block_size, int32_t num_kv_heads, int32_t num_seqs,
+                    int32_t num_q_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                    int32_t max_context_len, int64_t num_blocks, pa_dtype dtype,
+                    int32_t partition_size, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/* Workspace bytes pa_decode needs for these sizes (0 when nothing splits).
+ * Pass the same partition_size, head counts and block_size as to pa_decode. */
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size, int32_t max_context_len,
+                                 int32_t partition_size, pa_dtype dtype);
+
+/* The partition size pa_decode uses for these arguments (0 = no split). */
+int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size, int32_t max_context_len,
+                                 int32_t partition_size, pa_dtype dtype);
+
+/* ------------------------------------------------------------------------
+ * pa_reshape_and_cache -- write new tokens' K and V rows into their slots.
+ *
+ * Token t (row k[t*k_token_stride ...], [num_kv_heads][head_dim] contiguous,
+ * same for v) goes to slot = slot_mapping[t] = block * BS + offset ([P4]
+ * pseudocode), in both pools, bit for bit.  A negative slot is padding and is
+ * skipped.  Slots must be distinct within one call (duplicates race).  This is
+ * the write that precedes attention in each iteration ([P5] section 三).
+ *  k, v          device token rows of dtype; strides in elements, >= Hkv*D
+ *  slot_mapping  [num_tokens] int64 (device)
+ * Requirements: head_dim * element size a multiple of 16 bytes; k, v and the
+ * pools 16-byte aligned; strides a multiple of 16 bytes.
+ * ---------------------------------------------------------------------- */
+pa_status pa_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,
+                               const int64_t* slot_mapping, int32_t num_tokens,
+                               int64_t k_token_stride, int64_t v_token_stride,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int64_t num_blocks, pa_dtype dtype, void* stream);
+
+/* ------------------------------------------------------------------------
+ * pa_copy_blocks -- copy-on-write of whole blocks ([P5] section 二, part
+ * "共享与写时复制"; [P1] / [P3] copy-on-write).
+ *
+ * For each pair p, every byte of block src_dst_pairs[2p] (all heads, all BS
+ * slots, K and V) is copied to block src_dst_pairs[2p+1].  Destinations must
+ * be distinct and no destination may be a source in the same call.
+ *  src_dst_pairs  [num_pairs][2] int64 (device)
+ * ---------------------------------------------------------------------- */
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* src_dst_pairs,
+                         int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int64_t num_blocks, pa_dtype dtype, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Host block allocator ([P1] section 1 PhysicalTokenBlock / BlockTable,
+ * [P3] BlockManager, [P5] sections 二 and 三).  Host memory only; not thread
+ * safe (one allocator per scheduler thread).
+ *
+ * Physical ids are shuffled once from shuffle_seed (splitmix64-driven
+ * Fisher-Yates; seed 0 keeps ids in order) and then taken from the end of the
+ * free list and returned to its end (LIFO).  A sequence holds ceil(L / BS)
+ * blocks.  Every block has a reference count; a block returns to the free
+ * list only when its count reaches 0.
+ * ---------------------------------------------------------------------- */
+typedef struct pa_alloc pa_alloc;
+
+/* NULL on bad arguments or host OOM. */
+pa_alloc* pa_alloc_create(int64_t num_blocks, int32_t block_size, uint64_t shuffle_seed);
+void pa_alloc_destroy(pa_alloc* a);
+
+/* New sequence holding num_tokens (>= 0) tokens: ceil(num_tokens / BS) fresh
+ * blocks, all or nothing (PA_ENOMEM leaves the allocator unchanged). */
+pa_status pa_alloc_add_seq(pa_alloc* a, int64_t seq_id, int32_t num_tokens);
+
+/* child shares every block of parent (each count + 1) and its length. */
+pa_status pa_alloc_fork(pa_alloc* a, int64_t parent_id, int64_t child_id);
+
+/* Reserve slots for the next n_tokens tokens of seq_id.  If the first write
+ * goes into a partially filled tail block whose count is > 1, the block is
+ * copied first: a fresh block replaces it in this sequence only, the old
+ * block loses one reference, and the pair (old, new) is written to
+ * cow_pairs_out[0..1] with *n_cow_out = 1 (else 0); the caller must run
+ * pa_copy_blocks with it before pa_reshape_and_cache.  A new block is taken
+ * whenever a position crosses a block boundary ([P5] section 三).
+ * slots_out receives n_tokens slots.  All or nothing on PA_ENOMEM. */
+pa_status pa_alloc_append(pa_alloc* a, int64_t seq_id, int32_t n_tokens, int64_t* slots_out,
+                          int64_t* cow_pairs_out, int32_t* n_cow_out);
+
+/* Drop the sequence: each of its blocks loses one reference; blocks at 0 are
+ * reclaimed. */
+pa_status pa_alloc_free_seq(pa_alloc* a, int64_t seq_id);
+
+/* Host rows for pa_decode: tables_out [n][max_blocks] (padded with -1) and
+ * lens_out [n].  PA_EINVAL if a sequence holds more than max_blocks blocks. */
+pa_status pa_alloc_block_tables(const pa_alloc* a, const int64_t* seq_ids, int32_t n,
+                                 int32_t max_blocks, int32_t* tables_out, int32_t* lens_out);
+
+int64_t pa_alloc_num_free(const pa_alloc* a);
+/* Reference count of a physical block (-1 for an out-of-range id). */
+int32_t pa_alloc_refcount(const pa_alloc* a, int64_t block);
+/* Length / number of blocks of a sequence (-1 if unknown). */
+int32_t pa_alloc_seq_len(const pa_alloc* a, int64_t seq_id);
+int32_t pa_alloc_seq_num_blocks(const pa_alloc* a, int64_t seq_id);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

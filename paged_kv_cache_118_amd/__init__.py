@@ -1,0 +1,267 @@
+"""Paged KV-cache decode attention for AMD MI355X (gfx950).
+
+A thin ctypes binding over ``libpa.so`` (the C ABI in ``include/pa.h``): the
+functions below only turn torch tensors into pointers and sizes; every step
+of the computation runs in libpa's HIP kernels.  PyTorch supplies device
+memory and streams.  If ``libpa.so`` has not been built this module raises
+ImportError -- there is no fallback implementation.
+
+Pool layout (BS = block_size, D = head_dim, VS = min(BS, 16)):
+    k_cache: [num_blocks, Hkv, BS, D]
+    v_cache: [num_blocks, Hkv, BS // VS, D, VS]
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpa.so")
+
+PA_F32, PA_F16, PA_BF16 = 0, 1, 2
+_DTYPE = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -m paged_kv_cache_118_amd.build` "
+            "(or __graft_entry__.build())")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                             ctypes.c_size_t)
+    sig = {
+        "pa_strerror": (ctypes.c_char_p, [i32]),
+        "pa_decode": (i32, [vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, i32, i32, i32, i32, i64,
+                            i32, i32, vp, sz, vp]),
+        "pa_decode_workspace_bytes": (sz, [i32, i32, i32, i32, i32, i32, i32, i32]),
+        "pa_decode_partition_size": (i32, [i32, i32, i32, i32, i32, i32, i32, i32]),
+        "pa_reshape_and_cache": (i32, [vp, vp, vp, vp, vp, i32, i64, i64, i32, i32, i32, i64,
+                                       i32, vp]),
+        "pa_copy_blocks": (i32, [vp, vp, vp, i32, i32, i32, i32, i64, i32, vp]),
+        "pa_alloc_create": (vp, [i64, i32, ctypes.c_uint64]),
+        "pa_alloc_destroy": (None, [vp]),
+        "pa_alloc_add_seq": (i32, [vp, i64, i32]),
+        "pa_alloc_fork": (i32, [vp, i64, i64]),
+        "pa_alloc_append": (i32, [vp, i64, i32, vp, vp, vp]),
+        "pa_alloc_free_seq": (i32, [vp, i64]),
+        "pa_alloc_block_tables": (i32, [vp, vp, i32, i32, vp, vp]),
+        "pa_alloc_num_free": (i64, [vp]),
+        "pa_alloc_refcount": (i32, [vp, i64]),
+        "pa_alloc_seq_len": (i32, [vp, i64]),
+        "pa_alloc_seq_num_blocks": (i32, [vp, i64]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+# every symbol include/pa.h declares (checked by the CPU test suite)
+EXPORTED = ("pa_strerror", "pa_decode", "pa_decode_workspace_bytes", "pa_decode_partition_size",
+            "pa_reshape_and_cache", "pa_copy_blocks", "pa_alloc_create", "pa_alloc_destroy",
+            "pa_alloc_add_seq", "pa_alloc_fork", "pa_alloc_append", "pa_alloc_free_seq",
+            "pa_alloc_block_tables", "pa_alloc_num_free", "pa_alloc_refcount",
+            "pa_alloc_seq_len", "pa_alloc_seq_num_blocks")
+
+
+def lib():
+    return _lib
+
+
+class PAError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__(f"libpa status {status}: {pa_strerror(status)}")
+
+
+class OutOfBlocks(PAError):
+    pass
+
+
+def pa_strerror(status: int) -> str:
+    return _lib.pa_strerror(status).decode()
+
+
+def _check(rc: int) -> None:
+    if rc == -3:
+        raise OutOfBlocks(rc)
+    if rc != 0:
+        raise PAError(rc)
+
+
+def _dev_ptr(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    try:
+        return _DTYPE[t.dtype]
+    except KeyError:
+        raise ValueError(f"unsupported dtype {t.dtype}") from None
+
+
+def v_slab(block_size: int) -> int:
+    return block_size if block_size < 16 else 16
+
+
+# ---------------------------------------------------------------- decode --
+def pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                              max_context_len, partition_size=0, dtype=torch.float16) -> int:
+    return int(_lib.pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                              block_size, max_context_len, partition_size,
+                                              _DTYPE[dtype]))
+
+
+def pa_decode_partition_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                             max_context_len, partition_size=0, dtype=torch.float16) -> int:
+    return int(_lib.pa_decode_partition_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                             block_size, max_context_len, partition_size,
+                                             _DTYPE[dtype]))
+
+
+def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
+              num_kv_heads, max_context_len, partition_size=0, workspace=None, stream=None):
+    """out[b, h] = softmax over the first context_lens[b] positions (see pa.h).
+
+    ``max_context_len`` is a host int >= every context length.  ``workspace``
+    is a uint8 device tensor of pa_decode_workspace_bytes(...) bytes; one is
+    allocated when omitted and needed."""
+    B, hq, D = q.shape
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q in shape and dtype")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("pools must have q's dtype")
+    nb = k_cache.shape[0]
+    vs = v_slab(block_size)
+    if tuple(k_cache.shape) != (nb, num_kv_heads, block_size, D):
+        raise ValueError(f"k_cache shape {tuple(k_cache.shape)} is not "
+                         f"{(nb, num_kv_heads, block_size, D)}")
+    if tuple(v_cache.shape) != (nb, num_kv_heads, block_size // vs, D, vs):
+        raise ValueError(f"v_cache shape {tuple(v_cache.shape)} is not "
+                         f"{(nb, num_kv_heads, block_size // vs, D, vs)}")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("block_tables and context_lens must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_tables must be [num_seqs, max_blocks], context_lens [num_seqs]")
+    dt = _dtype_code(q)
+    ws_bytes = int(_lib.pa_decode_workspace_bytes(B, hq, num_kv_heads, D, block_size,
+                                                  max_context_len, partition_size, dt))
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_lib.pa_decode(_dev_ptr(out, "out"), _dev_ptr(q, "q"), _dev_ptr(k_cache, "k_cache"),
+                          _dev_ptr(v_cache, "v_cache"), _dev_ptr(block_tables, "block_tables"),
+                          _dev_ptr(context_lens, "context_lens"), float(scale), block_size,
+                          num_kv_heads, B, hq, D, block_tables.shape[1], int(max_context_len),
+                          nb, dt, int(partition_size), ws_ptr, ws_len, _stream(stream)))
+    return out
+
+
+# ------------------------------------------------------------ cache ops --
+def pa_reshape_and_cache(k, v, k_cache, v_cache, slot_mapping, block_size, stream=None):
+    """Write token rows k, v ([T, Hkv, D]; the token dim may be strided) into
+    their slots (int64 [T], negative = skip)."""
+    T, hkv, D = k.shape
+    if v.shape != k.shape or k.dtype != k_cache.dtype or v.dtype != k_cache.dtype:
+        raise ValueError("k / v must match each other and the pools")
+    for name, t in (("k", k), ("v", v)):
+        if t.stride(2) != 1 or t.stride(1) != D:
+            raise ValueError(f"{name} rows must be [Hkv, D] contiguous per token")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (T,):
+        raise ValueError("slot_mapping must be int64 [num_tokens]")
+    nb = k_cache.shape[0]
+    _check(_lib.pa_reshape_and_cache(ctypes.c_void_p(k.data_ptr()),
+                                     ctypes.c_void_p(v.data_ptr()),
+                                     _dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"),
+                                     _dev_ptr(slot_mapping, "slot_mapping"), T, k.stride(0),
+                                     v.stride(0), hkv, D, block_size, nb, _dtype_code(k_cache),
+                                     _stream(stream)))
+
+
+def pa_copy_blocks(k_cache, v_cache, src_dst_pairs, block_size, stream=None):
+    """Copy whole blocks src -> dst in both pools; pairs int64 [P, 2]."""
+    if src_dst_pairs.dtype != torch.int64 or src_dst_pairs.dim() != 2 or \
+            src_dst_pairs.shape[1] != 2:
+        raise ValueError("src_dst_pairs must be int64 [num_pairs, 2]")
+    nb, hkv, _, D = k_cache.shape
+    _check(_lib.pa_copy_blocks(_dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"),
+                               _dev_ptr(src_dst_pairs, "src_dst_pairs"), src_dst_pairs.shape[0],
+                               hkv, D, block_size, nb, _dtype_code(k_cache), _stream(stream)))
+
+
+# ------------------------------------------------------------ allocator --
+class BlockAllocator:
+    """Host ref-counted block pool (pa_alloc_* in pa.h)."""
+
+    def __init__(self, num_blocks: int, block_size: int, shuffle_seed: int = 0):
+        self._h = _lib.pa_alloc_create(num_blocks, block_size, shuffle_seed)
+        if not self._h:
+            raise ValueError("pa_alloc_create failed")
+        self.block_size = block_size
+        self.num_blocks = num_blocks
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h:
+            _lib.pa_alloc_destroy(h)
+            self._h = None
+
+    def add_seq(self, seq_id: int, num_tokens: int) -> None:
+        _check(_lib.pa_alloc_add_seq(self._h, seq_id, num_tokens))
+
+    def fork(self, parent_id: int, child_id: int) -> None:
+        _check(_lib.pa_alloc_fork(self._h, parent_id, child_id))
+
+    def append(self, seq_id: int, n_tokens: int):
+        """Returns (slots int64[n_tokens], cow_pair (src, dst) or None)."""
+        slots = np.empty(max(n_tokens, 1), dtype=np.int64)
+        pair = np.empty(2, dtype=np.int64)
+        n = ctypes.c_int32(0)
+        _check(_lib.pa_alloc_append(self._h, seq_id, n_tokens,
+                                    slots.ctypes.data_as(ctypes.c_void_p),
+                                    pair.ctypes.data_as(ctypes.c_void_p), ctypes.byref(n)))
+        return slots[:n_tokens], ((int(pair[0]), int(pair[1])) if n.value else None)
+
+    def free_seq(self, seq_id: int) -> None:
+        _check(_lib.pa_alloc_free_seq(self._h, seq_id))
+
+    def block_tables(self, seq_ids, max_blocks: int):
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        tables = np.empty((len(ids), max_blocks), dtype=np.int32)
+        lens = np.empty(len(ids), dtype=np.int32)
+        _check(_lib.pa_alloc_block_tables(self._h, ids.ctypes.data_as(ctypes.c_void_p), len(ids),
+                                          max_blocks, tables.ctypes.data_as(ctypes.c_void_p),
+                                          lens.ctypes.data_as(ctypes.c_void_p)))
+        return tables, lens
+
+    def num_free(self) -> int:
+        return int(_lib.pa_alloc_num_free(self._h))
+
+    def refcount(self, block: int) -> int:
+        return int(_lib.pa_alloc_refcount(self._h, block))
+
+    def seq_len(self, seq_id: int) -> int:
+        return int(_lib.pa_alloc_seq_len(self._h, seq_id))
+
+    def seq_num_blocks(self, seq_id: int) -> int:
+        return int(_lib.pa_alloc_seq_num_blocks(self._h, seq_id))

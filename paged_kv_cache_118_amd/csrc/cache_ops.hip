@@ -1,0 +1,135 @@
+// KV-cache write (reshape_and_cache) and copy-on-write block copy for gfx950.
+//
+// Both are pure bit moves.  The write puts token t's K/V rows into slot
+// slot_mapping[t] = block * BS + offset (flat slot numbering of the kernel
+// pseudocode on vkads.cloudxian.cn "vLLM PagedAttention源码：KV Cache"); the
+// copy duplicates whole blocks before a write into a shared tail block
+// (wq-win.github.io "079 | vLLM 与 PagedAttention", section 二, part
+// "共享与写时复制").
+#include "pa_internal.h"
+
+namespace pa {
+
+namespace {
+
+constexpr int kWriteTokens = 32;  // tokens per workgroup in the cache write
+constexpr int kThreads = 256;
+
+// One workgroup = kWriteTokens consecutive tokens of one kv head.
+//  K: token rows are contiguous on both sides -> 16-byte vector copies.
+//  V: the pool stores 16-token slabs [D][VS]; rows are staged in LDS and each
+//     lane then writes one token's element, so lanes with consecutive slots
+//     write consecutive addresses of a slab row.
+template <int ES>
+__global__ __launch_bounds__(kThreads) void reshape_and_cache_kernel(
+    const char* __restrict__ k, const char* __restrict__ v, char* __restrict__ k_cache,
+    char* __restrict__ v_cache, const int64_t* __restrict__ slots, int32_t num_tokens,
+    int64_t k_stride, int64_t v_stride, int32_t hkv, int32_t D, int32_t bs, int64_t num_blocks) {
+  using E = typename std::conditional<ES == 4, uint32_t, uint16_t>::type;
+  extern __shared__ __align__(16) char smem[];
+  const int row_bytes = D * ES;
+  const int lds_stride = row_bytes + 4;  // pad: consecutive tokens hit different banks
+  const int h = blockIdx.y;
+  const int t0 = blockIdx.x * kWriteTokens;
+  const int nt = min(kWriteTokens, num_tokens - t0);
+  const int64_t max_slot = num_blocks * (int64_t)bs;
+  const int vs = v_slab(bs);
+
+  // K rows (and V rows into LDS): one 16-byte chunk per thread per iteration.
+  const int chunks = row_bytes / 16;
+  for (int i = threadIdx.x; i < nt * chunks; i += kThreads) {
+    const int tt = i / chunks, c = i % chunks;
+    const int64_t t = t0 + tt;
+    const int64_t slot = slots[t];
+    const uint4 kv = *reinterpret_cast<const uint4*>(k + (t * k_stride + (int64_t)h * D) * ES +
+                                                      c * 16);
+    const uint4 vv = *reinterpret_cast<const uint4*>(v + (t * v_stride + (int64_t)h * D) * ES +
+                                                      c * 16);
+    // LDS row pitch is 4-byte aligned only: store as four dwords
+    uint32_t* dst = reinterpret_cast<uint32_t*>(smem + tt * lds_stride + c * 16);
+    dst[0] = vv.x;
+    dst[1] = vv.y;
+    dst[2] = vv.z;
+    dst[3] = vv.w;
+    if (slot >= 0 && slot < max_slot) {
+      const int64_t blk = slot / bs;
+      const int off = (int)(slot - blk * bs);
+      *reinterpret_cast<uint4*>(k_cache + (((blk * hkv + h) * bs + off) * D) * ES + c * 16) = kv;
+    }
+  }
+  __syncthreads();
+
+  // V elements: lane = token (fastest), threads stride over d.
+  const int tt = threadIdx.x % kWriteTokens;
+  const int dgrp = threadIdx.x / kWriteTokens;
+  if (tt >= nt) return;
+  const int64_t slot = slots[t0 + tt];
+  if (slot < 0 || slot >= max_slot) return;
+  const int64_t blk = slot / bs;
+  const int off = (int)(slot - blk * bs);
+  E* vdst = reinterpret_cast<E*>(v_cache) + ((blk * hkv + h) * (bs / vs) + off / vs) * (int64_t)D * vs +
+            off % vs;
+  const E* src = reinterpret_cast<const E*>(smem + tt * lds_stride);
+  for (int d = dgrp; d < D; d += kThreads / kWriteTokens) vdst[(int64_t)d * vs] = src[d];
+}
+
+// Whole-block copies: block b of either pool is one contiguous run of
+// block_bytes bytes (all heads, all slots), so each pair is two memcpys.
+__global__ __launch_bounds__(kThreads) void copy_blocks_kernel(char* __restrict__ k_cache,
+                                                               char* __restrict__ v_cache,
+                                                               const int64_t* __restrict__ pairs,
+                                                               int64_t block_bytes,
+                                                               int64_t num_blocks) {
+  const int64_t src = pairs[2 * blockIdx.y], dst = pairs[2 * blockIdx.y + 1];
+  if (src < 0 || dst < 0 || src >= num_blocks || dst >= num_blocks) return;
+  const int64_t n16 = block_bytes / 16;
+  const uint4* ks = reinterpret_cast<const uint4*>(k_cache + src * block_bytes);
+  const uint4* vs = reinterpret_cast<const uint4*>(v_cache + src * block_bytes);
+  uint4* kd = reinterpret_cast<uint4*>(k_cache + dst * block_bytes);
+  uint4* vd = reinterpret_cast<uint4*>(v_cache + dst * block_bytes);
+  for (int64_t i = blockIdx.x * (int64_t)kThreads + threadIdx.x; i < n16;
+       i += (int64_t)gridDim.x * kThreads) {
+    const uint4 a = ks[i];
+    const uint4 b = vs[i];
+    kd[i] = a;
+    vd[i] = b;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,
+                                    const int64_t* slots, int32_t num_tokens, int64_t k_stride,
+                                    int64_t v_stride, int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t block_size, int64_t num_blocks, int elem_bytes,
+                                    hipStream_t s) {
+  if (num_tokens == 0) return hipSuccess;
+  dim3 grid((num_tokens + kWriteTokens - 1) / kWriteTokens, num_kv_heads);
+  const size_t lds = (size_t)kWriteTokens * (head_dim * elem_bytes + 4);
+  if (elem_bytes == 4)
+    hipLaunchKernelGGL(reshape_and_cache_kernel<4>, grid, dim3(kThreads), lds, s,
+                       (const char*)k, (const char*)v, (char*)k_cache, (char*)v_cache, slots,
+                       num_tokens, k_stride, v_stride, num_kv_heads, head_dim, block_size,
+                       num_blocks);
+  else
+    hipLaunchKernelGGL(reshape_and_cache_kernel<2>, grid, dim3(kThreads), lds, s,
+                       (const char*)k, (const char*)v, (char*)k_cache, (char*)v_cache, slots,
+                       num_tokens, k_stride, v_stride, num_kv_heads, head_dim, block_size,
+                       num_blocks);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs,
+                              int32_t num_pairs, int64_t block_bytes, int64_t num_blocks,
+                              hipStream_t s) {
+  if (num_pairs == 0) return hipSuccess;
+  const int64_t n16 = block_bytes / 16;
+  int gx = (int)((n16 + kThreads * 4 - 1) / (kThreads * 4));
+  if (gx < 1) gx = 1;
+  dim3 grid(gx, num_pairs);
+  hipLaunchKernelGGL(copy_blocks_kernel, grid, dim3(kThreads), 0, s, (char*)k_cache,
+                     (char*)v_cache, pairs, block_bytes, num_blocks);
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -1,0 +1,284 @@
+// libpa C ABI: argument checks, launch configuration and dispatch.
+// The operations themselves are defined in include/pa.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <unordered_set>
+#include <vector>
+
+#include "pa.h"
+#include "pa_internal.h"
+
+using namespace pa;
+
+namespace {
+
+constexpr int kPartGranule = 256;  // partitions are a multiple of this many tokens
+constexpr int kDefaultPart = 512;
+// A GQA group this large or larger goes to the matrix cores.
+constexpr int kMfmaMinGroup = 4;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elem_bytes(pa_dtype d) { return d == PA_F32 ? 4 : 2; }
+
+bool dtype_ok(pa_dtype d) { return d == PA_F32 || d == PA_F16 || d == PA_BF16; }
+
+bool block_size_ok(int bs) {
+  return bs == 1 || bs == 2 || bs == 4 || bs == 8 || (bs >= 16 && bs % 16 == 0);
+}
+
+bool validate_enabled() {
+  static int v = -1;
+  if (v < 0) {
+    const char* e = std::getenv("PA_VALIDATE");
+    v = (e && e[0] && e[0] != '0') ? 1 : 0;
+  }
+  return v == 1;
+}
+
+enum class Path { kValu, kMfma, kGeneric };
+
+Path choose_path(pa_dtype dt, int head_dim, int block_size, int group) {
+  if (group >= kMfmaMinGroup && decode_mfma_supported(dt, head_dim, block_size, group))
+    return Path::kMfma;
+  if (decode_valu_supported(dt, head_dim, block_size)) return Path::kValu;
+  return Path::kGeneric;
+}
+
+// Tokens per partition; 0 means "no split".
+int resolve_partition(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                      int block_size, int max_context_len, int partition_size, pa_dtype dt) {
+  const int group = num_kv_heads > 0 ? num_q_heads / num_kv_heads : 1;
+  if (choose_path(dt, head_dim, block_size, group) == Path::kGeneric) return 0;
+  if (partition_size < 0) return 0;
+  int p = partition_size;
+  if (p == 0) {
+    (void)num_seqs;
+    p = kDefaultPart;
+  }
+  if (max_context_len <= p) return 0;
+  return p;
+}
+
+struct WsLayout {
+  size_t m_off, l_off, o_off, total;
+};
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+WsLayout ws_layout(int num_seqs, int num_q_heads, int head_dim, int max_parts) {
+  WsLayout w{};
+  const size_t rows = (size_t)num_seqs * num_q_heads * max_parts;
+  w.m_off = 0;
+  w.l_off = round_up(rows * 4, 256);
+  w.o_off = w.l_off + round_up(rows * 4, 256);
+  w.total = w.o_off + round_up(rows * head_dim * 4, 256);
+  return w;
+}
+
+pa_status hip_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_EHIP; }
+
+template <typename T>
+bool copy_to_host(std::vector<T>& dst, const T* src, size_t n, hipStream_t s) {
+  dst.resize(n);
+  if (n == 0) return true;
+  if (hipMemcpyAsync(dst.data(), src, n * sizeof(T), hipMemcpyDeviceToHost, s) != hipSuccess)
+    return false;
+  return hipStreamSynchronize(s) == hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_strerror(pa_status s) {
+  switch (s) {
+    case PA_OK: return "success";
+    case PA_EINVAL: return "invalid argument";
+    case PA_ENOTSUP: return "unsupported dtype / head_dim / block_size";
+    case PA_ENOMEM: return "not enough free KV blocks";
+    case PA_EHIP: return "HIP runtime or launch failure";
+    case PA_EVALIDATE: return "device index data failed validation";
+    case PA_ENOENT: return "unknown or duplicate sequence id";
+  }
+  return "unknown status";
+}
+
+int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size, int32_t max_context_len,
+                                 int32_t partition_size, pa_dtype dtype) {
+  return resolve_partition(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                           max_context_len, partition_size, dtype);
+}
+
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size, int32_t max_context_len,
+                                 int32_t partition_size, pa_dtype dtype) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len <= 0) return 0;
+  const int p = resolve_partition(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                  max_context_len, partition_size, dtype);
+  if (p == 0) return 0;
+  const int max_parts = (max_context_len + p - 1) / p;
+  return ws_layout(num_seqs, num_q_heads, head_dim, max_parts).total;
+}
+
+pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* context_lens, float scale,
+                    int32_t block_size, int32_t num_kv_heads, int32_t num_seqs,
+                    int32_t num_q_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                    int32_t max_context_len, int64_t num_blocks, pa_dtype dtype,
+                    int32_t partition_size, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      block_size <= 0 || max_blocks_per_seq < 0 || max_context_len < 0 || num_blocks <= 0)
+    return PA_EINVAL;
+  if (!dtype_ok(dtype)) return PA_ENOTSUP;
+  if (num_q_heads % num_kv_heads != 0) return PA_EINVAL;
+  if (!std::isfinite(scale)) return PA_EINVAL;
+  if (!(head_dim == 16 || head_dim == 32 || head_dim == 64 || head_dim == 128 || head_dim == 256))
+    return PA_ENOTSUP;
+  if (!block_size_ok(block_size)) return PA_ENOTSUP;
+  if (partition_size > 0 && partition_size % kPartGranule != 0) return PA_EINVAL;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_EINVAL;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    return PA_EINVAL;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+
+  const int64_t cap64 = std::min<int64_t>((int64_t)max_context_len,
+                                          (int64_t)max_blocks_per_seq * block_size);
+  const int len_cap = (int)cap64;
+  const int group = num_q_heads / num_kv_heads;
+  const Path path = choose_path(dtype, head_dim, block_size, group);
+  const int p = resolve_partition(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                  max_context_len, partition_size, dtype);
+
+  DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.scale_log2e = scale * 1.4426950408889634f;
+  a.block_size = block_size;
+  a.num_kv_heads = num_kv_heads;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.head_dim = head_dim;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.len_cap = len_cap;
+  a.num_blocks = num_blocks;
+  if (p == 0) {
+    a.part = std::max(len_cap, 1);
+    // round up so partition arithmetic never sees 0 and steps stay aligned
+    a.part = (int)round_up((size_t)a.part, kPartGranule);
+    a.max_parts = 1;
+  } else {
+    a.part = p;
+    a.max_parts = std::max(1, (len_cap + p - 1) / p);
+    const WsLayout w = ws_layout(num_seqs, num_q_heads, head_dim,
+                                 (max_context_len + p - 1) / p);
+    if (!workspace || workspace_bytes < w.total || !aligned16(workspace)) return PA_EINVAL;
+    char* base = static_cast<char*>(workspace);
+    // partial arrays use the pitch of max_parts computed from len_cap
+    const WsLayout wl = ws_layout(num_seqs, num_q_heads, head_dim, a.max_parts);
+    a.ws_m = reinterpret_cast<float*>(base + wl.m_off);
+    a.ws_l = reinterpret_cast<float*>(base + wl.l_off);
+    a.ws_o = reinterpret_cast<float*>(base + wl.o_off);
+  }
+
+  if (validate_enabled()) {
+    std::vector<int32_t> lens, tab;
+    if (!copy_to_host(lens, context_lens, (size_t)num_seqs, s)) return PA_EHIP;
+    if (!copy_to_host(tab, block_tables, (size_t)num_seqs * max_blocks_per_seq, s))
+      return PA_EHIP;
+    for (int b = 0; b < num_seqs; ++b) {
+      if (lens[b] < 0 || lens[b] > len_cap) return PA_EVALIDATE;
+      const int nb = (lens[b] + block_size - 1) / block_size;
+      for (int j = 0; j < nb; ++j) {
+        const int32_t e = tab[(size_t)b * max_blocks_per_seq + j];
+        if (e < 0 || e >= num_blocks) return PA_EVALIDATE;
+      }
+    }
+  }
+
+  hipError_t e = hipSuccess;
+  switch (path) {
+    case Path::kMfma: e = launch_decode_mfma(a, dtype, s); break;
+    case Path::kValu: e = launch_decode_valu(a, dtype, s); break;
+    case Path::kGeneric: e = launch_decode_generic(a, dtype, s); break;
+  }
+  if (e != hipSuccess) return PA_EHIP;
+  if (a.max_parts > 1) e = launch_decode_reduce(a, dtype, s);
+  return hip_status(e);
+}
+
+pa_status pa_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,
+                               const int64_t* slot_mapping, int32_t num_tokens,
+                               int64_t k_token_stride, int64_t v_token_stride,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int64_t num_blocks, pa_dtype dtype, void* stream) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+    return PA_EINVAL;
+  if (!dtype_ok(dtype)) return PA_ENOTSUP;
+  if (!block_size_ok(block_size) || head_dim > 256) return PA_ENOTSUP;
+  const int es = elem_bytes(dtype);
+  if ((head_dim * es) % 16 != 0) return PA_ENOTSUP;
+  if (num_tokens == 0) return PA_OK;
+  if (!k || !v || !k_cache || !v_cache || !slot_mapping) return PA_EINVAL;
+  if (k_token_stride < (int64_t)num_kv_heads * head_dim ||
+      v_token_stride < (int64_t)num_kv_heads * head_dim)
+    return PA_EINVAL;
+  if ((k_token_stride * es) % 16 != 0 || (v_token_stride * es) % 16 != 0) return PA_EINVAL;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache))
+    return PA_EINVAL;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (validate_enabled()) {
+    std::vector<int64_t> slots;
+    if (!copy_to_host(slots, slot_mapping, (size_t)num_tokens, s)) return PA_EHIP;
+    std::unordered_set<int64_t> seen;
+    for (int64_t x : slots) {
+      if (x < 0) continue;
+      if (x >= num_blocks * block_size || !seen.insert(x).second) return PA_EVALIDATE;
+    }
+  }
+  return hip_status(launch_reshape_and_cache(k, v, k_cache, v_cache, slot_mapping, num_tokens,
+                                             k_token_stride, v_token_stride, num_kv_heads,
+                                             head_dim, block_size, num_blocks, es, s));
+}
+
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* src_dst_pairs,
+                         int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int64_t num_blocks, pa_dtype dtype, void* stream) {
+  if (num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+    return PA_EINVAL;
+  if (!dtype_ok(dtype)) return PA_ENOTSUP;
+  const int64_t block_bytes = (int64_t)num_kv_heads * block_size * head_dim * elem_bytes(dtype);
+  if (block_bytes % 16 != 0) return PA_ENOTSUP;
+  if (num_pairs == 0) return PA_OK;
+  if (!k_cache || !v_cache || !src_dst_pairs) return PA_EINVAL;
+  if (!aligned16(k_cache) || !aligned16(v_cache)) return PA_EINVAL;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (validate_enabled()) {
+    std::vector<int64_t> pr;
+    if (!copy_to_host(pr, src_dst_pairs, (size_t)num_pairs * 2, s)) return PA_EHIP;
+    std::unordered_set<int64_t> dsts, srcs;
+    for (int i = 0; i < num_pairs; ++i) {
+      const int64_t a = pr[2 * i], b = pr[2 * i + 1];
+      if (a < 0 || b < 0 || a >= num_blocks || b >= num_blocks) return PA_EVALIDATE;
+      if (!dsts.insert(b).second) return PA_EVALIDATE;
+      srcs.insert(a);
+    }
+    for (int64_t d : dsts)
+      if (srcs.count(d)) return PA_EVALIDATE;
+  }
+  return hip_status(
+      launch_copy_blocks(k_cache, v_cache, src_dst_pairs, num_pairs, block_bytes, num_blocks, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,107 @@
+// Internal declarations shared by libpa's HIP sources (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa.h"
+
+namespace pa {
+
+// ---------------------------------------------------------------- storage --
+// Tag types for the three storage dtypes.  Raw elements are moved as bits;
+// arithmetic is always fp32.
+struct F32 {
+  using raw = float;
+  static constexpr int bytes = 4;
+};
+struct F16 {
+  using raw = uint16_t;
+  static constexpr int bytes = 2;
+};
+struct BF16 {
+  using raw = uint16_t;
+  static constexpr int bytes = 2;
+};
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf168_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float lo_to_float(F16, uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+}
+__device__ __forceinline__ float hi_to_float(F16, uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+__device__ __forceinline__ float lo_to_float(BF16, uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_to_float(BF16, uint32_t w) {
+  return __uint_as_float(w & 0xffff0000u);
+}
+
+// fp32 -> storage bits, round to nearest even.
+__device__ __forceinline__ uint16_t to_bits(F16, float f) {
+  return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+__device__ __forceinline__ uint16_t to_bits(BF16, float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+__device__ __forceinline__ float to_bits(F32, float f) { return f; }
+
+// Dot product of two packed pairs accumulated in fp32.
+__device__ __forceinline__ float dot2(F16, uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c,
+                                false);
+}
+__device__ __forceinline__ float dot2(BF16, uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, a),
+                                         __builtin_bit_cast(bf162_t, b), c, false);
+}
+
+// ------------------------------------------------------------ decode args --
+struct DecodeArgs {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  float scale_log2e;   // scale * log2(e): scores live in the base-2 domain
+  int32_t block_size;
+  int32_t num_kv_heads;
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t head_dim;
+  int32_t max_blocks_per_seq;
+  int32_t len_cap;     // min(max_context_len, max_blocks_per_seq * block_size)
+  int64_t num_blocks;
+  int32_t part;        // tokens per partition (>= len_cap when nothing splits)
+  int32_t max_parts;   // ceil(len_cap / part)
+  // split workspace (valid when max_parts > 1)
+  float* ws_m;         // [num_seqs][num_q_heads][max_parts]
+  float* ws_l;         // same
+  float* ws_o;         // [num_seqs][num_q_heads][max_parts][head_dim]
+};
+
+// Launchers (return hipSuccess or the launch error).
+hipError_t launch_decode_valu(const DecodeArgs& a, pa_dtype dt, hipStream_t s);
+hipError_t launch_decode_mfma(const DecodeArgs& a, pa_dtype dt, hipStream_t s);
+hipError_t launch_decode_generic(const DecodeArgs& a, pa_dtype dt, hipStream_t s);
+hipError_t launch_decode_reduce(const DecodeArgs& a, pa_dtype dt, hipStream_t s);
+bool decode_valu_supported(pa_dtype dt, int head_dim, int block_size);
+bool decode_mfma_supported(pa_dtype dt, int head_dim, int block_size, int group);
+
+hipError_t launch_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,
+                                    const int64_t* slots, int32_t num_tokens, int64_t k_stride,
+                                    int64_t v_stride, int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t block_size, int64_t num_blocks, int elem_bytes,
+                                    hipStream_t s);
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs,
+                              int32_t num_pairs, int64_t block_bytes, int64_t num_blocks,
+                              hipStream_t s);
+
+__host__ __device__ inline int v_slab(int block_size) { return block_size < 16 ? block_size : 16; }
+
+}  // namespace pa

@@ -1,0 +1,130 @@
+"""pa_reshape_and_cache and pa_copy_blocks on the GPU: bit-exact against the
+oracle over the whole pools."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_118_amd as pa
+import workloads as W
+from tests.gpu_util import DEV, log
+
+pytestmark = pytest.mark.gpu
+
+
+def _pool(nb, hkv, bs, D, dtype, seed):
+    g = W.make_generator(seed, DEV)
+    k = W.randn(W.k_pool_shape(nb, hkv, bs, D), dtype, g, DEV)
+    v = W.randn(W.v_pool_shape(nb, hkv, bs, D), dtype, g, DEV)
+    return k, v
+
+
+@pytest.mark.parametrize("dtype,hkv,D,bs,T", [
+    ("f16", 40, 128, 16, 64),
+    ("bf16", 8, 128, 32, 37),
+    ("f16", 4, 128, 8, 100),
+    ("f16", 4, 128, 128, 300),
+    ("f32", 2, 16, 4, 2),
+    ("f32", 2, 64, 16, 33),
+    ("bf16", 3, 256, 16, 65),
+    ("f16", 2, 32, 2, 9),
+])
+def test_reshape_and_cache_bit_exact(dtype, hkv, D, bs, T):
+    log(f"[write] {dtype} hkv={hkv} D={D} bs={bs} T={T}")
+    nb = max(4, -(-T // bs) + 5)
+    rng = np.random.default_rng(T)
+    slots = rng.permutation(nb * bs)[:T].astype(np.int64)
+    slots[rng.random(T) < 0.1] = -1  # padding tokens are skipped
+    kc, vc = _pool(nb, hkv, bs, D, dtype, 1)
+    g = W.make_generator(2, DEV)
+    k, v = W.new_token_rows(T, hkv, D, dtype, g, DEV)
+    kr, vr = W.to_numpy_bits(kc).copy(), W.to_numpy_bits(vc).copy()
+    oracle.get().reshape_and_cache(W.to_numpy_bits(k), W.to_numpy_bits(v), kr, vr, slots, hkv, D,
+                                   bs, dtype)
+    pa.pa_reshape_and_cache(k, v, kc, vc, torch.from_numpy(slots).to(DEV), bs)
+    torch.cuda.synchronize()
+    assert np.array_equal(W.to_numpy_bits(kc), kr)
+    assert np.array_equal(W.to_numpy_bits(vc), vr)
+
+
+def test_reshape_and_cache_strided_rows():
+    """k and v as views into a fused [T][3][Hkv][D] buffer (token stride 3*Hkv*D)."""
+    T, hkv, D, bs, nb = 50, 4, 128, 16, 8
+    qkv = W.randn((T, 3, hkv, D), "f16", W.make_generator(3, DEV), DEV)
+    k, v = qkv[:, 1], qkv[:, 2]
+    slots = np.random.default_rng(0).permutation(nb * bs)[:T].astype(np.int64)
+    kc, vc = _pool(nb, hkv, bs, D, "f16", 4)
+    kr, vr = W.to_numpy_bits(kc).copy(), W.to_numpy_bits(vc).copy()
+    oracle.get().reshape_and_cache(W.to_numpy_bits(k.contiguous()), W.to_numpy_bits(v.contiguous()),
+                                   kr, vr, slots, hkv, D, bs, "f16")
+    pa.pa_reshape_and_cache(k, v, kc, vc, torch.from_numpy(slots).to(DEV), bs)
+    torch.cuda.synchronize()
+    assert np.array_equal(W.to_numpy_bits(kc), kr)
+    assert np.array_equal(W.to_numpy_bits(vc), vr)
+
+
+def test_reshape_and_cache_out_of_range_slot_is_skipped():
+    T, hkv, D, bs, nb = 4, 2, 128, 16, 3
+    kc, vc = _pool(nb, hkv, bs, D, "f16", 5)
+    k, v = W.new_token_rows(T, hkv, D, "f16", W.make_generator(6, DEV), DEV)
+    slots = np.array([1, nb * bs + 3, 5, -2], dtype=np.int64)
+    kr, vr = W.to_numpy_bits(kc).copy(), W.to_numpy_bits(vc).copy()
+    ok = slots.copy()
+    ok[1] = -1  # the oracle has no "beyond the pool": treat it as skipped
+    oracle.get().reshape_and_cache(W.to_numpy_bits(k), W.to_numpy_bits(v), kr, vr, ok, hkv, D, bs,
+                                   "f16")
+    pa.pa_reshape_and_cache(k, v, kc, vc, torch.from_numpy(slots).to(DEV), bs)
+    torch.cuda.synchronize()
+    assert np.array_equal(W.to_numpy_bits(kc), kr)
+    assert np.array_equal(W.to_numpy_bits(vc), vr)
+
+
+@pytest.mark.parametrize("dtype,hkv,D,bs,P", [
+    ("bf16", 40, 128, 16, 240),
+    ("f16", 8, 128, 32, 7),
+    ("f32", 2, 16, 4, 3),
+    ("f16", 72, 128, 128, 5),
+    ("f16", 2, 64, 8, 1),
+])
+def test_copy_blocks_bit_exact(dtype, hkv, D, bs, P):
+    log(f"[copy] {dtype} hkv={hkv} D={D} bs={bs} pairs={P}")
+    nb = 2 * P + 6
+    rng = np.random.default_rng(P)
+    ids = rng.permutation(nb)
+    pairs = np.stack([ids[:P], ids[P:2 * P]], axis=1).astype(np.int64)
+    kc, vc = _pool(nb, hkv, bs, D, dtype, 7)
+    kr, vr = W.to_numpy_bits(kc).copy(), W.to_numpy_bits(vc).copy()
+    oracle.get().copy_blocks(kr, vr, pairs, hkv, D, bs, dtype)
+    pa.pa_copy_blocks(kc, vc, torch.from_numpy(pairs).to(DEV), bs)
+    torch.cuda.synchronize()
+    assert np.array_equal(W.to_numpy_bits(kc), kr)
+    assert np.array_equal(W.to_numpy_bits(vc), vr)
+
+
+def test_validate_mode_rejects_bad_indices():
+    """PA_VALIDATE=1 checks device index data on the host (separate process
+    so the cached environment flag does not leak into other tests)."""
+    import subprocess
+    import sys
+    code = r"""
+import numpy as np, torch, paged_kv_cache_118_amd as pa
+dev = torch.device('cuda:0')
+kc = torch.zeros(4, 2, 16, 128, dtype=torch.float16, device=dev)
+vc = torch.zeros(4, 2, 1, 128, 16, dtype=torch.float16, device=dev)
+k = torch.zeros(2, 2, 128, dtype=torch.float16, device=dev)
+bad = torch.tensor([3, 3], dtype=torch.int64, device=dev)
+try:
+    pa.pa_reshape_and_cache(k, k, kc, vc, bad, 16); print('no error')
+except pa.PAError as e:
+    print('status', e.status)
+pairs = torch.tensor([[0, 1], [1, 2]], dtype=torch.int64, device=dev)
+try:
+    pa.pa_copy_blocks(kc, vc, pairs, 16); print('no error')
+except pa.PAError as e:
+    print('status', e.status)
+"""
+    env = dict(__import__("os").environ, PA_VALIDATE="1")
+    from tests.conftest import ROOT
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env,
+                       timeout=120, cwd=ROOT)
+    assert r.stdout.split("\n")[:2] == ["status -5", "status -5"], r.stdout + r.stderr

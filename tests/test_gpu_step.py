@@ -1,0 +1,236 @@
+"""Whole decode steps on the GPU -- copy-on-write, cache write, decode -- against
+the oracle running the same step on the CPU.
+
+The product side takes its slots, tables and copy pairs from libpa's block
+allocator; the oracle side from the reference block manager.  Physical ids
+differ between the two, so what is compared is what is unique: every
+sequence's logical K/V rows, and the attention outputs."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_118_amd as pa
+import workloads as W
+from oracle.alloc_ref import BlockPool
+from tests.gpu_util import DEV, TOL, gpu_decode, log, max_err, oracle_decode
+
+pytestmark = pytest.mark.gpu
+
+
+def test_tiny_step():
+    """Tiny worked example: lengths 5 and 9 after the step, block size 4, 8
+    blocks; the new tokens land at offset 0 of fresh blocks."""
+    spec = W.TINY
+    case = W.make_decode_case(spec, device="cpu", poison=True)
+    assert case.tables.shape == (2, 3) and (case.tables[0, 2] == -1)
+    gen = W.make_generator(spec.seed + 1, "cpu")
+    k_new, v_new = W.new_token_rows(2, 2, 16, "f32", gen, "cpu")
+    slots = W.slots_for_positions(case.tables, [(0, 4), (1, 8)], 4)
+    assert all(s % 4 == 0 for s in slots)
+    orc = oracle.get()
+    kr, vr = W.to_numpy_bits(case.k_cache).copy(), W.to_numpy_bits(case.v_cache).copy()
+    orc.reshape_and_cache(k_new.numpy(), v_new.numpy(), kr, vr, slots, 2, 16, 4, "f32")
+    want = orc.decode(case.q.numpy(), kr, vr, case.tables, case.lens, spec.scale, 4, 2, "f32")
+    kc, vc = case.k_cache.to(DEV), case.v_cache.to(DEV)
+    pa.pa_reshape_and_cache(k_new.to(DEV), v_new.to(DEV), kc, vc, torch.from_numpy(slots).to(DEV), 4)
+    dcase = W.DecodeCase(spec, case.lens, case.tables, case.num_blocks, case.q.to(DEV), kc, vc)
+    out = gpu_decode(dcase)
+    assert np.array_equal(kc.cpu().numpy(), kr, equal_nan=True)
+    assert np.array_equal(vc.cpu().numpy(), vr, equal_nan=True)
+    assert max_err(out, want) <= TOL["f32"]
+
+
+class _Side:
+    """One side of a paged step: an allocator and a pool."""
+
+    def __init__(self, gpu, nb, bs, hkv, D, dtype, seed):
+        self.gpu = gpu
+        self.bs = bs
+        self.alloc = pa.BlockAllocator(nb, bs, shuffle_seed=seed) if gpu else \
+            BlockPool(nb, bs, shuffle_seed=seed)
+        shape_k = W.k_pool_shape(nb, hkv, bs, D)
+        shape_v = W.v_pool_shape(nb, hkv, bs, D)
+        tdt = W.TORCH_DTYPE[dtype]
+        if gpu:
+            self.k = torch.full(shape_k, float("nan"), dtype=tdt, device=DEV)
+            self.v = torch.full(shape_v, float("nan"), dtype=tdt, device=DEV)
+        else:
+            self.k = W.to_numpy_bits(torch.full(shape_k, float("nan"), dtype=tdt)).copy()
+            self.v = W.to_numpy_bits(torch.full(shape_v, float("nan"), dtype=tdt)).copy()
+        self.hkv, self.D, self.dtype = hkv, D, dtype
+
+    # allocator calls with one interface
+    def add(self, sid, n):
+        self.alloc.add_seq(sid, n)
+
+    def fork(self, p, c):
+        self.alloc.fork(p, c)
+
+    def append(self, sid, n):
+        slots, pair = self.alloc.append(sid, n)
+        if not self.gpu:
+            pair = pair[0] if pair else None
+        return np.asarray(slots, dtype=np.int64), pair
+
+    def tables(self, ids, maxb):
+        if self.gpu:
+            return self.alloc.block_tables(ids, maxb)
+        t = np.full((len(ids), maxb), -1, dtype=np.int32)
+        lens = np.zeros(len(ids), dtype=np.int32)
+        for i, s in enumerate(ids):
+            row = self.alloc.tables[s]
+            t[i, :len(row)] = row
+            lens[i] = self.alloc.lens[s]
+        return t, lens
+
+    def write(self, k_rows, v_rows, slots):
+        if self.gpu:
+            pa.pa_reshape_and_cache(k_rows, v_rows, self.k, self.v,
+                                    torch.from_numpy(slots).to(DEV), self.bs)
+        else:
+            oracle.get().reshape_and_cache(W.to_numpy_bits(k_rows), W.to_numpy_bits(v_rows),
+                                           self.k, self.v, slots, self.hkv, self.D, self.bs,
+                                           self.dtype)
+
+    def copy(self, pairs):
+        if not pairs:
+            return
+        arr = np.asarray(pairs, dtype=np.int64).reshape(-1, 2)
+        if self.gpu:
+            pa.pa_copy_blocks(self.k, self.v, torch.from_numpy(arr).to(DEV), self.bs)
+        else:
+            oracle.get().copy_blocks(self.k, self.v, arr, self.hkv, self.D, self.bs, self.dtype)
+
+    def host_pools(self):
+        if self.gpu:
+            torch.cuda.synchronize()
+            return W.to_numpy_bits(self.k), W.to_numpy_bits(self.v)
+        return self.k, self.v
+
+
+def _logical_rows(k, v, table, L, bs):
+    """[L][Hkv][D] K and V rows of one sequence, read through its table with
+    numpy shaped indexing of the documented layout."""
+    vs = W.v_slab(bs)
+    ks = np.stack([k[table[u // bs], :, u % bs, :] for u in range(L)])
+    vv = np.stack([v[table[u // bs], :, (u % bs) // vs, :, (u % bs) % vs] for u in range(L)])
+    return ks, vv
+
+
+@pytest.mark.parametrize("groups,prefix,tail_hi,bs", [(2, 64, 64, 16), (3, 512, 512, 16),
+                                                      (2, 96, 40, 32)])
+def test_prefix_sharing_cow_step(groups, prefix, tail_hi, bs):
+    """Groups of 8 sequences share a prompt's full prefix blocks; each member
+    has its own tail, and its partial tail block is also held by a beam parent
+    (reference count 2).  One step: the allocator reports a copy-on-write pair
+    for each shared partial tail, pa_copy_blocks copies it, the new token is
+    written, and every member *and* every beam parent is decoded -- the
+    parents must not see their children's new tokens."""
+    log(f"[cow step] groups={groups} prefix={prefix} tails<= {tail_hi} bs={bs}")
+    hq = hkv = 4
+    D, dtype = 128, "bf16"
+    rng = np.random.default_rng(groups * 1000 + prefix)
+    members = groups * 8
+    tails = rng.integers(1, tail_hi + 1, size=members)
+    need = groups * (prefix // bs + 1) + sum(-(-(int(t) + 1) // bs) + 1 for t in tails)
+    nb = int(need * 1.25) + 8
+    gen = W.make_generator(7, DEV)
+    pre_k = [W.new_token_rows(prefix, hkv, D, dtype, gen, DEV) for _ in range(groups)]
+    own = [W.new_token_rows(int(t) - 1, hkv, D, dtype, gen, DEV) for t in tails]
+    new = W.new_token_rows(members, hkv, D, dtype, gen, DEV)
+    q = W.randn((2 * members, hq, D), dtype, gen, DEV)
+
+    sides = [_Side(True, nb, bs, hkv, D, dtype, 3), _Side(False, nb, bs, hkv, D, dtype, 4)]
+    results = []
+    for sd in sides:
+        n_pairs = 0
+        for gi in range(groups):
+            sd.add(10_000 + gi, 0)
+            slots, _ = sd.append(10_000 + gi, prefix)
+            sd.write(pre_k[gi][0], pre_k[gi][1], slots)
+        for c in range(members):
+            sd.fork(10_000 + c // 8, c)
+            if tails[c] > 1:
+                slots, pair = sd.append(c, int(tails[c]) - 1)
+                assert pair is None  # prefix blocks are full, nothing to copy
+                sd.write(own[c][0], own[c][1], slots)
+            sd.fork(c, 20_000 + c)  # beam parent: shares the partial tail
+        # the step: allocate, copy-on-write, write, decode
+        step_slots, pairs = [], []
+        for c in range(members):
+            slots, pair = sd.append(c, 1)
+            step_slots.append(int(slots[0]))
+            if pair:
+                pairs.append(pair)
+        sd.copy(pairs)
+        sd.write(new[0], new[1], np.array(step_slots, dtype=np.int64))
+        n_pairs = len(pairs)
+        ids = list(range(members)) + [20_000 + c for c in range(members)]
+        maxb = (prefix + tail_hi + bs) // bs + 1
+        tables, lens = sd.tables(ids, maxb)
+        results.append((tables, lens, n_pairs))
+        if sd.gpu:
+            spec = W.Spec("cow", dtype, hq, hkv, D, bs, len(ids), ("fixed", tuple(lens)))
+            gcase = W.DecodeCase(spec, lens, tables, nb, q, sd.k, sd.v)
+            gpu_out = gpu_decode(gcase)
+        else:
+            want = oracle.get().decode(W.to_numpy_bits(q), sd.k, sd.v, tables, lens,
+                                       1 / np.sqrt(D), bs, hkv, dtype)
+    (tg, lg, pg), (to, lo, po) = results
+    expect_pairs = int(sum((prefix + int(t) - 1) % bs != 0 for t in tails))
+    assert pg == po == expect_pairs
+    assert np.array_equal(lg, lo)
+    assert np.array_equal(lg[:members], prefix + tails)
+    assert np.array_equal(lg[members:], prefix + tails - 1)
+    kg, vg = sides[0].host_pools()
+    ko, vo = sides[1].host_pools()
+    for i, L in enumerate(lg):
+        a = _logical_rows(kg, vg, tg[i], int(L), bs)
+        b = _logical_rows(ko, vo, to[i], int(L), bs)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]), f"seq {i}"
+    err = max_err(gpu_out, want)
+    log(f"  pairs={pg} max abs err {err:.3e}")
+    assert err <= TOL[dtype]
+
+
+@pytest.mark.parametrize("bs", [8, 16, 32, 128])
+def test_mixed_chunk_write_and_decode_step(bs):
+    """66B-shaped mixed step at reduced size: two sequences write a 64-token
+    chunk, the rest write one token and decode."""
+    log(f"[mixed step] bs={bs}")
+    spec = W.OPT66B_SWEEP.with_(num_seqs=8, num_q_heads=4, num_kv_heads=4, block_size=bs,
+                                lengths=("uniform", 1, 1024))
+    rng = np.random.default_rng(bs)
+    before = W.draw_lengths(spec, rng)
+    chunk = 64
+    writers = [0, 1]
+    after = before.copy()
+    after[writers] += chunk
+    dec = [i for i in range(8) if i not in writers]
+    after[dec] += 1
+    case = W.make_decode_case(spec, device=DEV, poison=True, lens=after)
+    positions = [(s, p) for s in writers for p in range(int(before[s]), int(after[s]))] + \
+                [(s, int(after[s]) - 1) for s in dec]
+    slots = W.slots_for_positions(case.tables, positions, bs)
+    gen = W.make_generator(11, DEV)
+    k_new, v_new = W.new_token_rows(len(slots), 4, 128, "f16", gen, DEV)
+    kr, vr = W.to_numpy_bits(case.k_cache).copy(), W.to_numpy_bits(case.v_cache).copy()
+    orc = oracle.get()
+    orc.reshape_and_cache(W.to_numpy_bits(k_new), W.to_numpy_bits(v_new), kr, vr, slots, 4, 128,
+                          bs, "f16")
+    pa.pa_reshape_and_cache(k_new, v_new, case.k_cache, case.v_cache,
+                            torch.from_numpy(slots).to(DEV), bs)
+    torch.cuda.synchronize()
+    assert np.array_equal(W.to_numpy_bits(case.k_cache), kr)
+    assert np.array_equal(W.to_numpy_bits(case.v_cache), vr)
+    dspec = spec.with_(num_seqs=len(dec))
+    dcase = W.DecodeCase(dspec, after[dec].astype(np.int32), case.tables[dec], case.num_blocks,
+                         case.q[torch.tensor(dec, device=DEV)].contiguous(), case.k_cache,
+                         case.v_cache)
+    out = gpu_decode(dcase)
+    want = orc.decode(W.to_numpy_bits(dcase.q), kr, vr, dcase.tables, dcase.lens, spec.scale, bs,
+                      4, "f16")
+    err = max_err(out, want)
+    log(f"  max abs err {err:.3e}")
+    assert err <= TOL["f16"]
