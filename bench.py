@@ -49,6 +49,8 @@ def parse():
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--stream-probe", action="store_true",
+                    help="only measure plain device read / copy bandwidth (context for peak)")
     return ap.parse_args()
 
 
@@ -252,34 +254,45 @@ class Workload:
             self.config["unique_kv_bytes_per_step"] = self.unique_kv_bytes
         self._snapshot_for_oracle()
 
-    def _snapshot_for_oracle(self):
-        """Host copies of the sample the CPU baseline decodes, taken now --
-        before any libpa kernel has touched the pools."""
-        if self.args.no_cpu_baseline:
-            return
+    def _snapshot(self, k):
+        """Host copies of the first k sequences' q, blocks and renumbered
+        tables (taken before any libpa kernel has touched the pools)."""
         W, torch = self.W, self.torch
-        sp = self.spec
-        bs = sp.block_size
-        tok_heads = np.cumsum(self.lens.astype(np.int64)) * sp.num_q_heads
-        # sample size: about cpu_seconds of oracle work at ~0.1 M token-heads/s/thread
-        threads = max(1, len(os.sched_getaffinity(0)))
-        budget = self.args.cpu_seconds * 0.15e6 * threads
-        k = int(np.searchsorted(tok_heads, budget)) + 1
-        k = max(1, min(k, len(self.lens)))
-        seqs = list(range(k))
-        used = sorted({int(b) for s in seqs for b in self.tables[s, :W.blocks_needed(
+        bs = self.spec.block_size
+        used = sorted({int(b) for s in range(k) for b in self.tables[s, :W.blocks_needed(
             int(self.lens[s]), bs)]})
         remap = {b: i for i, b in enumerate(used)}
         t = np.full((k, self.tables.shape[1]), -1, dtype=np.int32)
-        for i, s in enumerate(seqs):
+        for s in range(k):
             n = W.blocks_needed(int(self.lens[s]), bs)
-            t[i, :n] = [remap[int(b)] for b in self.tables[s, :n]]
-        idx = torch.tensor(used, dtype=torch.long, device=self.dev)
-        qsel = self.q[0] if self.decode_idx is None else self.q[0]
-        self._host = dict(
-            q=W.to_numpy_bits(qsel[:k]), k=W.to_numpy_bits(self.k[0].index_select(0, idx)),
-            v=W.to_numpy_bits(self.v[0].index_select(0, idx)), tables=t,
-            lens=self.lens[:k].copy(), seqs=k)
+            t[s, :n] = [remap[int(b)] for b in self.tables[s, :n]]
+        idx = torch.tensor(used or [0], dtype=torch.long, device=self.dev)
+        return dict(q=W.to_numpy_bits(self.q[0][:k]),
+                    k=W.to_numpy_bits(self.k[0].index_select(0, idx)),
+                    v=W.to_numpy_bits(self.v[0].index_select(0, idx)), tables=t,
+                    lens=self.lens[:k].copy(), seqs=k)
+
+    def _run_oracle(self, h, threads):
+        import oracle
+        sp = self.spec
+        t = time.perf_counter()
+        oracle.get().decode(h["q"], h["k"], h["v"], h["tables"], h["lens"], sp.scale,
+                            sp.block_size, sp.num_kv_heads, sp.dtype, nthreads=threads)
+        return time.perf_counter() - t
+
+    def _snapshot_for_oracle(self):
+        """Pick the CPU-baseline sample: time the oracle on the first sequence,
+        then take as many sequences as fit in about --cpu-seconds."""
+        if self.args.no_cpu_baseline:
+            return
+        threads = max(1, len(os.sched_getaffinity(0)))
+        self.threads = threads
+        h1 = self._snapshot(1)
+        dt1 = max(self._run_oracle(h1, threads), 1e-4)
+        per_token = dt1 / max(1, int(self.lens[0]))
+        cum = np.cumsum(self.lens.astype(np.int64))
+        k = int(np.searchsorted(cum, self.args.cpu_seconds / per_token, side="right"))
+        self._host = self._snapshot(max(1, min(k, len(self.lens))))
 
     # -- the timed step ----------------------------------------------------
     def step(self, r, ev=None):
@@ -298,20 +311,35 @@ class Workload:
 
     # -- CPU baseline --------------------------------------------------------
     def cpu_baseline(self, seconds):
-        import oracle
         h = self._host
-        sp = self.spec
-        threads = max(1, len(os.sched_getaffinity(0)))
-        orc = oracle.get()
-        t = time.perf_counter()
-        orc.decode(h["q"], h["k"], h["v"], h["tables"], h["lens"], sp.scale, sp.block_size,
-                   sp.num_kv_heads, sp.dtype, nthreads=threads)
-        dt = time.perf_counter() - t
+        dt = self._run_oracle(h, self.threads)
         kv = int(np.sum(h["lens"].astype(np.int64))) * self._tok_bytes()
-        return {"value": round(kv / 1e9 / dt, 4), "unit": "GB/s", "cores": threads,
+        return {"value": round(kv / 1e9 / dt, 4), "unit": "GB/s", "cores": self.threads,
                 "kind": "oracle", "seconds": round(dt, 3),
                 "sample": f"fp64 oracle decode of the first {h['seqs']} of {len(self.lens)} "
-                          f"sequences ({kv / 1e6:.1f} MB of K/V), all q heads"}
+                          f"sequences ({kv / 1e6:.1f} MB of K/V, all q heads), "
+                          f"{self.threads} threads"}
+
+
+def stream_probe(torch, gib=4, reps=10):
+    """Plain torch device kernels over a 4 GiB buffer: a read-only reduction
+    and a copy.  Reported as context for the 8 TB/s nominal peak."""
+    n = gib << 30
+    x = torch.ones(n // 2, dtype=torch.float16, device="cuda")
+    y = torch.empty_like(x)
+    res = {}
+    for name, fn, bytes_moved in (("sum_read", lambda: x.sum(), n),
+                                  ("copy", lambda: y.copy_(x), 2 * n)):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        res[name + "_GBps"] = round(bytes_moved * reps / (a.elapsed_time(b) / 1e3) / 1e9, 1)
+    return res
 
 
 def build_workload(args, dev):
@@ -335,25 +363,34 @@ def main():
         print(json.dumps({"calib_copy_bytes": n, "launches": 5}))
         return
 
+    if args.stream_probe:
+        print(json.dumps(stream_probe(torch)), flush=True)
+        return
+
     dev = torch.device("cuda:0")
     wl = build_workload(args, dev)
     torch.cuda.synchronize()
 
-    stream = torch.cuda.current_stream()
-    # host allocator cost per step (its outputs are the resident inputs below)
     for i in range(args.warmup):
         wl.step(i % wl.replicas)
     torch.cuda.synchronize()
 
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    torch.cuda.synchronize()
+    # timed region 1: K whole steps back to back (the value)
     t0 = time.perf_counter()
     for i in range(args.steps):
-        wl.step(i % wl.replicas, ev[i])
+        wl.step(i % wl.replicas)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
+
+    # timed region 2: the same K steps with HIP events around each pa_decode
+    # call, on the stream it runs on (the roofline's kernel duration)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        wl.step(i % wl.replicas, ev[i])
+    torch.cuda.synchronize()
     dec_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
 
     kv_gb = wl.kv_read_bytes / 1e9

@@ -31,13 +31,15 @@
  *    out-of-range id, a duplicate slot or an overlapping copy pair.
  *
  * KV pool layout (one layer).  BS = block_size, D = head_dim, Hkv = kv heads,
- * VS = min(BS, 16).  Element (physical block b, kv head h, offset o, dim d):
+ * VS = min(BS, 8).  Element (physical block b, kv head h, offset o, dim d):
  *   K:  k_cache[((b*Hkv + h)*BS + o)*D + d]
  *   V:  v_cache[(((b*Hkv + h)*(BS/VS) + o/VS)*D + d)*VS + o%VS]
  *  K stores token rows; V stores slabs of VS tokens, each slab [D][VS]
- *  (token index fastest), so that one wavefront reads a whole 16-token slab
- *  of either pool with contiguous 16-byte loads.  A token's slot is
- *  b*BS + o ([P4]).  BS must be 1, 2, 4, 8, 16 or a multiple of 16.
+ *  (token index fastest): one 16-byte load is 8 tokens of one V row, which
+ *  is what the weighted sum over tokens consumes (a VALU lane per row, or an
+ *  MFMA operand for grouped heads), and a wavefront reads each slab with
+ *  fully contiguous 16-byte loads.  A token's slot is b*BS + o ([P4]).
+ *  BS must be 1, 2, 4, 8 or a multiple of 16.
  */
 #ifndef PA_H
 #define PA_H
@@ -86,10 +88,16 @@ const char* pa_strerror(pa_status s);
  *               L <= max_context_len and L <= max_blocks_per_seq * BS;
  *               positions beyond either bound are ignored.
  *  scale        score scale (1/sqrt(head_dim) for standard attention)
- *  partition_size  tokens per work item: 0 = library choice, -1 = never
- *               split a sequence, > 0 = that many (a multiple of 256).  Split
- *               sequences are merged by a second kernel from per-partition
- *               fp32 (max, sum, unnormalised output).
+ *  partition_size  how the work is divided among wavefronts:
+ *               0  = token-balanced: all (sequence, head) items are laid end
+ *                    to end and every wavefront of one full-chip round takes
+ *                    an equal share of the tokens, whatever the lengths;
+ *               -1 = one wavefront per (sequence, head) item, nothing split;
+ *               >0 = each wavefront takes that many tokens of the stream (a
+ *                    multiple of 256).
+ *               An item shared by several wavefronts is merged exactly by a
+ *               second kernel from fp32 (max, sum, unnormalised output)
+ *               partials; results agree across modes within rounding.
  *  workspace    device scratch of at least pa_decode_workspace_bytes(...)
  *               bytes (may be NULL when that size is 0); contents need no
  *               initialisation and are clobbered.
@@ -105,12 +113,14 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
                     void* stream);
 
 /* Workspace bytes pa_decode needs for these sizes (0 when nothing splits).
- * Pass the same partition_size, head counts and block_size as to pa_decode. */
+ * Pass the same arguments as to pa_decode, on the device it will run on (the
+ * balanced split sizes itself by the device's CU count). */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t block_size, int32_t max_context_len,
                                  int32_t partition_size, pa_dtype dtype);
 
-/* The partition size pa_decode uses for these arguments (0 = no split). */
+/* The split pa_decode uses for these arguments: -1 = one wavefront per
+ * item, 0 = token-balanced, > 0 = fixed tokens per wavefront. */
 int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t block_size, int32_t max_context_len,
                                  int32_t partition_size, pa_dtype dtype);

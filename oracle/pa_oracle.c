@@ -35,7 +35,7 @@
  * Pool layout (the product's documented layout, re-implemented here):
  *   K element (blk, h, off, d)  at  ((blk*Hkv + h)*BS + off)*D + d
  *   V element (blk, h, off, d)  at  (((blk*Hkv + h)*(BS/VS) + off/VS)*D + d)*VS + off%VS
- *   with VS = min(BS, 16): V is stored as 16-token slabs, each slab [D][VS].
+ *   with VS = min(BS, 8): V is stored as 8-token slabs, each slab [D][VS].
  *
  * Parity status of each function: see the module docstring of the Python
  * wrapper; every function here is pinned by CPU tests.
@@ -83,7 +83,7 @@ static double load_elem(const void* base, int dtype, int64_t i) {
   return dtype == OR_F16 ? half_bits_to_double(bits) : bf16_bits_to_double(bits);
 }
 
-static int v_slab(int bs) { return bs < 16 ? bs : 16; }
+static int v_slab(int bs) { return bs < 8 ? bs : 8; }
 
 static int64_t k_index(int64_t blk, int h, int off, int d, int hkv, int bs, int D) {
   return ((blk * hkv + h) * bs + off) * (int64_t)D + d;

@@ -6,7 +6,7 @@ of the computation runs in libpa's HIP kernels.  PyTorch supplies device
 memory and streams.  If ``libpa.so`` has not been built this module raises
 ImportError -- there is no fallback implementation.
 
-Pool layout (BS = block_size, D = head_dim, VS = min(BS, 16)):
+Pool layout (BS = block_size, D = head_dim, VS = min(BS, 8)):
     k_cache: [num_blocks, Hkv, BS, D]
     v_cache: [num_blocks, Hkv, BS // VS, D, VS]
 """
@@ -120,7 +120,7 @@ def _dtype_code(t: torch.Tensor) -> int:
 
 
 def v_slab(block_size: int) -> int:
-    return block_size if block_size < 16 else 16
+    return block_size if block_size < 8 else 8
 
 
 # ---------------------------------------------------------------- decode --

@@ -12,16 +12,16 @@ namespace pa {
 
 namespace {
 
-constexpr int kWriteTokens = 32;  // tokens per workgroup in the cache write
 constexpr int kThreads = 256;
 
-// One workgroup = kWriteTokens consecutive tokens of one kv head.
+// One workgroup = TT consecutive tokens of one kv head, 8*TT threads (TT = 32
+// for large writes, 8 for decode-sized ones so more CUs share the stores).
 //  K: token rows are contiguous on both sides -> 16-byte vector copies.
 //  V: the pool stores 16-token slabs [D][VS]; rows are staged in LDS and each
 //     lane then writes one token's element, so lanes with consecutive slots
 //     write consecutive addresses of a slab row.
-template <int ES>
-__global__ __launch_bounds__(kThreads) void reshape_and_cache_kernel(
+template <int ES, int TT>
+__global__ __launch_bounds__(8 * TT) void reshape_and_cache_kernel(
     const char* __restrict__ k, const char* __restrict__ v, char* __restrict__ k_cache,
     char* __restrict__ v_cache, const int64_t* __restrict__ slots, int32_t num_tokens,
     int64_t k_stride, int64_t v_stride, int32_t hkv, int32_t D, int32_t bs, int64_t num_blocks) {
@@ -30,14 +30,15 @@ __global__ __launch_bounds__(kThreads) void reshape_and_cache_kernel(
   const int row_bytes = D * ES;
   const int lds_stride = row_bytes + 4;  // pad: consecutive tokens hit different banks
   const int h = blockIdx.y;
-  const int t0 = blockIdx.x * kWriteTokens;
-  const int nt = min(kWriteTokens, num_tokens - t0);
+  constexpr int NT = 8 * TT;
+  const int t0 = blockIdx.x * TT;
+  const int nt = min(TT, num_tokens - t0);
   const int64_t max_slot = num_blocks * (int64_t)bs;
   const int vs = v_slab(bs);
 
   // K rows (and V rows into LDS): one 16-byte chunk per thread per iteration.
   const int chunks = row_bytes / 16;
-  for (int i = threadIdx.x; i < nt * chunks; i += kThreads) {
+  for (int i = threadIdx.x; i < nt * chunks; i += NT) {
     const int tt = i / chunks, c = i % chunks;
     const int64_t t = t0 + tt;
     const int64_t slot = slots[t];
@@ -60,8 +61,8 @@ __global__ __launch_bounds__(kThreads) void reshape_and_cache_kernel(
   __syncthreads();
 
   // V elements: lane = token (fastest), threads stride over d.
-  const int tt = threadIdx.x % kWriteTokens;
-  const int dgrp = threadIdx.x / kWriteTokens;
+  const int tt = threadIdx.x % TT;
+  const int dgrp = threadIdx.x / TT;
   if (tt >= nt) return;
   const int64_t slot = slots[t0 + tt];
   if (slot < 0 || slot >= max_slot) return;
@@ -70,7 +71,7 @@ __global__ __launch_bounds__(kThreads) void reshape_and_cache_kernel(
   E* vdst = reinterpret_cast<E*>(v_cache) + ((blk * hkv + h) * (bs / vs) + off / vs) * (int64_t)D * vs +
             off % vs;
   const E* src = reinterpret_cast<const E*>(smem + tt * lds_stride);
-  for (int d = dgrp; d < D; d += kThreads / kWriteTokens) vdst[(int64_t)d * vs] = src[d];
+  for (int d = dgrp; d < D; d += NT / TT) vdst[(int64_t)d * vs] = src[d];
 }
 
 // Whole-block copies: block b of either pool is one contiguous run of
@@ -96,6 +97,22 @@ __global__ __launch_bounds__(kThreads) void copy_blocks_kernel(char* __restrict_
   }
 }
 
+template <int TT>
+void launch_rc(const void* k, const void* v, void* k_cache, void* v_cache, const int64_t* slots,
+               int32_t num_tokens, int64_t k_stride, int64_t v_stride, int32_t hkv, int32_t D,
+               int32_t bs, int64_t num_blocks, int es, hipStream_t s) {
+  dim3 grid((num_tokens + TT - 1) / TT, hkv);
+  const size_t lds = (size_t)TT * (D * es + 4);
+  if (es == 4)
+    hipLaunchKernelGGL((reshape_and_cache_kernel<4, TT>), grid, dim3(8 * TT), lds, s,
+                       (const char*)k, (const char*)v, (char*)k_cache, (char*)v_cache, slots,
+                       num_tokens, k_stride, v_stride, hkv, D, bs, num_blocks);
+  else
+    hipLaunchKernelGGL((reshape_and_cache_kernel<2, TT>), grid, dim3(8 * TT), lds, s,
+                       (const char*)k, (const char*)v, (char*)k_cache, (char*)v_cache, slots,
+                       num_tokens, k_stride, v_stride, hkv, D, bs, num_blocks);
+}
+
 }  // namespace
 
 hipError_t launch_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,
@@ -104,18 +121,12 @@ hipError_t launch_reshape_and_cache(const void* k, const void* v, void* k_cache,
                                     int32_t block_size, int64_t num_blocks, int elem_bytes,
                                     hipStream_t s) {
   if (num_tokens == 0) return hipSuccess;
-  dim3 grid((num_tokens + kWriteTokens - 1) / kWriteTokens, num_kv_heads);
-  const size_t lds = (size_t)kWriteTokens * (head_dim * elem_bytes + 4);
-  if (elem_bytes == 4)
-    hipLaunchKernelGGL(reshape_and_cache_kernel<4>, grid, dim3(kThreads), lds, s,
-                       (const char*)k, (const char*)v, (char*)k_cache, (char*)v_cache, slots,
-                       num_tokens, k_stride, v_stride, num_kv_heads, head_dim, block_size,
-                       num_blocks);
+  if (num_tokens >= 1024)
+    launch_rc<32>(k, v, k_cache, v_cache, slots, num_tokens, k_stride, v_stride, num_kv_heads,
+                  head_dim, block_size, num_blocks, elem_bytes, s);
   else
-    hipLaunchKernelGGL(reshape_and_cache_kernel<2>, grid, dim3(kThreads), lds, s,
-                       (const char*)k, (const char*)v, (char*)k_cache, (char*)v_cache, slots,
-                       num_tokens, k_stride, v_stride, num_kv_heads, head_dim, block_size,
-                       num_blocks);
+    launch_rc<8>(k, v, k_cache, v_cache, slots, num_tokens, k_stride, v_stride, num_kv_heads,
+                 head_dim, block_size, num_blocks, elem_bytes, s);
   return hipGetLastError();
 }
 

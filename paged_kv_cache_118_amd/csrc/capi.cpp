@@ -16,10 +16,28 @@ using namespace pa;
 
 namespace {
 
-constexpr int kPartGranule = 256;  // partitions are a multiple of this many tokens
-constexpr int kDefaultPart = 512;
+constexpr int kPartGranule = 256;  // fixed chunks are a multiple of this many tokens
 // A GQA group this large or larger goes to the matrix cores.
 constexpr int kMfmaMinGroup = 4;
+// The token-balanced split keeps per-sequence prefix sums in LDS.
+constexpr int kMaxSplitSeqs = 8192;
+// Resident wavefronts per CU of each kernel (its occupancy): one round of
+// workers fills the chip.
+constexpr int kValuWavesPerCu = 16;
+constexpr int kMfmaWavesPerCu = 8;
+
+// Tuning override of the workers per CU (PA_VALU_WAVES_PER_CU,
+// PA_MFMA_WAVES_PER_CU); the default is the kernel's occupancy.
+int waves_per_cu(bool mfma) {
+  static int v[2] = {-1, -1};
+  int& x = v[mfma ? 1 : 0];
+  if (x < 0) {
+    const char* e = std::getenv(mfma ? "PA_MFMA_WAVES_PER_CU" : "PA_VALU_WAVES_PER_CU");
+    const int def = mfma ? kMfmaWavesPerCu : kValuWavesPerCu;
+    x = (e && std::atoi(e) > 0 && std::atoi(e) <= 64) ? std::atoi(e) : def;
+  }
+  return x;
+}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -40,6 +58,15 @@ bool validate_enabled() {
   return v == 1;
 }
 
+int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    return 256;
+  return cus;
+}
+
 enum class Path { kValu, kMfma, kGeneric };
 
 Path choose_path(pa_dtype dt, int head_dim, int block_size, int group) {
@@ -49,35 +76,53 @@ Path choose_path(pa_dtype dt, int head_dim, int block_size, int group) {
   return Path::kGeneric;
 }
 
-// Tokens per partition; 0 means "no split".
-int resolve_partition(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
-                      int block_size, int max_context_len, int partition_size, pa_dtype dt) {
-  const int group = num_kv_heads > 0 ? num_q_heads / num_kv_heads : 1;
-  if (choose_path(dt, head_dim, block_size, group) == Path::kGeneric) return 0;
-  if (partition_size < 0) return 0;
-  int p = partition_size;
-  if (p == 0) {
-    (void)num_seqs;
-    p = kDefaultPart;
-  }
-  if (max_context_len <= p) return 0;
-  return p;
-}
-
-struct WsLayout {
-  size_t m_off, l_off, o_off, total;
+// How one pa_decode call divides its work (decode_split.h).
+struct Plan {
+  Path path;
+  int split;        // 0: one worker per item, 1: token-balanced split
+  int step;         // tokens per worker step
+  int items_per_seq;
+  int rows_per_item;
+  int chunk_steps;  // split 1: fixed steps per worker, 0 = balanced
+  int num_workers;
+  size_t ws_bytes;
+  size_t m_off, l_off, o_off, desc_off;
 };
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-WsLayout ws_layout(int num_seqs, int num_q_heads, int head_dim, int max_parts) {
-  WsLayout w{};
-  const size_t rows = (size_t)num_seqs * num_q_heads * max_parts;
-  w.m_off = 0;
-  w.l_off = round_up(rows * 4, 256);
-  w.o_off = w.l_off + round_up(rows * 4, 256);
-  w.total = w.o_off + round_up(rows * head_dim * 4, 256);
-  return w;
+Plan make_plan(int num_seqs, int hq, int hkv, int head_dim, int block_size, int len_cap,
+               int partition_size, pa_dtype dt) {
+  Plan p{};
+  const int group = hkv > 0 ? hq / hkv : 1;
+  p.path = choose_path(dt, head_dim, block_size, group);
+  p.step = p.path == Path::kMfma ? 32 : 16;
+  p.items_per_seq = p.path == Path::kMfma ? hkv : hq;
+  p.rows_per_item = p.path == Path::kMfma ? group : 1;
+  const int64_t items = (int64_t)num_seqs * p.items_per_seq;
+  const int64_t max_steps = items * ((int64_t)(len_cap + p.step - 1) / p.step);
+  p.split = (p.path != Path::kGeneric && partition_size >= 0 && len_cap > 0 &&
+             num_seqs <= kMaxSplitSeqs && max_steps < (int64_t)1 << 30)
+                ? 1
+                : 0;
+  if (!p.split) {
+    p.num_workers = (int)items;
+    return p;
+  }
+  if (partition_size > 0) {
+    p.chunk_steps = std::max(1, partition_size / p.step);
+    p.num_workers = (int)((max_steps + p.chunk_steps - 1) / p.chunk_steps);
+  } else {
+    p.chunk_steps = 0;
+    p.num_workers = device_cus() * waves_per_cu(p.path == Path::kMfma);
+  }
+  const size_t rows = (size_t)(items + p.num_workers) * p.rows_per_item;
+  p.m_off = 0;
+  p.l_off = round_up(rows * 4, 256);
+  p.o_off = p.l_off + round_up(rows * 4, 256);
+  p.desc_off = p.o_off + round_up(rows * head_dim * 4, 256);
+  p.ws_bytes = p.desc_off + round_up((size_t)items * 8, 256);
+  return p;
 }
 
 pa_status hip_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_EHIP; }
@@ -111,19 +156,22 @@ const char* pa_strerror(pa_status s) {
 int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t block_size, int32_t max_context_len,
                                  int32_t partition_size, pa_dtype dtype) {
-  return resolve_partition(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_context_len <= 0) return -1;
+  const Plan p = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                            max_context_len, partition_size, dtype);
+  if (!p.split) return -1;
+  return p.chunk_steps * p.step;
 }
 
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t block_size, int32_t max_context_len,
                                  int32_t partition_size, pa_dtype dtype) {
-  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len <= 0) return 0;
-  const int p = resolve_partition(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
-                                  max_context_len, partition_size, dtype);
-  if (p == 0) return 0;
-  const int max_parts = (max_context_len + p - 1) / p;
-  return ws_layout(num_seqs, num_q_heads, head_dim, max_parts).total;
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      max_context_len <= 0)
+    return 0;
+  return make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_context_len,
+                   partition_size, dtype)
+      .ws_bytes;
 }
 
 pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -152,10 +200,11 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   const int64_t cap64 = std::min<int64_t>((int64_t)max_context_len,
                                           (int64_t)max_blocks_per_seq * block_size);
   const int len_cap = (int)cap64;
-  const int group = num_q_heads / num_kv_heads;
-  const Path path = choose_path(dtype, head_dim, block_size, group);
-  const int p = resolve_partition(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
-                                  max_context_len, partition_size, dtype);
+  // the workspace size depends on max_context_len only (what the caller sized it with)
+  const Plan sized = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                               max_context_len, partition_size, dtype);
+  Plan p = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, len_cap,
+                     partition_size, dtype);
 
   DecodeArgs a{};
   a.out = out;
@@ -173,23 +222,17 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.len_cap = len_cap;
   a.num_blocks = num_blocks;
-  if (p == 0) {
-    a.part = std::max(len_cap, 1);
-    // round up so partition arithmetic never sees 0 and steps stay aligned
-    a.part = (int)round_up((size_t)a.part, kPartGranule);
-    a.max_parts = 1;
-  } else {
-    a.part = p;
-    a.max_parts = std::max(1, (len_cap + p - 1) / p);
-    const WsLayout w = ws_layout(num_seqs, num_q_heads, head_dim,
-                                 (max_context_len + p - 1) / p);
-    if (!workspace || workspace_bytes < w.total || !aligned16(workspace)) return PA_EINVAL;
+  a.split = p.split;
+  a.chunk_steps = p.chunk_steps;
+  a.num_workers = p.num_workers;
+  if (p.split) {
+    if (p.ws_bytes > sized.ws_bytes) return PA_EINVAL;  // cannot happen: len_cap <= max
+    if (!workspace || workspace_bytes < p.ws_bytes || !aligned16(workspace)) return PA_EINVAL;
     char* base = static_cast<char*>(workspace);
-    // partial arrays use the pitch of max_parts computed from len_cap
-    const WsLayout wl = ws_layout(num_seqs, num_q_heads, head_dim, a.max_parts);
-    a.ws_m = reinterpret_cast<float*>(base + wl.m_off);
-    a.ws_l = reinterpret_cast<float*>(base + wl.l_off);
-    a.ws_o = reinterpret_cast<float*>(base + wl.o_off);
+    a.ws_m = reinterpret_cast<float*>(base + p.m_off);
+    a.ws_l = reinterpret_cast<float*>(base + p.l_off);
+    a.ws_o = reinterpret_cast<float*>(base + p.o_off);
+    a.ws_desc = reinterpret_cast<int2*>(base + p.desc_off);
   }
 
   if (validate_enabled()) {
@@ -208,13 +251,13 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   }
 
   hipError_t e = hipSuccess;
-  switch (path) {
+  switch (p.path) {
     case Path::kMfma: e = launch_decode_mfma(a, dtype, s); break;
     case Path::kValu: e = launch_decode_valu(a, dtype, s); break;
     case Path::kGeneric: e = launch_decode_generic(a, dtype, s); break;
   }
   if (e != hipSuccess) return PA_EHIP;
-  if (a.max_parts > 1) e = launch_decode_reduce(a, dtype, s);
+  if (p.split) e = launch_decode_merge(a, dtype, p.items_per_seq, s);
   return hip_status(e);
 }
 

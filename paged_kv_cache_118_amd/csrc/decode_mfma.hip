@@ -7,22 +7,25 @@
 // The G q rows of one kv head form a real, if small, dense contraction, so
 // each K and V element is read from HBM once per kv head and used G times.
 //
-// Work item = (partition, kv head, sequence); four wavefronts per workgroup,
-// each streaming 32-token groups.  With lane = 16*kb + n (n = lane % 16,
+// Work items are (sequence, kv head); every wavefront is an independent
+// worker streaming an equal share of all items' 32-token groups
+// (decode_split.h).  With lane = 16*kb + n (n = lane % 16,
 // kb = lane / 16) and v_mfma_f32_16x16x32 (A: row n, k-slots of group kb;
 // B: column n, same k-slots; C: column n, rows 4*kb .. 4*kb+3):
 //   S^T = K Q^T  : A = K rows (tokens), B = Q^T (heads, zero past G), two
-//                  16-token tiles x D/32 k-steps.  Tile j's row r holds
+//                  16-token tiles x D/32 k-steps (k-step s, group kb: d =
+//                  32*s + 8*kb .. +7, a contiguous 64 B per row per load).  Tile j's row r holds
 //                  token 8*(r/4) + 4*j + r%4, so lane (n, kb) ends up with
 //                  the scores of head n for the 8 tokens 8*kb .. 8*kb+7.
 //   O^T += V^T P^T : A = V^T (16 d rows, 8 tokens per k-group, read as one
-//                  16-byte run of a [D][16] V slab), B = P^T, which is
+//                  16-byte row of an 8-token [D][8] V slab), B = P^T, which is
 //                  exactly the lane's 8 weights; C = O^T keeps head n in lane
 //                  n for every d tile, so the online-softmax rescale of the
 //                  accumulators needs no data exchange.
 // Only the max / sum over the 4 k-groups of a head crosses lanes (xor 16, 32).
 #include <math.h>
 
+#include "decode_split.h"
 #include "pa_internal.h"
 
 namespace pa {
@@ -75,60 +78,93 @@ struct TableWindow {
   }
 };
 
-template <typename TT, int D, int VS>
-__global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeArgs a) {
+template <typename TT, int D>
+__global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeArgs a) {
+  constexpr int VS = 8;       // V slab width (tokens)
   constexpr int EB = 2;
   constexpr int KN = D / 32;  // uint4 per lane per K tile (= QK k-steps)
   constexpr int MT = D / 16;  // d tiles of O^T
-  constexpr int OST = D + 4;  // LDS row pitch of the merge buffer (floats)
+  extern __shared__ int smem[];  // split 1: s_pre[B+1], s_len[B]
 
-  __shared__ float s_m[kWaves][16], s_l[kWaves][16];
-  __shared__ float s_o[kWaves][16][OST];
-
-  const int p = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int worker = blockIdx.x * kWaves + wv;
   const int n = lane & 15, kb = lane >> 4;
+  const int H = a.num_kv_heads, B = a.num_seqs;
   const int G = a.num_q_heads / a.num_kv_heads;
   const int bs = a.block_size;
-  int L = a.context_lens[b];
-  L = L < 0 ? 0 : (L > a.len_cap ? a.len_cap : L);
-  const int t0 = p * a.part;
-  const int64_t head0 = (int64_t)b * a.num_q_heads + (int64_t)g * G;  // first q row
-  if (t0 >= L) {
-    if (p == 0)
-      for (int i = threadIdx.x; i < G * D; i += kThreads) store_out<TT>(a.out, head0 * D + i, 0.f);
-    return;
+  const int64_t hkv = a.num_kv_heads;
+  int* s_pre = smem;
+  int* s_len = smem + B + 1;
+
+  Cursor c0;
+  int count;
+  int C = 0, x0 = 0;  // split 1: steps per worker, first stream step of this worker
+  if (a.split) {
+    if (wv == 0) wave_scan_steps(a.context_lens, B, H, a.len_cap, kGroup, s_pre, s_len);
+    __syncthreads();
+    const int N = s_pre[B];
+    C = chunk_steps(a, N);
+    x0 = worker * C;
+    if (x0 >= N) return;
+    count = min(C, N - x0);
+    c0 = locate(s_pre, s_len, B, H, kGroup, x0);
+  } else {
+    if (worker >= B * H) return;
+    c0.b = worker / H;
+    c0.h = worker % H;
+    c0.k = 0;
+    c0.L = clamp_len(a.context_lens[c0.b], a.len_cap);
+    c0.n = (c0.L + kGroup - 1) / kGroup;
+    count = c0.n;
+    if (count == 0) {  // empty sequence: zero rows for the group's q heads
+      const int64_t head0 = (int64_t)c0.b * a.num_q_heads + (int64_t)c0.h * G;
+      for (int i = lane; i < G * D; i += 64) store_out<TT>(a.out, head0 * D + i, 0.f);
+      return;
+    }
   }
-  const int t1 = min(t0 + a.part, L);
-  const int nblk = (L + bs - 1) / bs;
-  const int32_t* trow = a.block_tables + (int64_t)b * a.max_blocks_per_seq;
-  const int ngroups = (t1 - t0 + kGroup - 1) / kGroup;
-  const int s_begin = ngroups * w / kWaves, s_end = ngroups * (w + 1) / kWaves;
-  const int nb_grp = bs >= kGroup ? 1 : kGroup / bs;  // blocks touched by one group
+  auto uniform = [](Cursor& x) {
+    x.b = __builtin_amdgcn_readfirstlane(x.b);
+    x.h = __builtin_amdgcn_readfirstlane(x.h);
+    x.k = __builtin_amdgcn_readfirstlane(x.k);
+    x.n = __builtin_amdgcn_readfirstlane(x.n);
+    x.L = __builtin_amdgcn_readfirstlane(x.L);
+  };
+  uniform(c0);
 
   const char* kbase = reinterpret_cast<const char*>(a.k_cache);
   const char* vbase = reinterpret_cast<const char*>(a.v_cache);
-  const int64_t hkv = a.num_kv_heads;
-
-  // Q^T operand: head n, d = kb*D/4 + 8*s + e for k-step s.
-  uint4 qv[KN];
-  {
-    const char* qp = reinterpret_cast<const char*>(a.q) + ((head0 + n) * D + kb * (D / 4)) * EB;
-#pragma unroll
-    for (int s = 0; s < KN; ++s) qv[s] = n < G ? ld16(qp + 16 * s) : make_uint4(0, 0, 0, 0);
-  }
+  const char* qbase = reinterpret_cast<const char*>(a.q);
+  const int nb_grp = bs >= kGroup ? 1 : kGroup / bs;  // blocks touched by one group
 
   TableWindow tw;
-  tw.base = 0x7fffffff;
+  int tw_b = -1;
+  tw.base = 0;
   tw.entry = 0;
 
-  // K row of tile j for this lane, and the V token run of k-group kb.
+  // K row of tile j for this lane plus (when the item changes) the Q^T
+  // operand of the item: head n.  K-step s, element e of k-group kb carries
+  // d = 32*s + 8*kb + e in both operands, so the four k-groups of one row read
+  // a contiguous 64-byte segment per load instruction.
   const int kt_off0 = (n >> 2) * 8 + (n & 3);  // token of tile 0 row n (tile 1: +4)
-  auto issue = [&](int s, uint4 (&kr)[2][KN], uint4 (&vr)[MT]) {
-    const int tok = t0 + s * kGroup;
+  auto issue_k = [&](const Cursor& cu, uint4 (&kr)[2][KN], uint4 (&qr)[KN], int& qitem) {
+    const int item = cu.item(H);
+    if (qitem != item) {
+      qitem = item;
+      const int64_t head = (int64_t)cu.b * a.num_q_heads + (int64_t)cu.h * G + n;
+      const char* qp = qbase + (head * D + kb * 8) * EB;
+#pragma unroll
+      for (int s = 0; s < KN; ++s) qr[s] = n < G ? ld16(qp + 64 * s) : make_uint4(0, 0, 0, 0);
+    }
+    const int32_t* trow = a.block_tables + (int64_t)cu.b * a.max_blocks_per_seq;
+    const int tok = cu.k * kGroup;
     const int lb0 = tok / bs;
-    tw.ensure(trow, nblk, a.num_blocks, lb0, nb_grp, lane);
+    if (tw_b != cu.b) {
+      tw_b = cu.b;
+      tw.base = 0x7fffffff;
+    }
+    tw.ensure(trow, a.max_blocks_per_seq, a.num_blocks, lb0, nb_grp, lane);
+    const int64_t g = cu.h;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int t = tok + kt_off0 + 4 * j;
@@ -136,38 +172,55 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeArgs a) {
       int64_t phys = tw.get(lb0);
       for (int q = 1; q < nb_grp; ++q)
         if (lb == lb0 + q) phys = tw.get(lb0 + q);
-      const char* kp = kbase + (((phys * hkv + g) * bs + (t - lb * bs)) * D + kb * (D / 4)) * EB;
+      const char* kp = kbase + (((phys * hkv + g) * bs + (t - lb * bs)) * D + kb * 8) * EB;
 #pragma unroll
-      for (int i = 0; i < KN; ++i) kr[j][i] = ld16(kp + 16 * i);
+      for (int i = 0; i < KN; ++i) kr[j][i] = ld16(kp + 64 * i);
     }
-    {
-      const int t = tok + kb * 8;
-      const int lb = t / bs;
-      int64_t phys = tw.get(lb0);
-      for (int q = 1; q < nb_grp; ++q)
-        if (lb == lb0 + q) phys = tw.get(lb0 + q);
-      const int off = t - lb * bs;
-      const char* vp =
-          vbase + ((((phys * hkv + g) * (bs / VS) + off / VS) * D + n) * VS + off % VS) * EB;
+  };
+  // The V token run of k-group kb (8 tokens of one slab row per d tile).  Its
+  // group's K was issued earlier, so the table window already covers it.
+  auto issue_v = [&](const Cursor& cu, uint4 (&vr)[MT]) {
+    const int tok = cu.k * kGroup;
+    const int lb0 = tok / bs;
+    const int t = tok + kb * 8;
+    const int lb = t / bs;
+    int64_t phys = tw.get(lb0);
+    for (int q = 1; q < nb_grp; ++q)
+      if (lb == lb0 + q) phys = tw.get(lb0 + q);
+    const int off = t - lb * bs;
+    const char* vp =
+        vbase + ((((phys * hkv + cu.h) * (bs / VS) + off / VS) * D + n) * VS) * EB;
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) vr[mt] = ld16(vp + (int64_t)mt * 16 * VS * EB);
-    }
+    for (int mt = 0; mt < MT; ++mt) vr[mt] = ld16(vp + (int64_t)mt * 16 * VS * EB);
   };
 
   float m_run = -INFINITY, l_lane = 0.f;
   float4_t acc[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
+  int seg_k0 = c0.k;
 
-  auto compute = [&](int s, const uint4 (&kr)[2][KN], uint4 (&vr)[MT]) {
-    const int tok = t0 + s * kGroup;
-    const int nvalid = min(kGroup, t1 - tok);
+  // Phase 1 of a group: S^T = K Q^T, online-softmax update, P^T operand.
+  auto qk = [&](const Cursor& cu, const uint4 (&kr)[2][KN], const uint4 (&qr)[KN], int j,
+                uint4& pb, int& nvalid) {
+    if (j == 0 || cu.k == 0) {  // a new segment starts
+      m_run = -INFINITY;
+      l_lane = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
+      seg_k0 = cu.k;
+      if (a.split && cu.k == 0 && lane == 0) {  // this worker starts the item
+        const int last = (x0 + j + cu.n - 1) / C;
+        a.ws_desc[cu.item(H)] = make_int2(worker, last - worker + 1);
+      }
+    }
+    nvalid = min(kGroup, cu.L - cu.k * kGroup);
     float4_t st[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      st[j] = float4_t{0.f, 0.f, 0.f, 0.f};
+    for (int jj = 0; jj < 2; ++jj) {
+      st[jj] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < KN; ++i) st[j] = mfma(TT{}, kr[j][i], qv[i], st[j]);
+      for (int i = 0; i < KN; ++i) st[jj] = mfma(TT{}, kr[jj][i], qr[i], st[jj]);
     }
     float sc[8];
 #pragma unroll
@@ -195,8 +248,14 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeArgs a) {
     }
     l_lane = l_lane * alpha + psum;
     m_run = m_new;
-    const uint4 pb = make_uint4(pack2(TT{}, pw[0], pw[1]), pack2(TT{}, pw[2], pw[3]),
-                                pack2(TT{}, pw[4], pw[5]), pack2(TT{}, pw[6], pw[7]));
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] *= alpha;
+    pb = make_uint4(pack2(TT{}, pw[0], pw[1]), pack2(TT{}, pw[2], pw[3]),
+                    pack2(TT{}, pw[4], pw[5]), pack2(TT{}, pw[6], pw[7]));
+  };
+
+  // Phase 2: O^T += V^T P^T, and the segment's output at its end.
+  auto pv = [&](const Cursor& cu, uint4 (&vr)[MT], const uint4& pb, int nvalid, int j) {
     if (nvalid < kGroup) {  // zero V of masked tokens (their bits may be NaN)
       const int keep = min(max(nvalid - kb * 8, 0), 8);  // valid tokens of this k-group
       uint32_t m4[4];
@@ -215,73 +274,87 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeArgs a) {
       }
     }
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      acc[mt] *= alpha;
-      acc[mt] = mfma(TT{}, vr[mt], pb, acc[mt]);
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma(TT{}, vr[mt], pb, acc[mt]);
+    if (j == count - 1 || cu.k == cu.n - 1) {  // the segment ends here
+      float l_tot = l_lane + __shfl_xor(l_lane, 16);
+      l_tot += __shfl_xor(l_tot, 32);
+      const int item = cu.item(H);
+      if (n < G) {
+        if (seg_k0 == 0 && cu.k == cu.n - 1) {
+          const int64_t orow = ((int64_t)cu.b * a.num_q_heads + (int64_t)cu.h * G + n) * D;
+          const float inv = 1.f / l_tot;
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              store_out<TT>(a.out, orow + mt * 16 + 4 * kb + e, acc[mt][e] * inv);
+        } else {
+          const int64_t row = ((int64_t)item + worker) * G + n;  // slot item + worker
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            *reinterpret_cast<float4_t*>(a.ws_o + row * D + mt * 16 + 4 * kb) = acc[mt];
+          if (kb == 0) {
+            a.ws_m[row] = m_run;
+            a.ws_l[row] = l_tot;
+          }
+        }
+      }
     }
   };
 
-  {
-    uint4 ka[2][KN], va[MT], kb2[2][KN], vb2[MT];
-    int s = s_begin;
-    if (s < s_end) issue(s, ka, va);
-    while (s < s_end) {
-      if (s + 1 < s_end) issue(s + 1, kb2, vb2);
-      compute(s, ka, va);
-      ++s;
-      if (s >= s_end) break;
-      if (s + 1 < s_end) issue(s + 1, ka, va);
-      compute(s, kb2, vb2);
-      ++s;
+  // Pipeline, per group j: qk(j) | issue V(j+1) | pv(j) | issue K(j+2).  Each
+  // load is issued a full group ahead of its use, yet only three of the four
+  // K/V register sets are live at any time.  Issues past the worker's last
+  // group repeat that group's (cached) addresses, keeping the waits static.
+  uint4 kA[2][KN], kB[2][KN], vA[MT], vB[MT], qA[KN], qB[KN];
+  int qia = -1, qib = -1;
+  auto next = [&](Cursor& c, int idx) {  // cursor of group idx, given idx-1's
+    if (idx < count) {
+      advance(c, s_pre, s_len, H, kGroup);
+      uniform(c);
     }
-  }
-
-  // per-head sum over the 4 k-groups, then merge the waves through LDS
-  l_lane += __shfl_xor(l_lane, 16);
-  l_lane += __shfl_xor(l_lane, 32);
-  if (kb == 0) {
-    s_m[w][n] = m_run;
-    s_l[w][n] = l_lane;
-  }
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) s_o[w][n][mt * 16 + 4 * kb + e] = acc[mt][e];
-  __syncthreads();
-
-  const bool split = (L + a.part - 1) / a.part > 1;
-  for (int i = threadIdx.x; i < G * D; i += kThreads) {
-    const int hn = i / D, d = i % D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, s_m[ww][hn]);
-    float o = 0.f, Lt = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) {
-      const float f = s_m[ww][hn] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s_m[ww][hn] - M);
-      o += f * s_o[ww][hn][d];
-      Lt += f * s_l[ww][hn];
+  };
+  Cursor c1 = c0;
+  next(c1, 1);
+  issue_k(c0, kA, qA, qia);
+  issue_v(c0, vA);
+  issue_k(c1, kB, qB, qib);
+  int j = 0;
+  for (;;) {
+    Cursor c2 = c1;
+    next(c2, j + 2);
+    {
+      uint4 pb;
+      int nv;
+      qk(c0, kA, qA, j, pb, nv);
+      issue_v(c1, vB);
+      pv(c0, vA, pb, nv, j);
+      issue_k(c2, kA, qA, qia);
     }
-    if (!split) {
-      store_out<TT>(a.out, (head0 + hn) * D + d, o / Lt);
-    } else {
-      const int64_t pi = (head0 + hn) * a.max_parts + p;
-      a.ws_o[pi * D + d] = o;
-      if (d == 0) {
-        a.ws_m[pi] = M;
-        a.ws_l[pi] = Lt;
-      }
+    if (++j >= count) break;
+    c0 = c1;
+    c1 = c2;
+    c2 = c1;
+    next(c2, j + 2);
+    {
+      uint4 pb;
+      int nv;
+      qk(c0, kB, qB, j, pb, nv);
+      issue_v(c1, vA);
+      pv(c0, vB, pb, nv, j);
+      issue_k(c2, kB, qB, qib);
     }
+    if (++j >= count) break;
+    c0 = c1;
+    c1 = c2;
   }
 }
 
 template <typename TT, int D>
 hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
-  dim3 grid(a.max_parts, a.num_kv_heads, a.num_seqs);
-  if (a.block_size >= 16)
-    hipLaunchKernelGGL((decode_mfma_kernel<TT, D, 16>), grid, dim3(kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((decode_mfma_kernel<TT, D, 8>), grid, dim3(kThreads), 0, s, a);
+  dim3 grid((a.num_workers + kWaves - 1) / kWaves);
+  const size_t lds = a.split ? sizeof(int) * (2 * (size_t)a.num_seqs + 1) : 0;
+  hipLaunchKernelGGL((decode_mfma_kernel<TT, D>), grid, dim3(kThreads), lds, s, a);
   return hipGetLastError();
 }
 

@@ -9,24 +9,28 @@
 // the block table: logical block u / BS, offset u % BS (gitcode.csdn.net
 // "vLLM 推理引擎：PagedAttention 与 KVCache 管理", section 3).
 //
-// decode_valu_kernel -- the MHA path (one q head per kv head read).  Work item
-// = (partition of P tokens, q head, sequence), one 256-thread workgroup.  Each
-// of the 4 wavefronts streams a contiguous run of 16-token steps:
-//   K  step = 16 token rows; lane (t = lane/4, c = lane%4) loads D/4 elements
-//      of row t (64 B for fp16 D=128), dot2 with q, quad-reduce via DPP.
-//   V  step = one 16-token slab [D][16] (two 8-token slabs when BS = 8);
-//      lane owns D/64 full slab rows, so its accumulators are complete sums
-//      and need no cross-lane reduction; the 16 weights are broadcast with
-//      readlane into scalar registers.
-// Loads for step i+1 are issued before step i is computed.  The four waves
-// merge (m, l, acc) through LDS; a sequence longer than P writes fp32
-// partials that decode_reduce.hip merges.
+// decode_valu_kernel -- the MHA path (one q head per kv head read).  Work
+// items are (sequence, q head); each wavefront is an independent worker that
+// streams a contiguous, equal share of all items' 16-token steps
+// (decode_split.h), writing finished rows or fp32 partials:
+//   K  step = 16 token rows; lane (t = lane/4, c = lane%4) loads the 16-byte
+//      chunks c, c+4, c+8, ... of row t (D/4 elements), so the four lanes of a
+//      quad read 64 contiguous bytes per instruction; dot2 with the matching q
+//      chunks, quad-reduce via DPP.
+//   V  step = two 8-token slabs [D][8]; lane owns slab rows lane + 64*r, so
+//      one load instruction covers 1 KiB of a slab contiguously and all lanes
+//      hold the same 8 tokens -- the 16 weights are broadcast with readlane
+//      into scalar registers, and each lane's accumulators are complete sums
+//      needing no cross-lane reduction.
+// Loads for step i+1 are issued before step i is computed, also across item
+// boundaries.  Items split between workers are merged by decode_merge.hip.
 //
 // decode_generic_kernel -- any head_dim <= 256 / block_size / dtype, one
 // wavefront per (q head, sequence), one token at a time.  Used for shapes the
 // fast kernels do not cover (e.g. head_dim 16, block_size 4).
 #include <math.h>
 
+#include "decode_split.h"
 #include "pa_internal.h"
 
 namespace pa {
@@ -52,22 +56,6 @@ __device__ __forceinline__ float wave_sum(float x) {
 __device__ __forceinline__ uint4 ld16(const char* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
-
-// Storage-type helpers over the uint4 words a lane holds.
-template <typename TT>
-struct Words;
-template <>
-struct Words<F32> {
-  static constexpr int per16 = 4;  // elements per 16 bytes
-};
-template <>
-struct Words<F16> {
-  static constexpr int per16 = 8;
-};
-template <>
-struct Words<BF16> {
-  static constexpr int per16 = 8;
-};
 
 __device__ __forceinline__ uint32_t word(const uint4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
@@ -99,49 +87,53 @@ __device__ __forceinline__ float lane_dot(TT t, const uint4 (&q)[NK], const uint
   return s0 + s1;
 }
 
+// V register j*R*NVR + r*NVR + u (piece j = tokens 8j .. 8j+7 of the step,
+// slab row lane + 64*r, NVR uint4 per 8-token row piece) holds the tokens
+// 8*j + u*EPV + e, EPV = elements per uint4.
+template <typename TT, int R>
+struct VMap {
+  static constexpr int EPV = 16 / TT::bytes;
+  static constexpr int NVR = 8 / EPV;
+  static constexpr int token(int idx, int e) {
+    return (idx / (R * NVR)) * 8 + (idx % NVR) * EPV + e;
+  }
+  static constexpr int row(int idx) { return (idx / NVR) % R; }
+};
+
 // acc[r] += sum_tau p[tau] * v[r][tau] over the lane's V elements.
-// Element e of the lane's data: piece j = e / (R*VS), row r = (e % (R*VS)) / VS,
-// token tau = j*VS + e % VS.
-template <typename TT, int R, int VS, int NK>
+template <typename TT, int R, int NK>
 __device__ __forceinline__ void lane_pv(float (&acc)[R], const float (&p)[kStep],
                                         const uint4 (&v)[NK]) {
+  using M = VMap<TT, R>;
 #pragma unroll
   for (int i = 0; i < NK; ++i)
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const uint32_t x = word(v[i], w);
+      const int r = M::row(i);
       if constexpr (TT::bytes == 4) {
-        const int e = i * 4 + w;
-        const int j = e / (R * VS), r = (e % (R * VS)) / VS, tau = j * VS + e % VS;
-        acc[r] = fmaf(p[tau], __uint_as_float(x), acc[r]);
+        acc[r] = fmaf(p[M::token(i, w)], __uint_as_float(x), acc[r]);
       } else {
-        const int e = i * 8 + w * 2;
-        const int j = e / (R * VS), r = (e % (R * VS)) / VS, tau = j * VS + e % VS;
-        acc[r] = fmaf(p[tau], lo_to_float(TT{}, x), acc[r]);
-        acc[r] = fmaf(p[tau + 1], hi_to_float(TT{}, x), acc[r]);
+        acc[r] = fmaf(p[M::token(i, 2 * w)], lo_to_float(TT{}, x), acc[r]);
+        acc[r] = fmaf(p[M::token(i, 2 * w + 1)], hi_to_float(TT{}, x), acc[r]);
       }
     }
 }
 
 // Zero V elements of tokens >= nvalid (their bits may be NaN; 0 * NaN = NaN).
-template <typename TT, int R, int VS, int NK>
+template <typename TT, int R, int NK>
 __device__ __forceinline__ void mask_v(uint4 (&v)[NK], int nvalid) {
-  constexpr int per16 = Words<TT>::per16;
-  constexpr int eb = 16 / per16 * 8;  // bits per element
+  using M = VMap<TT, R>;
 #pragma unroll
   for (int i = 0; i < NK; ++i) {
     uint32_t w4[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      constexpr int per_word = 32 / eb;
-#pragma unroll
-      for (int h = 0; h < per_word; ++h) {
-        const int e = i * per16 + w * per_word + h;
-        const int j = e / (R * VS), tau = j * VS + e % VS;
-        if (tau >= nvalid) {
-          const uint32_t m = eb == 32 ? 0xffffffffu : (0xffffu << (16 * h));
-          w4[w] &= ~m;
-        }
+      if constexpr (TT::bytes == 4) {
+        if (M::token(i, w) >= nvalid) w4[w] = 0u;
+      } else {
+        if (M::token(i, 2 * w) >= nvalid) w4[w] &= 0xffff0000u;
+        if (M::token(i, 2 * w + 1) >= nvalid) w4[w] &= 0x0000ffffu;
       }
     }
     v[i] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
@@ -157,8 +149,9 @@ __device__ __forceinline__ void store_out(void* out, int64_t idx, float x) {
 }
 
 // Block-table window: lane i holds the physical id of logical block base + i
-// (0 past the sequence's last block, and for ids outside the pool, so that a
-// bad table never produces an out-of-range address).
+// (0 past the table row, and for ids outside the pool -- padding included --
+// so that no entry ever produces an out-of-range address; such blocks only
+// ever feed masked positions).
 struct TableWindow {
   int base;
   int entry;
@@ -179,93 +172,116 @@ struct TableWindow {
   }
 };
 
-template <typename TT, int D, int VS>
+template <typename TT, int D>
 __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
   constexpr int EB = TT::bytes;
-  constexpr int LANE_BYTES = D * EB / 4;  // per lane per step, K and V alike
-  constexpr int NK = LANE_BYTES / 16;
-  constexpr int R = D / 64;  // slab rows owned by a lane
-  constexpr int PIECES = kStep / VS;
-  constexpr int PIECE_NK = NK / PIECES;
-  static_assert(NK % PIECES == 0 && R >= 1, "unsupported shape");
+  constexpr int NK = D * EB / 64;  // uint4 per lane per step, K and V alike
+  constexpr int R = D / 64;        // slab rows owned by a lane
+  constexpr int NVR = VMap<TT, R>::NVR;
+  static_assert(R >= 1 && 2 * R * NVR == NK, "unsupported shape");
+  extern __shared__ int smem[];  // split 1: s_pre[B+1], s_len[B]
 
-  __shared__ float s_m[kWaves], s_l[kWaves];
-  __shared__ float s_acc[kWaves][D];
-
-  const int p = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int group = a.num_q_heads / a.num_kv_heads;
-  const int g = h / group;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int worker = blockIdx.x * kWaves + wv;
+  const int H = a.num_q_heads, B = a.num_seqs;
+  const int group = H / a.num_kv_heads;
   const int bs = a.block_size;
-  int L = a.context_lens[b];
-  L = L < 0 ? 0 : (L > a.len_cap ? a.len_cap : L);
-  const int t0 = p * a.part;
-  const int64_t orow = ((int64_t)b * a.num_q_heads + h) * D;
-  if (t0 >= L) {
-    if (p == 0)  // empty sequence: zero row
-      for (int d = threadIdx.x; d < D; d += kThreads) store_out<TT>(a.out, orow + d, 0.f);
-    return;
-  }
-  const int t1 = min(t0 + a.part, L);
-  const int nblk = (L + bs - 1) / bs;
-  const int32_t* trow = a.block_tables + (int64_t)b * a.max_blocks_per_seq;
-
-  // this wave's steps
-  const int nsteps = (t1 - t0 + kStep - 1) / kStep;
-  const int s_begin = nsteps * w / kWaves, s_end = nsteps * (w + 1) / kWaves;
-
+  const int64_t hkv = a.num_kv_heads;
   const int tq = lane >> 2, c = lane & 3;
+  int* s_pre = smem;
+  int* s_len = smem + B + 1;
+
+  Cursor c0;
+  int count;
+  int C = 0, x0 = 0;  // split 1: steps per worker, first stream step of this worker
+  if (a.split) {
+    if (wv == 0) wave_scan_steps(a.context_lens, B, H, a.len_cap, kStep, s_pre, s_len);
+    __syncthreads();
+    const int N = s_pre[B];
+    C = chunk_steps(a, N);
+    x0 = worker * C;
+    if (x0 >= N) return;
+    count = min(C, N - x0);
+    c0 = locate(s_pre, s_len, B, H, kStep, x0);
+  } else {
+    if (worker >= B * H) return;
+    c0.b = worker / H;
+    c0.h = worker % H;
+    c0.k = 0;
+    c0.L = clamp_len(a.context_lens[c0.b], a.len_cap);
+    c0.n = (c0.L + kStep - 1) / kStep;
+    count = c0.n;
+    if (count == 0) {  // empty sequence: zero row
+      const int64_t orow = ((int64_t)c0.b * H + c0.h) * D;
+#pragma unroll
+      for (int r = 0; r < R; ++r) store_out<TT>(a.out, orow + lane + 64 * r, 0.f);
+      return;
+    }
+  }
+  auto uniform = [](Cursor& x) {
+    x.b = __builtin_amdgcn_readfirstlane(x.b);
+    x.h = __builtin_amdgcn_readfirstlane(x.h);
+    x.k = __builtin_amdgcn_readfirstlane(x.k);
+    x.n = __builtin_amdgcn_readfirstlane(x.n);
+    x.L = __builtin_amdgcn_readfirstlane(x.L);
+  };
+  uniform(c0);
+
   const char* kbase = reinterpret_cast<const char*>(a.k_cache);
   const char* vbase = reinterpret_cast<const char*>(a.v_cache);
+  const char* qbase = reinterpret_cast<const char*>(a.q);
 
-  // q slice of this lane: elements c*D/4 .. (c+1)*D/4
-  uint4 qv[NK];
-  {
-    const char* qp = reinterpret_cast<const char*>(a.q) + (orow + c * (D / 4)) * EB;
-#pragma unroll
-    for (int i = 0; i < NK; ++i) qv[i] = ld16(qp + 16 * i);
-  }
-
+  // Block-table window of the sequence being issued (reloaded when the
+  // sequence changes or the window runs out).
   TableWindow tw;
-  tw.base = 0x7fffffff;
+  int tw_b = -1;
+  tw.base = 0;
   tw.entry = 0;
 
-  auto issue = [&](int s, uint4 (&kr)[NK], uint4 (&vr)[NK]) {
-    const int tok = t0 + s * kStep;
-    const int lb = tok / bs;
-    if constexpr (VS == 16) {
-      tw.ensure(trow, nblk, a.num_blocks, lb, 1, lane);
-      const int64_t phys = tw.get(lb);
-      const int off = tok - lb * bs;  // multiple of 16
-      const char* kp =
-          kbase + (((phys * a.num_kv_heads + g) * bs + off + tq) * D + c * (D / 4)) * EB;
+  // The step's tokens tok .. tok+15 form two 8-token slabs; slab j lies in
+  // block (tok + 8j) / BS (BS is 8 or a multiple of 16).  The q slice of the
+  // step's item travels with the step's K/V registers (reloaded only when the
+  // buffer's item changes).
+  auto issue = [&](const Cursor& cu, uint4 (&kr)[NK], uint4 (&vr)[NK], uint4 (&qr)[NK],
+                   int& qitem) {
+    const int item = cu.item(H);
+    if (qitem != item) {
+      qitem = item;
+      const char* qp = qbase + (int64_t)item * D * EB + c * 16;
 #pragma unroll
-      for (int i = 0; i < NK; ++i) kr[i] = ld16(kp + 16 * i);
-      const char* vp =
-          vbase +
-          ((((phys * a.num_kv_heads + g) * (bs / 16) + off / 16) * D + lane * R) * 16) * EB;
+      for (int i = 0; i < NK; ++i) qr[i] = ld16(qp + 64 * i);  // chunks c + 4i
+    }
+    const int32_t* trow = a.block_tables + (int64_t)cu.b * a.max_blocks_per_seq;
+    const int tok = cu.k * kStep;
+    const int lb0 = tok / bs, lb1 = (tok + 8) / bs;
+    if (tw_b != cu.b) {
+      tw_b = cu.b;
+      tw.load(trow, a.max_blocks_per_seq, a.num_blocks, lb0, lane);
+    } else {
+      tw.ensure(trow, a.max_blocks_per_seq, a.num_blocks, lb0, lb1 - lb0 + 1, lane);
+    }
+    const int64_t ph0 = tw.get(lb0), ph1 = tw.get(lb1);
+    const int off0 = tok - lb0 * bs, off1 = tok + 8 - lb1 * bs;  // multiples of 8
+    const int64_t g = cu.h / group;
+    {
+      const bool hi = tq >= 8;
+      const int64_t phys = hi ? ph1 : ph0;
+      const int off = (hi ? off1 : off0) + (tq & 7);
+      const char* kp = kbase + ((phys * hkv + g) * bs + off) * (D * EB) + c * 16;
 #pragma unroll
-      for (int i = 0; i < NK; ++i) vr[i] = ld16(vp + 16 * i);
-    } else {  // BS == VS < 16: the step spans PIECES blocks
-      tw.ensure(trow, nblk, a.num_blocks, lb, PIECES, lane);
-      int64_t ph[PIECES];
+      for (int i = 0; i < NK; ++i) kr[i] = ld16(kp + 64 * i);
+    }
 #pragma unroll
-      for (int j = 0; j < PIECES; ++j) ph[j] = tw.get(lb + j);
-      int64_t mine = ph[0];
+    for (int j = 0; j < 2; ++j) {
+      const int64_t phys = j ? ph1 : ph0;
+      const int off = j ? off1 : off0;
+      const char* vp = vbase + (((phys * hkv + g) * (bs / 8) + off / 8) * D + lane) * (8 * EB);
 #pragma unroll
-      for (int j = 1; j < PIECES; ++j)
-        if (tq / VS == j) mine = ph[j];
-      const char* kp =
-          kbase + (((mine * a.num_kv_heads + g) * VS + tq % VS) * D + c * (D / 4)) * EB;
+      for (int r = 0; r < R; ++r)
 #pragma unroll
-      for (int i = 0; i < NK; ++i) kr[i] = ld16(kp + 16 * i);
-#pragma unroll
-      for (int j = 0; j < PIECES; ++j) {
-        const char* vp = vbase + (((ph[j] * a.num_kv_heads + g) * D + lane * R) * VS) * EB;
-#pragma unroll
-        for (int i = 0; i < PIECE_NK; ++i) vr[j * PIECE_NK + i] = ld16(vp + 16 * i);
-      }
+        for (int u = 0; u < NVR; ++u)
+          vr[(j * R + r) * NVR + u] = ld16(vp + (int64_t)r * 64 * 8 * EB + 16 * u);
     }
   };
 
@@ -273,11 +289,23 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
   float acc[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = 0.f;
+  int seg_k0 = c0.k;  // first step of the current segment within its item
 
-  auto compute = [&](int s, const uint4 (&kr)[NK], uint4 (&vr)[NK]) {
-    const int tok = t0 + s * kStep;
-    const int nvalid = min(kStep, t1 - tok);
-    float d = lane_dot(TT{}, qv, kr);
+  auto compute = [&](const Cursor& cu, const uint4 (&kr)[NK], uint4 (&vr)[NK],
+                     const uint4 (&qr)[NK], int j) {
+    if (j == 0 || cu.k == 0) {  // a new segment starts
+      m_run = -INFINITY;
+      l_lane = 0.f;
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[r] = 0.f;
+      seg_k0 = cu.k;
+      if (a.split && cu.k == 0 && lane == 0) {  // this worker starts the item
+        const int last = (x0 + j + cu.n - 1) / C;
+        a.ws_desc[cu.item(H)] = make_int2(worker, last - worker + 1);
+      }
+    }
+    const int nvalid = min(kStep, cu.L - cu.k * kStep);
+    float d = lane_dot(TT{}, qr, kr);
     d += dpp<0xB1>(d);  // quad_perm [1,0,3,2]
     d += dpp<0x4E>(d);  // quad_perm [2,3,0,1]
     float sc = d * a.scale_log2e;
@@ -294,60 +322,58 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
     float pt[kStep];
 #pragma unroll
     for (int t = 0; t < kStep; ++t) pt[t] = bcast_lane(pv, 4 * t);
-    if (nvalid < kStep) mask_v<TT, R, VS, NK>(vr, nvalid);
+    if (nvalid < kStep) mask_v<TT, R, NK>(vr, nvalid);
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[r] *= alpha;
-    lane_pv<TT, R, VS, NK>(acc, pt, vr);
+    lane_pv<TT, R, NK>(acc, pt, vr);
+
+    if (j == count - 1 || cu.k == cu.n - 1) {  // the segment ends here
+      const float l_tot = wave_sum(l_lane);
+      const int item = cu.item(H);
+      if (seg_k0 == 0 && cu.k == cu.n - 1) {
+        const int64_t orow = (int64_t)item * D;
+#pragma unroll
+        for (int r = 0; r < R; ++r) store_out<TT>(a.out, orow + lane + 64 * r, acc[r] / l_tot);
+      } else {
+        const int64_t slot = (int64_t)item + worker;
+#pragma unroll
+        for (int r = 0; r < R; ++r) a.ws_o[slot * D + lane + 64 * r] = acc[r];
+        if (lane == 0) {
+          a.ws_m[slot] = m_run;
+          a.ws_l[slot] = l_tot;
+        }
+      }
+    }
   };
 
-  {
-    uint4 ka[NK], va[NK], kb2[NK], vb2[NK];
-    int s = s_begin;
-    if (s < s_end) issue(s, ka, va);
-    while (s < s_end) {
-      if (s + 1 < s_end) issue(s + 1, kb2, vb2);
-      compute(s, ka, va);
-      ++s;
-      if (s >= s_end) break;
-      if (s + 1 < s_end) issue(s + 1, ka, va);
-      compute(s, kb2, vb2);
-      ++s;
+  // Two register sets: step j+1 is always in flight while step j computes.
+  // The prefetch is unconditional (the last step re-issues its own, cached,
+  // addresses) so the wait before each compute covers only the older set.
+  uint4 ka[NK], va[NK], qa[NK], kb2[NK], vb2[NK], qb[NK];
+  int qia = -1, qib = -1;
+  Cursor c1 = c0;
+  if (count > 1) {
+    advance(c1, s_pre, s_len, H, kStep);
+    uniform(c1);
+  }
+  issue(c0, ka, va, qa, qia);
+  int j = 0;
+  for (;;) {
+    issue(c1, kb2, vb2, qb, qib);
+    compute(c0, ka, va, qa, j);
+    if (++j >= count) break;
+    c0 = c1;
+    if (j + 1 < count) {
+      advance(c1, s_pre, s_len, H, kStep);
+      uniform(c1);
     }
-  }
-
-  // merge the four waves
-  const float l_w = wave_sum(l_lane);
-  if (lane == 0) {
-    s_m[w] = m_run;
-    s_l[w] = l_w;
-  }
-#pragma unroll
-  for (int r = 0; r < R; ++r) s_acc[w][lane * R + r] = acc[r];
-  __syncthreads();
-
-  float M = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < kWaves; ++i) M = fmaxf(M, s_m[i]);
-  float f[kWaves], Lt = 0.f;
-#pragma unroll
-  for (int i = 0; i < kWaves; ++i) {
-    f[i] = s_m[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s_m[i] - M);
-    Lt += f[i] * s_l[i];
-  }
-  const bool split = (L + a.part - 1) / a.part > 1;
-  for (int d = threadIdx.x; d < D; d += kThreads) {
-    float o = 0.f;
-#pragma unroll
-    for (int i = 0; i < kWaves; ++i) o += f[i] * s_acc[i][d];
-    if (!split) {
-      store_out<TT>(a.out, orow + d, o / Lt);
-    } else {
-      const int64_t pi = ((int64_t)b * a.num_q_heads + h) * a.max_parts + p;
-      a.ws_o[pi * D + d] = o;
-      if (d == 0) {
-        a.ws_m[pi] = M;
-        a.ws_l[pi] = Lt;
-      }
+    issue(c1, ka, va, qa, qia);
+    compute(c0, kb2, vb2, qb, j);
+    if (++j >= count) break;
+    c0 = c1;
+    if (j + 1 < count) {
+      advance(c1, s_pre, s_len, H, kStep);
+      uniform(c1);
     }
   }
 }
@@ -419,11 +445,9 @@ __global__ __launch_bounds__(64) void decode_generic_kernel(DecodeArgs a) {
 
 template <typename TT, int D>
 hipError_t launch_valu_d(const DecodeArgs& a, hipStream_t s) {
-  dim3 grid(a.max_parts, a.num_q_heads, a.num_seqs);
-  if (a.block_size >= 16)
-    hipLaunchKernelGGL((decode_valu_kernel<TT, D, 16>), grid, dim3(kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((decode_valu_kernel<TT, D, 8>), grid, dim3(kThreads), 0, s, a);
+  dim3 grid((a.num_workers + kWaves - 1) / kWaves);
+  const size_t lds = a.split ? sizeof(int) * (2 * (size_t)a.num_seqs + 1) : 0;
+  hipLaunchKernelGGL((decode_valu_kernel<TT, D>), grid, dim3(kThreads), lds, s, a);
   return hipGetLastError();
 }
 

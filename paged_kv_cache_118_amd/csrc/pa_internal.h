@@ -77,19 +77,24 @@ struct DecodeArgs {
   int32_t max_blocks_per_seq;
   int32_t len_cap;     // min(max_context_len, max_blocks_per_seq * block_size)
   int64_t num_blocks;
-  int32_t part;        // tokens per partition (>= len_cap when nothing splits)
-  int32_t max_parts;   // ceil(len_cap / part)
-  // split workspace (valid when max_parts > 1)
-  float* ws_m;         // [num_seqs][num_q_heads][max_parts]
-  float* ws_l;         // same
-  float* ws_o;         // [num_seqs][num_q_heads][max_parts][head_dim]
+  // work split (decode_split.h)
+  int32_t split;        // 0: one item per worker, 1: token-balanced stream split
+  int32_t chunk_steps;  // split 1: steps per worker, 0 = ceil(N / num_workers)
+  int32_t num_workers;  // wavefronts launched
+  // partials of split items, slot = item + worker (split 1 only); rows of an
+  // item are its q heads (1 for the MHA kernel, the group for the GQA kernel)
+  float* ws_m;          // [slots][rows]
+  float* ws_l;          // [slots][rows]
+  float* ws_o;          // [slots][rows][head_dim]
+  int2* ws_desc;        // [items]: (first worker, number of workers) of the item
 };
 
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_decode_valu(const DecodeArgs& a, pa_dtype dt, hipStream_t s);
 hipError_t launch_decode_mfma(const DecodeArgs& a, pa_dtype dt, hipStream_t s);
 hipError_t launch_decode_generic(const DecodeArgs& a, pa_dtype dt, hipStream_t s);
-hipError_t launch_decode_reduce(const DecodeArgs& a, pa_dtype dt, hipStream_t s);
+hipError_t launch_decode_merge(const DecodeArgs& a, pa_dtype dt, int items_per_seq,
+                              hipStream_t s);
 bool decode_valu_supported(pa_dtype dt, int head_dim, int block_size);
 bool decode_mfma_supported(pa_dtype dt, int head_dim, int block_size, int group);
 
@@ -102,6 +107,7 @@ hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs
                               int32_t num_pairs, int64_t block_bytes, int64_t num_blocks,
                               hipStream_t s);
 
-__host__ __device__ inline int v_slab(int block_size) { return block_size < 16 ? block_size : 16; }
+// Tokens per V slab: V is stored as [block][head][BS/VS][D][VS].
+__host__ __device__ inline int v_slab(int block_size) { return block_size < 8 ? block_size : 8; }
 
 }  // namespace pa

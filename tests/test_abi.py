@@ -51,6 +51,7 @@ def _decode_rc(**kw):
     (dict(scale=float("nan")), -1),
     (dict(nb=0), -1),
     (dict(maxlen=4096, part=512), -1),  # split needs a workspace
+    (dict(maxlen=4096, part=0), -1),
 ])
 def test_decode_rejects_before_touching_gpu(kw, code):
     assert _decode_rc(**kw) == code
@@ -61,15 +62,21 @@ def test_decode_no_seqs_is_noop():
 
 
 def test_workspace_and_partition_sizes():
-    ws = pa.pa_decode_workspace_bytes
-    assert ws(64, 40, 40, 128, 16, 512, 0) == 0          # fits one partition
-    assert pa.pa_decode_partition_size(64, 40, 40, 128, 16, 512, 0) == 0
-    assert pa.pa_decode_partition_size(64, 40, 40, 128, 16, 2048, -1) == 0
-    p = pa.pa_decode_partition_size(64, 40, 40, 128, 16, 2048, 0)
-    assert p > 0 and p % 256 == 0
-    parts = -(-2048 // p)
-    assert ws(64, 40, 40, 128, 16, 2048, 0) >= 64 * 40 * parts * (2 + 128) * 4
-    assert pa.pa_decode_partition_size(32, 64, 8, 128, 32, 32768, 512, pa.torch.bfloat16) == 512
+    ws, part = pa.pa_decode_workspace_bytes, pa.pa_decode_partition_size
+    # one wavefront per item: no workspace
+    assert part(64, 40, 40, 128, 16, 2048, -1) == -1
+    assert ws(64, 40, 40, 128, 16, 2048, -1) == 0
+    # token-balanced split: partial slots for items + workers (>= items)
+    assert part(64, 40, 40, 128, 16, 2048, 0) == 0
+    assert ws(64, 40, 40, 128, 16, 2048, 0) >= 2 * 64 * 40 * (2 + 128) * 4
+    # fixed chunks: workers = ceil(items * steps / chunk)
+    assert part(32, 64, 8, 128, 32, 32768, 512, pa.torch.bfloat16) == 512
+    items, steps = 32 * 8, 32768 // 32
+    workers = -(-items * steps // (512 // 32))
+    assert ws(32, 64, 8, 128, 32, 32768, 512, pa.torch.bfloat16) >= \
+        (items + workers) * 8 * (2 + 128) * 4
+    # shapes the fast kernels do not take run one wavefront per item
+    assert part(2, 2, 2, 16, 4, 9, 0, pa.torch.float32) == -1
 
 
 def test_cache_ops_reject_bad_args():

@@ -33,6 +33,8 @@ SMALL = {
                                         lengths=("uniform", 1, 1500)),
     "gqa_bf16_g16_d64": W.GQA_LONG.with_(num_seqs=3, num_q_heads=32, num_kv_heads=2, head_dim=64,
                                          block_size=128, lengths=("uniform", 1, 2000)),
+    "gqa_f16_g16_d128_bs32": W.GQA_LONG.with_(dtype="f16", num_seqs=3, num_q_heads=32,
+                                              num_kv_heads=2, lengths=("uniform", 1, 3000)),
     "gqa_f32_g4_generic_path": W.GQA_LONG.with_(dtype="f32", num_seqs=3, num_q_heads=8,
                                                 num_kv_heads=2, lengths=("uniform", 1, 700)),
     "mha_f16_d32_bs4_generic": W.OPT13B.with_(num_seqs=4, num_q_heads=2, num_kv_heads=2,

@@ -79,8 +79,9 @@ def test_write_strided_token_rows(orc):
     rng = np.random.default_rng(31)
     nb, hkv, bs, D = 4, 2, 16, 8
     qkv = rng.standard_normal((5, 3, hkv, D)).astype(np.float32)
+    vs = v_slab(bs)
     kc = np.zeros((nb, hkv, bs, D), dtype=np.float32)
-    vc = np.zeros((nb, hkv, 1, D, bs), dtype=np.float32)
+    vc = np.zeros((nb, hkv, bs // vs, D, vs), dtype=np.float32)
     slots = np.array([0, 17, 33, 50, 63])
     flat = np.ascontiguousarray(qkv.reshape(5, -1))
     base = flat.ctypes.data  # k rows start hkv*D elements in, v rows 2*hkv*D
@@ -92,7 +93,7 @@ def test_write_strided_token_rows(orc):
     assert rc == 0
     for t, s in enumerate(slots):
         assert np.array_equal(kc[s // bs, :, s % bs, :], qkv[t, 1])
-        assert np.array_equal(vc[s // bs, :, 0, :, s % bs], qkv[t, 2])
+        assert np.array_equal(vc[s // bs, :, (s % bs) // vs, :, s % vs], qkv[t, 2])
 
 
 def test_copy_blocks_bytes_and_decode(orc):

@@ -12,7 +12,7 @@ rounded to the storage dtype (round-to-nearest-even).
 
 Pool layout (shapes only; the index formula is documented in include/pa.h):
   K: [num_blocks][Hkv][BS][D]
-  V: [num_blocks][Hkv][BS/VS][D][VS],  VS = min(BS, 16)
+  V: [num_blocks][Hkv][BS/VS][D][VS],  VS = min(BS, 8)
 """
 from __future__ import annotations
 
@@ -26,7 +26,7 @@ TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat1
 
 
 def v_slab(block_size: int) -> int:
-    return block_size if block_size < 16 else 16
+    return block_size if block_size < 8 else 8
 
 
 def k_pool_shape(num_blocks, num_kv_heads, block_size, head_dim):
