@@ -24,6 +24,7 @@
 //                  accumulators needs no data exchange.
 // Only the max / sum over the 4 k-groups of a head crosses lanes (xor 16, 32).
 #include <math.h>
+#include <stdlib.h>
 
 #include "decode_split.h"
 #include "pa_internal.h"
@@ -38,6 +39,13 @@ constexpr int kGroup = 32;  // tokens per wave step
 
 __device__ __forceinline__ uint4 ld16(const char* p) {
   return *reinterpret_cast<const uint4*>(p);
+}
+// Streaming (non-temporal) 16-byte load for K/V data that is read exactly
+// once per whole cache line: measured faster than a plain load on gfx950.
+__device__ __forceinline__ uint4 ld16nt(const char* p) {
+  typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
 }
 
 __device__ __forceinline__ float4_t mfma(F16, const uint4& a, const uint4& b, float4_t c) {
@@ -78,8 +86,10 @@ struct TableWindow {
   }
 };
 
-template <typename TT, int D>
-__global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeArgs a) {
+// SCHED 0: two-phase pipeline (K and V of a group issued one phase apart).
+// SCHED 1: single phase (K and V of group j+1 issued before group j computes).
+template <typename TT, int D, int SCHED, int OCC>
+__global__ __launch_bounds__(kThreads, OCC) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int VS = 8;       // V slab width (tokens)
   constexpr int EB = 2;
   constexpr int KN = D / 32;  // uint4 per lane per K tile (= QK k-steps)
@@ -191,7 +201,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeArgs a) 
     const char* vp =
         vbase + ((((phys * hkv + cu.h) * (bs / VS) + off / VS) * D + n) * VS) * EB;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) vr[mt] = ld16(vp + (int64_t)mt * 16 * VS * EB);
+    for (int mt = 0; mt < MT; ++mt) vr[mt] = ld16nt(vp + (int64_t)mt * 16 * VS * EB);
   };
 
   float m_run = -INFINITY, l_lane = 0.f;
@@ -302,59 +312,116 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeArgs a) 
     }
   };
 
-  // Pipeline, per group j: qk(j) | issue V(j+1) | pv(j) | issue K(j+2).  Each
-  // load is issued a full group ahead of its use, yet only three of the four
-  // K/V register sets are live at any time.  Issues past the worker's last
-  // group repeat that group's (cached) addresses, keeping the waits static.
-  uint4 kA[2][KN], kB[2][KN], vA[MT], vB[MT], qA[KN], qB[KN];
-  int qia = -1, qib = -1;
   auto next = [&](Cursor& c, int idx) {  // cursor of group idx, given idx-1's
     if (idx < count) {
       advance(c, s_pre, s_len, H, kGroup);
       uniform(c);
     }
   };
-  Cursor c1 = c0;
-  next(c1, 1);
-  issue_k(c0, kA, qA, qia);
-  issue_v(c0, vA);
-  issue_k(c1, kB, qB, qib);
-  int j = 0;
-  for (;;) {
-    Cursor c2 = c1;
-    next(c2, j + 2);
-    {
-      uint4 pb;
-      int nv;
-      qk(c0, kA, qA, j, pb, nv);
+  if constexpr (SCHED == 0) {
+    // Pipeline, per group j: qk(j) | issue V(j+1) | pv(j) | issue K(j+2).
+    // Each load is issued a full group ahead of its use, yet only three of
+    // the four K/V register sets are live at any time.  Issues past the
+    // worker's last group repeat that group's (cached) addresses, keeping the
+    // waits static.
+    uint4 kA[2][KN], kB[2][KN], vA[MT], vB[MT], qA[KN], qB[KN];
+    int qia = -1, qib = -1;
+    Cursor c1 = c0;
+    next(c1, 1);
+    issue_k(c0, kA, qA, qia);
+    issue_v(c0, vA);
+    issue_k(c1, kB, qB, qib);
+    int j = 0;
+    for (;;) {
+      Cursor c2 = c1;
+      next(c2, j + 2);
+      {
+        uint4 pb;
+        int nv;
+        qk(c0, kA, qA, j, pb, nv);
+        issue_v(c1, vB);
+        pv(c0, vA, pb, nv, j);
+        issue_k(c2, kA, qA, qia);
+      }
+      if (++j >= count) break;
+      c0 = c1;
+      c1 = c2;
+      c2 = c1;
+      next(c2, j + 2);
+      {
+        uint4 pb;
+        int nv;
+        qk(c0, kB, qB, j, pb, nv);
+        issue_v(c1, vA);
+        pv(c0, vB, pb, nv, j);
+        issue_k(c2, kB, qB, qib);
+      }
+      if (++j >= count) break;
+      c0 = c1;
+      c1 = c2;
+    }
+  } else {
+    // Single phase: K and V of group j+1 are issued together before group j
+    // computes.
+    uint4 kA[2][KN], kB[2][KN], vA[MT], vB[MT], qA[KN], qB[KN];
+    int qia = -1, qib = -1;
+    Cursor c1 = c0;
+    next(c1, 1);
+    issue_k(c0, kA, qA, qia);
+    issue_v(c0, vA);
+    int j = 0;
+    for (;;) {
+      issue_k(c1, kB, qB, qib);
       issue_v(c1, vB);
-      pv(c0, vA, pb, nv, j);
-      issue_k(c2, kA, qA, qia);
-    }
-    if (++j >= count) break;
-    c0 = c1;
-    c1 = c2;
-    c2 = c1;
-    next(c2, j + 2);
-    {
-      uint4 pb;
-      int nv;
-      qk(c0, kB, qB, j, pb, nv);
+      {
+        uint4 pb;
+        int nv;
+        qk(c0, kA, qA, j, pb, nv);
+        pv(c0, vA, pb, nv, j);
+      }
+      if (++j >= count) break;
+      c0 = c1;
+      next(c1, j + 1);
+      issue_k(c1, kA, qA, qia);
       issue_v(c1, vA);
-      pv(c0, vB, pb, nv, j);
-      issue_k(c2, kB, qB, qib);
+      {
+        uint4 pb;
+        int nv;
+        qk(c0, kB, qB, j, pb, nv);
+        pv(c0, vB, pb, nv, j);
+      }
+      if (++j >= count) break;
+      c0 = c1;
+      next(c1, j + 1);
     }
-    if (++j >= count) break;
-    c0 = c1;
-    c1 = c2;
   }
+}
+
+// Schedule variant (tuning): PA_MFMA_SCHED = 0 two-phase (default),
+// 1 single-phase, 2 two-phase built for 3 waves per SIMD.
+int mfma_sched() {
+  static int v = -1;
+  if (v < 0) {
+    const char* e = std::getenv("PA_MFMA_SCHED");
+    v = (e && e[0] >= '0' && e[0] <= '2') ? e[0] - '0' : 0;
+  }
+  return v;
 }
 
 template <typename TT, int D>
 hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
   dim3 grid((a.num_workers + kWaves - 1) / kWaves);
   const size_t lds = a.split ? sizeof(int) * (2 * (size_t)a.num_seqs + 1) : 0;
-  hipLaunchKernelGGL((decode_mfma_kernel<TT, D>), grid, dim3(kThreads), lds, s, a);
+  switch (mfma_sched()) {
+    case 1:
+      hipLaunchKernelGGL((decode_mfma_kernel<TT, D, 1, 2>), grid, dim3(kThreads), lds, s, a);
+      break;
+    case 2:
+      hipLaunchKernelGGL((decode_mfma_kernel<TT, D, 0, 3>), grid, dim3(kThreads), lds, s, a);
+      break;
+    default:
+      hipLaunchKernelGGL((decode_mfma_kernel<TT, D, 0, 2>), grid, dim3(kThreads), lds, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -56,6 +56,13 @@ __device__ __forceinline__ float wave_sum(float x) {
 __device__ __forceinline__ uint4 ld16(const char* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
+// Streaming (non-temporal) 16-byte load for K/V data that is read exactly
+// once per whole cache line: measured faster than a plain load on gfx950.
+__device__ __forceinline__ uint4 ld16nt(const char* p) {
+  typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 __device__ __forceinline__ uint32_t word(const uint4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
@@ -270,7 +277,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
       const int off = (hi ? off1 : off0) + (tq & 7);
       const char* kp = kbase + ((phys * hkv + g) * bs + off) * (D * EB) + c * 16;
 #pragma unroll
-      for (int i = 0; i < NK; ++i) kr[i] = ld16(kp + 64 * i);
+      for (int i = 0; i < NK; ++i) kr[i] = ld16nt(kp + 64 * i);
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -281,7 +288,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
       for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int u = 0; u < NVR; ++u)
-          vr[(j * R + r) * NVR + u] = ld16(vp + (int64_t)r * 64 * 8 * EB + 16 * u);
+          vr[(j * R + r) * NVR + u] = ld16nt(vp + (int64_t)r * 64 * 8 * EB + 16 * u);
     }
   };
 
