@@ -222,7 +222,8 @@ class Workload:
         self.replicas = self.args.replicas or max(1, int(math.ceil(2e9 / per_step)))
         gen = W.make_generator(sp.seed, dev)
         self.k, self.v, self.q = [], [], []
-        base_k = W.randn(W.k_pool_shape(self.nb, sp.num_kv_heads, sp.block_size, sp.head_dim),
+        base_k = W.randn(W.k_pool_shape(self.nb, sp.num_kv_heads, sp.block_size, sp.head_dim,
+                                         sp.dtype),
                          sp.dtype, gen, dev)
         base_v = W.randn(W.v_pool_shape(self.nb, sp.num_kv_heads, sp.block_size, sp.head_dim),
                          sp.dtype, gen, dev)
@@ -244,7 +245,7 @@ class Workload:
         ws = self.pa.pa_decode_workspace_bytes(B, sp.num_q_heads, sp.num_kv_heads, sp.head_dim,
                                                sp.block_size, self.max_ctx, self.part,
                                                W.TORCH_DTYPE[sp.dtype])
-        self.ws = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
+        self.ws = torch.zeros(max(ws, 1), dtype=torch.uint8, device=dev)
         self.config["partition"] = self.pa.pa_decode_partition_size(
             B, sp.num_q_heads, sp.num_kv_heads, sp.head_dim, sp.block_size, self.max_ctx,
             self.part, W.TORCH_DTYPE[sp.dtype])

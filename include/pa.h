@@ -31,15 +31,20 @@
  *    out-of-range id, a duplicate slot or an overlapping copy pair.
  *
  * KV pool layout (one layer).  BS = block_size, D = head_dim, Hkv = kv heads,
- * VS = min(BS, 8).  Element (physical block b, kv head h, offset o, dim d):
- *   K:  k_cache[((b*Hkv + h)*BS + o)*D + d]
+ * X = 16 / element size (4 for fp32, 8 for fp16 / bf16), VS = min(BS, 8).
+ * Element (physical block b, kv head h, offset o, dim d):
+ *   K:  k_cache[(((b*Hkv + h)*(D/X) + d/X)*BS + o)*X + d%X]
  *   V:  v_cache[(((b*Hkv + h)*(BS/VS) + o/VS)*D + d)*VS + o%VS]
- *  K stores token rows; V stores slabs of VS tokens, each slab [D][VS]
- *  (token index fastest): one 16-byte load is 8 tokens of one V row, which
- *  is what the weighted sum over tokens consumes (a VALU lane per row, or an
- *  MFMA operand for grouped heads), and a wavefront reads each slab with
- *  fully contiguous 16-byte loads.  A token's slot is b*BS + o ([P4]).
- *  BS must be 1, 2, 4, 8 or a multiple of 16.
+ *  K stores 16-byte pieces of X dims; piece p of all BS offsets of a block's
+ *  head is one run, so the pieces p .. p+3 of 16 consecutive tokens form one
+ *  contiguous kilobyte: exactly what a wavefront loads for one step of the
+ *  dot products q . K[u] (four lanes per token on the VALU path, one MFMA
+ *  operand of 16 tokens for grouped heads), in whole cache lines.  V stores
+ *  slabs of VS tokens, each slab [D][VS] (token index fastest): one 16-byte
+ *  load is 8 tokens of one V row, which is what the weighted sum over tokens
+ *  consumes, and a wavefront reads each slab with contiguous 16-byte loads.
+ *  A token's slot is b*BS + o ([P4]).  BS must be 1, 2, 4, 8 or a multiple
+ *  of 16; D must be a multiple of X.
  */
 #ifndef PA_H
 #define PA_H
@@ -100,7 +105,8 @@ const char* pa_strerror(pa_status s);
  *               partials; results agree across modes within rounding.
  *  workspace    device scratch of at least pa_decode_workspace_bytes(...)
  *               bytes (may be NULL when that size is 0); contents need no
- *               initialisation and are clobbered.
+ *               initialisation and are clobbered.  Calls that run
+ *               concurrently must not share a workspace.
  * Requirements: num_q_heads % num_kv_heads == 0; head_dim in {16, 32, 64,
  * 128, 256}; q, out and the pools 16-byte aligned.
  * ---------------------------------------------------------------------- */

@@ -33,9 +33,12 @@
  *  - a negative slot in the cache-write is padding and is skipped.
  *
  * Pool layout (the product's documented layout, re-implemented here):
- *   K element (blk, h, off, d)  at  ((blk*Hkv + h)*BS + off)*D + d
+ *   K element (blk, h, off, d)  at  (((blk*Hkv + h)*(D/X) + d/X)*BS + off)*X + d%X
  *   V element (blk, h, off, d)  at  (((blk*Hkv + h)*(BS/VS) + off/VS)*D + d)*VS + off%VS
- *   with VS = min(BS, 8): V is stored as 8-token slabs, each slab [D][VS].
+ *   with X = 16 / element size (K is stored as 16-byte pieces of X dims, the
+ *   pieces of all BS offsets for the same dims adjacent) and VS = min(BS, 8)
+ *   (V is stored as 8-token slabs, each slab [D][VS]).  D must be a multiple
+ *   of X.
  *
  * Parity status of each function: see the module docstring of the Python
  * wrapper; every function here is pinned by CPU tests.
@@ -85,15 +88,18 @@ static double load_elem(const void* base, int dtype, int64_t i) {
 
 static int v_slab(int bs) { return bs < 8 ? bs : 8; }
 
-static int64_t k_index(int64_t blk, int h, int off, int d, int hkv, int bs, int D) {
-  return ((blk * hkv + h) * bs + off) * (int64_t)D + d;
+/* Dims per 16-byte K piece. */
+static int k_piece(int dtype) { return (int)(16 / elem_bytes(dtype)); }
+
+static int64_t k_index(int64_t blk, int h, int off, int d, int hkv, int bs, int D, int x) {
+  return (((blk * hkv + h) * (D / x) + d / x) * (int64_t)bs + off) * x + d % x;
 }
 
 static int64_t v_index(int64_t blk, int h, int off, int d, int hkv, int bs, int D) {
   int vs = v_slab(bs);
-#if ORACLE_MUTANT == 7 /* mutant: V read as token-major rows, like K */
+#if ORACLE_MUTANT == 7 /* mutant: V read as plain token-major rows */
   (void)vs;
-  return k_index(blk, h, off, d, hkv, bs, D);
+  return ((blk * hkv + h) * bs + off) * (int64_t)D + d;
 #else
   return (((blk * hkv + h) * (bs / vs) + off / vs) * (int64_t)D + d) * vs + off % vs;
 #endif
@@ -146,7 +152,7 @@ static int decode_one(const decode_job* j, int b, int h, double* scores) {
 #if ORACLE_MUTANT == 4 /* mutant: K and V swapped */
       double kv = load_elem(j->vc, j->dtype, v_index(blk, g, u % bs, d, j->hkv, bs, D));
 #else
-      double kv = load_elem(j->kc, j->dtype, k_index(blk, g, u % bs, d, j->hkv, bs, D));
+      double kv = load_elem(j->kc, j->dtype, k_index(blk, g, u % bs, d, j->hkv, bs, D, k_piece(j->dtype)));
 #endif
       dot += load_elem(j->q, j->dtype, qrow + d) * kv;
     }
@@ -185,7 +191,7 @@ static int decode_one(const decode_job* j, int b, int h, double* scores) {
     int64_t blk = j->tables[(int64_t)b * j->maxb + u / bs];
     for (int d = 0; d < D; ++d) {
 #if ORACLE_MUTANT == 4
-      double vv = load_elem(j->kc, j->dtype, k_index(blk, g, u % bs, d, j->hkv, bs, D));
+      double vv = load_elem(j->kc, j->dtype, k_index(blk, g, u % bs, d, j->hkv, bs, D, k_piece(j->dtype)));
 #else
       double vv = load_elem(j->vc, j->dtype, v_index(blk, g, u % bs, d, j->hkv, bs, D));
 #endif
@@ -221,7 +227,8 @@ int oracle_decode(double* out, const void* q, const void* k_cache, const void* v
                   int block_size, int num_kv_heads, int num_seqs, int num_q_heads, int head_dim,
                   int max_blocks_per_seq, int64_t num_blocks, int dtype, int nthreads) {
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
-      num_q_heads % num_kv_heads != 0 || (block_size > 16 && block_size % 16 != 0))
+      num_q_heads % num_kv_heads != 0 || (block_size > 16 && block_size % 16 != 0) ||
+      head_dim % k_piece(dtype) != 0)
     return -1;
   if (nthreads < 1) nthreads = 1;
   int64_t items = (int64_t)num_seqs * num_q_heads;
@@ -282,6 +289,7 @@ int oracle_reshape_and_cache(const void* k, const void* v, void* k_cache, void* 
                              int64_t v_token_stride, int num_kv_heads, int head_dim, int block_size,
                              int64_t num_blocks, int dtype) {
   size_t es = elem_bytes(dtype);
+  if (head_dim % k_piece(dtype) != 0) return -1;
   for (int t = 0; t < num_tokens; ++t) {
     int64_t slot = slot_mapping[t];
     if (slot < 0) continue;
@@ -292,7 +300,7 @@ int oracle_reshape_and_cache(const void* k, const void* v, void* k_cache, void* 
       for (int d = 0; d < head_dim; ++d) {
         int64_t src_k = t * k_token_stride + (int64_t)h * head_dim + d;
         int64_t src_v = t * v_token_stride + (int64_t)h * head_dim + d;
-        memcpy((char*)k_cache + es * k_index(blk, h, off, d, num_kv_heads, block_size, head_dim),
+        memcpy((char*)k_cache + es * k_index(blk, h, off, d, num_kv_heads, block_size, head_dim, k_piece(dtype)),
                (const char*)k + es * src_k, es);
         memcpy((char*)v_cache + es * v_index(blk, h, off, d, num_kv_heads, block_size, head_dim),
                (const char*)v + es * src_v, es);
@@ -308,14 +316,15 @@ int oracle_copy_blocks(void* k_cache, void* v_cache, const int64_t* src_dst_pair
                        int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
                        int dtype) {
   size_t es = elem_bytes(dtype);
+  if (head_dim % k_piece(dtype) != 0) return -1;
   for (int p = 0; p < num_pairs; ++p) {
     int64_t src = src_dst_pairs[2 * p], dst = src_dst_pairs[2 * p + 1];
     if (src < 0 || dst < 0 || src >= num_blocks || dst >= num_blocks) return -1;
     for (int h = 0; h < num_kv_heads; ++h)
       for (int off = 0; off < block_size; ++off)
         for (int d = 0; d < head_dim; ++d) {
-          int64_t ks = k_index(src, h, off, d, num_kv_heads, block_size, head_dim);
-          int64_t kd = k_index(dst, h, off, d, num_kv_heads, block_size, head_dim);
+          int64_t ks = k_index(src, h, off, d, num_kv_heads, block_size, head_dim, k_piece(dtype));
+          int64_t kd = k_index(dst, h, off, d, num_kv_heads, block_size, head_dim, k_piece(dtype));
           int64_t vs = v_index(src, h, off, d, num_kv_heads, block_size, head_dim);
           int64_t vd = v_index(dst, h, off, d, num_kv_heads, block_size, head_dim);
           memcpy((char*)k_cache + es * kd, (const char*)k_cache + es * ks, es);

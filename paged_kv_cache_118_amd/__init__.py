@@ -6,8 +6,9 @@ of the computation runs in libpa's HIP kernels.  PyTorch supplies device
 memory and streams.  If ``libpa.so`` has not been built this module raises
 ImportError -- there is no fallback implementation.
 
-Pool layout (BS = block_size, D = head_dim, VS = min(BS, 8)):
-    k_cache: [num_blocks, Hkv, BS, D]
+Pool layout (BS = block_size, D = head_dim, X = 16 / element size,
+VS = min(BS, 8)):
+    k_cache: [num_blocks, Hkv, D // X, BS, X]
     v_cache: [num_blocks, Hkv, BS // VS, D, VS]
 """
 from __future__ import annotations
@@ -123,6 +124,31 @@ def v_slab(block_size: int) -> int:
     return block_size if block_size < 8 else 8
 
 
+def k_pool_shape(num_blocks, num_kv_heads, block_size, head_dim, dtype):
+    """K pool shape [blocks][Hkv][D/X][BS][X], X = 16 / element size (pa.h)."""
+    x = 16 // torch.empty((), dtype=dtype).element_size()
+    return (num_blocks, num_kv_heads, head_dim // x, block_size, x)
+
+
+def v_pool_shape(num_blocks, num_kv_heads, block_size, head_dim):
+    """V pool shape [blocks][Hkv][BS/VS][D][VS], VS = min(BS, 8) (pa.h)."""
+    vs = v_slab(block_size)
+    return (num_blocks, num_kv_heads, block_size // vs, head_dim, vs)
+
+
+def _check_pools(k_cache, v_cache, num_kv_heads, block_size, head_dim):
+    nb = k_cache.shape[0]
+    want_k = k_pool_shape(nb, num_kv_heads, block_size, head_dim, k_cache.dtype)
+    want_v = v_pool_shape(nb, num_kv_heads, block_size, head_dim)
+    if tuple(k_cache.shape) != want_k:
+        raise ValueError(f"k_cache shape {tuple(k_cache.shape)} is not {want_k}")
+    if tuple(v_cache.shape) != want_v:
+        raise ValueError(f"v_cache shape {tuple(v_cache.shape)} is not {want_v}")
+    if k_cache.dtype != v_cache.dtype:
+        raise ValueError("k_cache and v_cache must have one dtype")
+    return nb
+
+
 # ---------------------------------------------------------------- decode --
 def pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                               max_context_len, partition_size=0, dtype=torch.float16) -> int:
@@ -143,21 +169,15 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, block
     """out[b, h] = softmax over the first context_lens[b] positions (see pa.h).
 
     ``max_context_len`` is a host int >= every context length.  ``workspace``
-    is a uint8 device tensor of pa_decode_workspace_bytes(...) bytes; one is
-    allocated when omitted and needed."""
+    is a uint8 device tensor of pa_decode_workspace_bytes(...) bytes (no
+    initialisation needed, reusable across calls); one is allocated when
+    omitted and needed."""
     B, hq, D = q.shape
     if out.shape != q.shape or out.dtype != q.dtype:
         raise ValueError("out must match q in shape and dtype")
     if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
         raise ValueError("pools must have q's dtype")
-    nb = k_cache.shape[0]
-    vs = v_slab(block_size)
-    if tuple(k_cache.shape) != (nb, num_kv_heads, block_size, D):
-        raise ValueError(f"k_cache shape {tuple(k_cache.shape)} is not "
-                         f"{(nb, num_kv_heads, block_size, D)}")
-    if tuple(v_cache.shape) != (nb, num_kv_heads, block_size // vs, D, vs):
-        raise ValueError(f"v_cache shape {tuple(v_cache.shape)} is not "
-                         f"{(nb, num_kv_heads, block_size // vs, D, vs)}")
+    nb = _check_pools(k_cache, v_cache, num_kv_heads, block_size, D)
     if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
         raise ValueError("block_tables and context_lens must be int32")
     if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
@@ -189,7 +209,7 @@ def pa_reshape_and_cache(k, v, k_cache, v_cache, slot_mapping, block_size, strea
             raise ValueError(f"{name} rows must be [Hkv, D] contiguous per token")
     if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (T,):
         raise ValueError("slot_mapping must be int64 [num_tokens]")
-    nb = k_cache.shape[0]
+    nb = _check_pools(k_cache, v_cache, hkv, block_size, D)
     _check(_lib.pa_reshape_and_cache(ctypes.c_void_p(k.data_ptr()),
                                      ctypes.c_void_p(v.data_ptr()),
                                      _dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"),
@@ -203,7 +223,10 @@ def pa_copy_blocks(k_cache, v_cache, src_dst_pairs, block_size, stream=None):
     if src_dst_pairs.dtype != torch.int64 or src_dst_pairs.dim() != 2 or \
             src_dst_pairs.shape[1] != 2:
         raise ValueError("src_dst_pairs must be int64 [num_pairs, 2]")
-    nb, hkv, _, D = k_cache.shape
+    if v_cache.dim() != 5:
+        raise ValueError("v_cache must be [blocks][Hkv][BS/VS][D][VS]")
+    hkv, D = v_cache.shape[1], v_cache.shape[3]
+    nb = _check_pools(k_cache, v_cache, hkv, block_size, D)
     _check(_lib.pa_copy_blocks(_dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"),
                                _dev_ptr(src_dst_pairs, "src_dst_pairs"), src_dst_pairs.shape[0],
                                hkv, D, block_size, nb, _dtype_code(k_cache), _stream(stream)))

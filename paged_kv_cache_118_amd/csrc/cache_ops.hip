@@ -16,8 +16,10 @@ constexpr int kThreads = 256;
 
 // One workgroup = TT consecutive tokens of one kv head, 8*TT threads (TT = 32
 // for large writes, 8 for decode-sized ones so more CUs share the stores).
-//  K: token rows are contiguous on both sides -> 16-byte vector copies.
-//  V: the pool stores 16-token slabs [D][VS]; rows are staged in LDS and each
+//  K: the pool stores 16-byte pieces [D/X][BS][X]; piece c of a token row is
+//     one 16-byte copy.  Threads take tokens fastest, so consecutive slots of
+//     one block write one contiguous run per piece.
+//  V: the pool stores 8-token slabs [D][VS]; rows are staged in LDS and each
 //     lane then writes one token's element, so lanes with consecutive slots
 //     write consecutive addresses of a slab row.
 template <int ES, int TT>
@@ -36,10 +38,10 @@ __global__ __launch_bounds__(8 * TT) void reshape_and_cache_kernel(
   const int64_t max_slot = num_blocks * (int64_t)bs;
   const int vs = v_slab(bs);
 
-  // K rows (and V rows into LDS): one 16-byte chunk per thread per iteration.
+  // K pieces (and V rows into LDS): one 16-byte piece per thread per iteration.
   const int chunks = row_bytes / 16;
   for (int i = threadIdx.x; i < nt * chunks; i += NT) {
-    const int tt = i / chunks, c = i % chunks;
+    const int c = i / nt, tt = i - c * nt;
     const int64_t t = t0 + tt;
     const int64_t slot = slots[t];
     const uint4 kv = *reinterpret_cast<const uint4*>(k + (t * k_stride + (int64_t)h * D) * ES +
@@ -55,7 +57,7 @@ __global__ __launch_bounds__(8 * TT) void reshape_and_cache_kernel(
     if (slot >= 0 && slot < max_slot) {
       const int64_t blk = slot / bs;
       const int off = (int)(slot - blk * bs);
-      *reinterpret_cast<uint4*>(k_cache + (((blk * hkv + h) * bs + off) * D) * ES + c * 16) = kv;
+      *reinterpret_cast<uint4*>(k_cache + (((blk * hkv + h) * chunks + c) * bs + off) * 16) = kv;
     }
   }
   __syncthreads();

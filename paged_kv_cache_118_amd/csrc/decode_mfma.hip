@@ -13,16 +13,20 @@
 // kb = lane / 16) and v_mfma_f32_16x16x32 (A: row n, k-slots of group kb;
 // B: column n, same k-slots; C: column n, rows 4*kb .. 4*kb+3):
 //   S^T = K Q^T  : A = K rows (tokens), B = Q^T (heads, zero past G), two
-//                  16-token tiles x D/32 k-steps (k-step s, group kb: d =
-//                  32*s + 8*kb .. +7, a contiguous 64 B per row per load).  Tile j's row r holds
-//                  token 8*(r/4) + 4*j + r%4, so lane (n, kb) ends up with
-//                  the scores of head n for the 8 tokens 8*kb .. 8*kb+7.
+//                  16-token tiles x D/32 k-steps.  Tile j's row r is token
+//                  16*j + r; k-step s of group kb is d = 32*s + 8*kb .. +7,
+//                  i.e. 16-byte K piece 4*s + kb, so each load instruction
+//                  reads pieces 4s .. 4s+3 of 16 consecutive offsets: whole
+//                  128-byte lines of the piece-major K pool.  Lane (n, kb)
+//                  gets the scores of head n for tokens 4*kb .. 4*kb+3 and
+//                  16+4*kb .. 16+4*kb+3.
 //   O^T += V^T P^T : A = V^T (16 d rows, 8 tokens per k-group, read as one
-//                  16-byte row of an 8-token [D][8] V slab), B = P^T, which is
-//                  exactly the lane's 8 weights; C = O^T keeps head n in lane
-//                  n for every d tile, so the online-softmax rescale of the
-//                  accumulators needs no data exchange.
-// Only the max / sum over the 4 k-groups of a head crosses lanes (xor 16, 32).
+//                  16-byte row of an 8-token [D][8] V slab), B = P^T: lane
+//                  (n, kb) needs the weights of tokens 8*kb .. 8*kb+7, which
+//                  four lane permutes gather from the QK layout.  C = O^T
+//                  keeps head n in lane n for every d tile, so the online-
+//                  softmax rescale of the accumulators is lane-local.
+// The max / sum over the 4 k-groups of a head cross lanes (xor 16, 32).
 #include <math.h>
 #include <stdlib.h>
 
@@ -109,16 +113,19 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_mfma_kernel(DecodeArgs a
 
   Cursor c0;
   int count;
-  int C = 0, x0 = 0;  // split 1: steps per worker, first stream step of this worker
+  Split sp{};
+  int64_t x0 = 0;  // split 1: first stream step of this worker
   if (a.split) {
     if (wv == 0) wave_scan_steps(a.context_lens, B, H, a.len_cap, kGroup, s_pre, s_len);
     __syncthreads();
-    const int N = s_pre[B];
-    C = chunk_steps(a, N);
-    x0 = worker * C;
-    if (x0 >= N) return;
-    count = min(C, N - x0);
-    c0 = locate(s_pre, s_len, B, H, kGroup, x0);
+    const int N = s_pre[B];  // empty sequences get their zero rows from the merge
+    if (N == 0) return;
+    sp = make_split(a, N);
+    if (worker >= sp.W) return;
+    x0 = sp.start(worker);
+    const int64_t x1 = sp.start(worker + 1);  // fixed chunks: the last one ends at N
+    count = (int)((x1 < N ? x1 : N) - x0);
+    c0 = locate(s_pre, s_len, B, H, kGroup, (int)x0);
   } else {
     if (worker >= B * H) return;
     c0.b = worker / H;
@@ -154,9 +161,9 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_mfma_kernel(DecodeArgs a
 
   // K row of tile j for this lane plus (when the item changes) the Q^T
   // operand of the item: head n.  K-step s, element e of k-group kb carries
-  // d = 32*s + 8*kb + e in both operands, so the four k-groups of one row read
-  // a contiguous 64-byte segment per load instruction.
-  const int kt_off0 = (n >> 2) * 8 + (n & 3);  // token of tile 0 row n (tile 1: +4)
+  // d = 32*s + 8*kb + e in both operands.
+  constexpr int NC = D / 8;                     // 16-byte K pieces per token
+  const int64_t pstride = (int64_t)4 * bs * 16;  // bytes from piece p to p + 4
   auto issue_k = [&](const Cursor& cu, uint4 (&kr)[2][KN], uint4 (&qr)[KN], int& qitem) {
     const int item = cu.item(H);
     if (qitem != item) {
@@ -177,14 +184,14 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_mfma_kernel(DecodeArgs a
     const int64_t g = cu.h;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int t = tok + kt_off0 + 4 * j;
+      const int t = tok + 16 * j + n;
       const int lb = t / bs;
       int64_t phys = tw.get(lb0);
       for (int q = 1; q < nb_grp; ++q)
         if (lb == lb0 + q) phys = tw.get(lb0 + q);
-      const char* kp = kbase + (((phys * hkv + g) * bs + (t - lb * bs)) * D + kb * 8) * EB;
+      const char* kp = kbase + (((phys * hkv + g) * NC + kb) * bs + (t - lb * bs)) * 16;
 #pragma unroll
-      for (int i = 0; i < KN; ++i) kr[j][i] = ld16(kp + 64 * i);
+      for (int i = 0; i < KN; ++i) kr[j][i] = ld16nt(kp + i * pstride);
     }
   };
   // The V token run of k-group kb (8 tokens of one slab row per d tile).  Its
@@ -220,7 +227,7 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_mfma_kernel(DecodeArgs a
       for (int mt = 0; mt < MT; ++mt) acc[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
       seg_k0 = cu.k;
       if (a.split && cu.k == 0 && lane == 0) {  // this worker starts the item
-        const int last = (x0 + j + cu.n - 1) / C;
+        const int last = sp.worker_of(x0 + j + cu.n - 1);
         a.ws_desc[cu.item(H)] = make_int2(worker, last - worker + 1);
       }
     }
@@ -240,8 +247,9 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_mfma_kernel(DecodeArgs a
     }
     if (nvalid < kGroup) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (kb * 8 + e >= nvalid) sc[e] = -INFINITY;  // select: masked K may be NaN
+      for (int e = 0; e < 8; ++e)  // token of sc[e]: 4*kb + e, then 16 + 4*kb + e-4
+        if ((e < 4 ? 4 * kb + e : 12 + 4 * kb + e) >= nvalid)
+          sc[e] = -INFINITY;  // select: masked K may be NaN
     }
     float mx = sc[0];
 #pragma unroll
@@ -260,8 +268,21 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_mfma_kernel(DecodeArgs a
     m_run = m_new;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[mt] *= alpha;
-    pb = make_uint4(pack2(TT{}, pw[0], pw[1]), pack2(TT{}, pw[2], pw[3]),
-                    pack2(TT{}, pw[4], pw[5]), pack2(TT{}, pw[6], pw[7]));
+    // P^T operand: lane kb needs tokens 8*kb .. 8*kb+7, the 4-token runs of
+    // tile kb/2 held by k-groups 2*(kb%2) and 2*(kb%2)+1.  Two permutes fetch
+    // them.  In each, a source lane offers tile 0 or tile 1 by its own parity,
+    // and the reader-to-source maps {0,2,1,3} and {1,3,0,2} send every reader
+    // to a source offering the tile it needs.
+    const uint32_t t0a = pack2(TT{}, pw[0], pw[1]), t0b = pack2(TT{}, pw[2], pw[3]);
+    const uint32_t t1a = pack2(TT{}, pw[4], pw[5]), t1b = pack2(TT{}, pw[6], pw[7]);
+    const bool ev = (kb & 1) == 0;
+    const int p1 = ((kb & 1) << 1) | (kb >> 1);
+    const int src1 = (n + 16 * p1) * 4, src2 = (n + 16 * (p1 ^ 1)) * 4;
+    const uint32_t a0 = __builtin_amdgcn_ds_bpermute(src1, ev ? t0a : t1a);
+    const uint32_t a1 = __builtin_amdgcn_ds_bpermute(src1, ev ? t0b : t1b);
+    const uint32_t b0 = __builtin_amdgcn_ds_bpermute(src2, ev ? t1a : t0a);
+    const uint32_t b1 = __builtin_amdgcn_ds_bpermute(src2, ev ? t1b : t0b);
+    pb = kb < 2 ? make_uint4(a0, a1, b0, b1) : make_uint4(b0, b1, a0, a1);
   };
 
   // Phase 2: O^T += V^T P^T, and the segment's output at its end.
@@ -289,16 +310,19 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_mfma_kernel(DecodeArgs a
       float l_tot = l_lane + __shfl_xor(l_lane, 16);
       l_tot += __shfl_xor(l_tot, 32);
       const int item = cu.item(H);
-      if (n < G) {
-        if (seg_k0 == 0 && cu.k == cu.n - 1) {
-          const int64_t orow = ((int64_t)cu.b * a.num_q_heads + (int64_t)cu.h * G + n) * D;
+      const int64_t orow0 = (int64_t)cu.b * a.num_q_heads + (int64_t)cu.h * G;
+      if (seg_k0 == 0 && cu.k == cu.n - 1) {
+        if (n < G) {
+          const int64_t orow = (orow0 + n) * D;
           const float inv = 1.f / l_tot;
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
               store_out<TT>(a.out, orow + mt * 16 + 4 * kb + e, acc[mt][e] * inv);
-        } else {
+        }
+      } else {
+        if (n < G) {
           const int64_t row = ((int64_t)item + worker) * G + n;  // slot item + worker
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt)

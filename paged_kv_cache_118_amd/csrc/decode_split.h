@@ -4,16 +4,18 @@
 // kernel, kv heads for the GQA kernel), ordered b-major.  Item (b, h) has
 // n_b = ceil(L_b / STEP) steps of STEP tokens.  Laid end to end the items form
 // one stream of N = sum_b H * n_b steps; worker w (one wavefront) takes steps
-// [w*C, min((w+1)*C, N)).  Every worker therefore streams the same number of
-// K/V bytes regardless of how lengths are distributed, and it prefetches
-// straight across item boundaries.
+// [start(w), start(w+1)): either W equal shares (start(w) = w*N/W, so shares
+// differ by at most one step) or fixed chunks of C steps.  Every worker
+// therefore streams the same number of K/V bytes regardless of how lengths
+// are distributed, and it prefetches straight across item boundaries.
 //
 // A worker that sees all of an item's steps writes the final output row;
 // otherwise it writes its partial (m, l, o) to slot item + w.  That slot is
 // unique: along the stream every new (item, worker) segment increases the
-// item index, the worker index or both.  The merge kernel recovers, for item
-// i starting at stream step S_i, the workers F = S_i / C .. Lw = (S_i+n-1)/C
-// that touched it and combines their slots.
+// item index, the worker index or both.  Item i starting at stream step S_i
+// is shared by the workers F = worker_of(S_i) .. Lw = worker_of(S_i + n - 1);
+// worker F records (F, Lw - F + 1) for the merge kernel, which combines the
+// slots.
 #pragma once
 
 #include "pa_internal.h"
@@ -53,14 +55,37 @@ __device__ inline int wave_scan_steps(const int32_t* lens, int B, int H, int cap
   return __shfl(incl, 63);
 }
 
-// Steps per worker: an equal share, but at least kMinChunk so that a worker's
-// start-up is amortised and an item never has more than n / kMinChunk + 1
-// partials.
+// Balanced shares are at least kMinChunk steps, so that a worker's start-up
+// is amortised and an item never has more than n / kMinChunk + 2 partials.
 constexpr int kMinChunk = 8;
-__device__ __forceinline__ int chunk_steps(const DecodeArgs& a, int N) {
-  if (a.chunk_steps > 0) return a.chunk_steps;
-  const int c = (N + a.num_workers - 1) / a.num_workers;
-  return c > kMinChunk ? c : kMinChunk;
+
+struct Split {
+  int64_t N;  // steps in the stream (> 0)
+  int W;      // workers that take steps
+  int C;      // fixed steps per worker, 0 = W equal shares
+  // First step of worker w's share (for w == W: N with equal shares, possibly
+  // past N with fixed chunks -- callers clamp).
+  __device__ __forceinline__ int64_t start(int w) const {
+    return C ? (int64_t)w * C : (int64_t)w * N / W;
+  }
+  // The worker whose share holds stream step x: the largest w with start(w) <= x.
+  __device__ __forceinline__ int worker_of(int64_t x) const {
+    return C ? (int)(x / C) : (int)(((x + 1) * W - 1) / N);
+  }
+};
+
+__device__ __forceinline__ Split make_split(const DecodeArgs& a, int N) {
+  Split s;
+  s.N = N;
+  if (a.chunk_steps > 0) {
+    s.C = a.chunk_steps;
+    s.W = (N + s.C - 1) / s.C;
+  } else {
+    s.C = 0;
+    const int cap = N / kMinChunk;
+    s.W = a.num_workers < cap ? a.num_workers : (cap > 0 ? cap : 1);
+  }
+  return s;
 }
 
 // Position in the step stream: sequence b, head h, step k of n, length L.

@@ -201,16 +201,19 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
 
   Cursor c0;
   int count;
-  int C = 0, x0 = 0;  // split 1: steps per worker, first stream step of this worker
+  Split sp{};
+  int64_t x0 = 0;  // split 1: first stream step of this worker
   if (a.split) {
     if (wv == 0) wave_scan_steps(a.context_lens, B, H, a.len_cap, kStep, s_pre, s_len);
     __syncthreads();
-    const int N = s_pre[B];
-    C = chunk_steps(a, N);
-    x0 = worker * C;
-    if (x0 >= N) return;
-    count = min(C, N - x0);
-    c0 = locate(s_pre, s_len, B, H, kStep, x0);
+    const int N = s_pre[B];  // empty sequences get their zero rows from the merge
+    if (N == 0) return;
+    sp = make_split(a, N);
+    if (worker >= sp.W) return;
+    x0 = sp.start(worker);
+    const int64_t x1 = sp.start(worker + 1);  // fixed chunks: the last one ends at N
+    count = (int)((x1 < N ? x1 : N) - x0);
+    c0 = locate(s_pre, s_len, B, H, kStep, (int)x0);
   } else {
     if (worker >= B * H) return;
     c0.b = worker / H;
@@ -272,12 +275,15 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
     const int off0 = tok - lb0 * bs, off1 = tok + 8 - lb1 * bs;  // multiples of 8
     const int64_t g = cu.h / group;
     {
+      // 16-byte K piece c + 4i of token tq: for each i the wavefront reads
+      // pieces 4i .. 4i+3 of 16 consecutive offsets, whole 128-byte lines.
       const bool hi = tq >= 8;
       const int64_t phys = hi ? ph1 : ph0;
       const int off = (hi ? off1 : off0) + (tq & 7);
-      const char* kp = kbase + ((phys * hkv + g) * bs + off) * (D * EB) + c * 16;
+      const char* kp = kbase + (((phys * hkv + g) * (4 * NK) + c) * bs + off) * 16;  // 4*NK pieces per row
+      const int64_t pstride = (int64_t)4 * bs * 16;  // 4 pieces further
 #pragma unroll
-      for (int i = 0; i < NK; ++i) kr[i] = ld16nt(kp + 64 * i);
+      for (int i = 0; i < NK; ++i) kr[i] = ld16nt(kp + i * pstride);
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -307,7 +313,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
       for (int r = 0; r < R; ++r) acc[r] = 0.f;
       seg_k0 = cu.k;
       if (a.split && cu.k == 0 && lane == 0) {  // this worker starts the item
-        const int last = (x0 + j + cu.n - 1) / C;
+        const int last = sp.worker_of(x0 + j + cu.n - 1);
         a.ws_desc[cu.item(H)] = make_int2(worker, last - worker + 1);
       }
     }
@@ -425,7 +431,8 @@ __global__ __launch_bounds__(64) void decode_generic_kernel(DecodeArgs a) {
     for (int r = 0; r < MAXR; ++r) {
       const int d = lane + 64 * r;
       if (d < D)
-        part += qd[r] * load_elem<TT>(a.k_cache, (((int64_t)blk * hkv + g) * bs + off) * D + d);
+        part += qd[r] * load_elem<TT>(a.k_cache,
+                                      k_elem_index(blk, g, off, d, hkv, bs, D, TT::bytes));
     }
     const float sc = wave_sum(part) * a.scale_log2e;
     const float m_new = fmaxf(m, sc);

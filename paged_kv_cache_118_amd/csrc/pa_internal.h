@@ -79,7 +79,7 @@ struct DecodeArgs {
   int64_t num_blocks;
   // work split (decode_split.h)
   int32_t split;        // 0: one item per worker, 1: token-balanced stream split
-  int32_t chunk_steps;  // split 1: steps per worker, 0 = ceil(N / num_workers)
+  int32_t chunk_steps;  // split 1: fixed steps per worker, 0 = equal shares
   int32_t num_workers;  // wavefronts launched
   // partials of split items, slot = item + worker (split 1 only); rows of an
   // item are its q heads (1 for the MHA kernel, the group for the GQA kernel)
@@ -109,5 +109,15 @@ hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs
 
 // Tokens per V slab: V is stored as [block][head][BS/VS][D][VS].
 __host__ __device__ inline int v_slab(int block_size) { return block_size < 8 ? block_size : 8; }
+
+// K is stored as 16-byte pieces, [block][head][D/X][BS][X] with X = 16 / element
+// size: piece p of every offset of a block's head is adjacent, so 16
+// consecutive tokens' piece p form one 256-byte run.  Element index of
+// (block, head, offset, d):
+__host__ __device__ inline int64_t k_elem_index(int64_t blk, int64_t h, int off, int d,
+                                                int64_t hkv, int bs, int D, int elem_bytes) {
+  const int x = 16 / elem_bytes;
+  return (((blk * hkv + h) * (D / x) + d / x) * bs + off) * x + d % x;
+}
 
 }  // namespace pa

@@ -5,8 +5,9 @@ failure message.  ``test_oracle_decode.py`` runs them on the real oracle (all
 must hold) and on builds with one planted mistake (each must break one).
 
 The pool is filled here with numpy shaped indexing -- K as
-[blocks][Hkv][BS][D], V as [blocks][Hkv][BS/VS][D][VS] -- independently of
-the oracle's pointer arithmetic.
+[blocks][Hkv][D/X][BS][X] (X dims per 16-byte piece: 4 for fp32, 8 for 16-bit
+types), V as [blocks][Hkv][BS/VS][D][VS] -- independently of the oracle's
+pointer arithmetic.
 """
 from __future__ import annotations
 
@@ -17,16 +18,17 @@ import numpy as np
 from workloads import v_slab
 
 
-def place(seqs_k, seqs_v, tables, bs, num_blocks, fill=np.nan):
-    """Pool arrays holding each sequence's logical K/V rows ([L][Hkv][D])."""
+def place(seqs_k, seqs_v, tables, bs, num_blocks, fill=np.nan, x=4):
+    """Pool arrays holding each sequence's logical K/V rows ([L][Hkv][D]);
+    x = dims per 16-byte K piece of the storage dtype the pools will be cast to."""
     hkv, D = seqs_k[0].shape[1], seqs_k[0].shape[2]
     vs = v_slab(bs)
-    kp = np.full((num_blocks, hkv, bs, D), fill, dtype=np.float32)
+    kp = np.full((num_blocks, hkv, D // x, bs, x), fill, dtype=np.float32)
     vp = np.full((num_blocks, hkv, bs // vs, D, vs), fill, dtype=np.float32)
     for i, (K, V) in enumerate(zip(seqs_k, seqs_v)):
         for u in range(K.shape[0]):
             blk, off = int(tables[i, u // bs]), u % bs
-            kp[blk, :, off, :] = K[u]
+            kp[blk, :, :, off, :] = K[u].reshape(hkv, D // x, x)
             vp[blk, :, off // vs, :, off % vs] = V[u]
     return kp, vp
 
@@ -60,12 +62,12 @@ def dense_attention(q, Ks, Vs, scale, group):
     return out
 
 
-def random_case(rng, lens, hq=4, hkv=2, D=8, bs=4, max_blocks=None):
+def random_case(rng, lens, hq=4, hkv=2, D=8, bs=4, max_blocks=None, x=4):
     Ks = [rng.standard_normal((L, hkv, D)).astype(np.float32) for L in lens]
     Vs = [rng.standard_normal((L, hkv, D)).astype(np.float32) for L in lens]
     q = rng.standard_normal((len(lens), hq, D)).astype(np.float32)
     t, nb = random_tables(lens, bs, rng, max_blocks=max_blocks)
-    kp, vp = place(Ks, Vs, t, bs, nb)
+    kp, vp = place(Ks, Vs, t, bs, nb, x=x)
     return q, Ks, Vs, t, nb, kp, vp
 
 
@@ -122,9 +124,10 @@ def pin_zero_k(orc):
 def pin_weights_1_2_4(orc):
     """Scores 0, ln2, 2 ln2 over three keys in two shuffled blocks of two:
     the global weights are 1 : 2 : 4, o = (v0 + 2 v1 + 4 v2) / 7."""
-    q = np.array([[[1.0, 0.0]]], dtype=np.float32)
-    K = np.array([[[0.0, 7.0]], [[1.0, -3.0]], [[2.0, 5.0]]], dtype=np.float32)
-    V = np.array([[[1.0, -2.0]], [[3.0, 0.5]], [[-4.0, 8.0]]], dtype=np.float32)
+    # head_dim 4 (one fp32 K piece): the last two dims are zero padding
+    q = np.array([[[1.0, 0.0, 0.0, 0.0]]], dtype=np.float32)
+    K = np.array([[[0.0, 7.0, 0, 0]], [[1.0, -3.0, 0, 0]], [[2.0, 5.0, 0, 0]]], dtype=np.float32)
+    V = np.array([[[1.0, -2.0, 0, 0]], [[3.0, 0.5, 0, 0]], [[-4.0, 8.0, 0, 0]]], dtype=np.float32)
     t = np.array([[2, 0]], dtype=np.int32)
     kp, vp = place([K], [V], t, 2, 3)
     out = orc.decode(q, kp, vp, t, [3], math.log(2.0), 2, 1, "f32")

@@ -14,7 +14,7 @@ pytestmark = pytest.mark.gpu
 
 def _pool(nb, hkv, bs, D, dtype, seed):
     g = W.make_generator(seed, DEV)
-    k = W.randn(W.k_pool_shape(nb, hkv, bs, D), dtype, g, DEV)
+    k = W.randn(W.k_pool_shape(nb, hkv, bs, D, dtype), dtype, g, DEV)
     v = W.randn(W.v_pool_shape(nb, hkv, bs, D), dtype, g, DEV)
     return k, v
 
@@ -109,8 +109,8 @@ def test_validate_mode_rejects_bad_indices():
     code = r"""
 import numpy as np, torch, paged_kv_cache_118_amd as pa
 dev = torch.device('cuda:0')
-kc = torch.zeros(4, 2, 16, 128, dtype=torch.float16, device=dev)
-vc = torch.zeros(4, 2, 1, 128, 16, dtype=torch.float16, device=dev)
+kc = torch.zeros(pa.k_pool_shape(4, 2, 16, 128, torch.float16), dtype=torch.float16, device=dev)
+vc = torch.zeros(pa.v_pool_shape(4, 2, 16, 128), dtype=torch.float16, device=dev)
 k = torch.zeros(2, 2, 128, dtype=torch.float16, device=dev)
 bad = torch.tensor([3, 3], dtype=torch.int64, device=dev)
 try:

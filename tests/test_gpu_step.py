@@ -49,7 +49,7 @@ class _Side:
         self.bs = bs
         self.alloc = pa.BlockAllocator(nb, bs, shuffle_seed=seed) if gpu else \
             BlockPool(nb, bs, shuffle_seed=seed)
-        shape_k = W.k_pool_shape(nb, hkv, bs, D)
+        shape_k = W.k_pool_shape(nb, hkv, bs, D, dtype)
         shape_v = W.v_pool_shape(nb, hkv, bs, D)
         tdt = W.TORCH_DTYPE[dtype]
         if gpu:
@@ -113,7 +113,8 @@ def _logical_rows(k, v, table, L, bs):
     """[L][Hkv][D] K and V rows of one sequence, read through its table with
     numpy shaped indexing of the documented layout."""
     vs = W.v_slab(bs)
-    ks = np.stack([k[table[u // bs], :, u % bs, :] for u in range(L)])
+    hkv = k.shape[1]
+    ks = np.stack([k[table[u // bs], :, :, u % bs, :].reshape(hkv, -1) for u in range(L)])
     vv = np.stack([v[table[u // bs], :, (u % bs) // vs, :, (u % bs) % vs] for u in range(L)])
     return ks, vv
 

@@ -16,24 +16,29 @@ def orc():
 
 
 @pytest.mark.parametrize("bs", [1, 4, 16, 32])
-def test_write_single_head_d1_is_flat_slot_array(orc, bs):
-    """Hkv = 1, D = 1: physical block b covers the flat slots b*BS ... (b+1)*BS-1,
-    so each pool, read flat, is indexed by the slot itself."""
-    nb = 6
+def test_write_single_head_is_flat_slot_array(orc, bs):
+    """Hkv = 1 and D = 4 (one 16-byte fp32 K piece): physical block b covers
+    the flat slots b*BS ... (b+1)*BS-1, so the K pool read as [slot][D] rows,
+    and the V pool once its slabs are turned back into rows, are indexed by
+    the slot itself."""
+    nb, D = 6, 4
+    vs = v_slab(bs)
     rng = np.random.default_rng(bs)
     slots = rng.permutation(nb * bs)[: nb * bs - 3].astype(np.int64)
     T = len(slots)
-    k = rng.standard_normal((T, 1, 1)).astype(np.float32)
-    v = rng.standard_normal((T, 1, 1)).astype(np.float32)
-    kc = np.full(nb * bs, np.nan, dtype=np.float32)
-    vc = np.full(nb * bs, np.nan, dtype=np.float32)
-    orc.reshape_and_cache(k, v, kc, vc, slots, 1, 1, bs, "f32")
-    want_k = np.full(nb * bs, np.nan, dtype=np.float32)
-    want_v = np.full(nb * bs, np.nan, dtype=np.float32)
-    want_k[slots] = k[:, 0, 0]
-    want_v[slots] = v[:, 0, 0]
-    assert np.array_equal(kc, want_k, equal_nan=True)
-    assert np.array_equal(vc, want_v, equal_nan=True)
+    k = rng.standard_normal((T, 1, D)).astype(np.float32)
+    v = rng.standard_normal((T, 1, D)).astype(np.float32)
+    kc = np.full(nb * bs * D, np.nan, dtype=np.float32)
+    vc = np.full(nb * bs * D, np.nan, dtype=np.float32)
+    orc.reshape_and_cache(k, v, kc, vc, slots, 1, D, bs, "f32")
+    k_rows = kc.reshape(nb * bs, D)
+    v_rows = vc.reshape(nb * bs // vs, D, vs).transpose(0, 2, 1).reshape(nb * bs, D)
+    want_k = np.full((nb * bs, D), np.nan, dtype=np.float32)
+    want_v = np.full((nb * bs, D), np.nan, dtype=np.float32)
+    want_k[slots] = k[:, 0]
+    want_v[slots] = v[:, 0]
+    assert np.array_equal(k_rows, want_k, equal_nan=True)
+    assert np.array_equal(v_rows, want_v, equal_nan=True)
 
 
 @pytest.mark.parametrize("bs", [2, 4, 16, 32])
@@ -47,7 +52,7 @@ def test_write_then_decode_is_dense_attention(orc, bs):
     Vs = [rng.standard_normal((L, hkv, D)).astype(np.float32) for L in lens]
     q = rng.standard_normal((len(lens), hq, D)).astype(np.float32)
     t, nb = P.random_tables(lens, bs, rng)
-    kc = np.full((nb, hkv, bs, D), np.nan, dtype=np.float32)
+    kc = np.full((nb, hkv, D // 4, bs, 4), np.nan, dtype=np.float32)
     vc = np.full((nb, hkv, bs // v_slab(bs), D, v_slab(bs)), np.nan, dtype=np.float32)
     slots = [int(t[i, u // bs]) * bs + u % bs for i, L in enumerate(lens) for u in range(L)]
     k = np.concatenate(Ks)
@@ -62,14 +67,14 @@ def test_write_then_decode_is_dense_attention(orc, bs):
 def test_write_skips_negative_slots_and_leaves_rest(orc):
     rng = np.random.default_rng(30)
     nb, hkv, bs, D = 5, 2, 4, 8
-    kc = rng.standard_normal((nb, hkv, bs, D)).astype(np.float32)
+    kc = rng.standard_normal((nb, hkv, D // 4, bs, 4)).astype(np.float32)
     vc = rng.standard_normal((nb, hkv, 1, D, bs)).astype(np.float32)
     k0, v0 = kc.copy(), vc.copy()
     k = rng.standard_normal((3, hkv, D)).astype(np.float32)
     v = rng.standard_normal((3, hkv, D)).astype(np.float32)
     orc.reshape_and_cache(k, v, kc, vc, np.array([-1, 9, -5]), hkv, D, bs, "f32")
     # only slot 9 = block 2, offset 1 changed
-    k0[2, :, 1, :] = k[1]
+    k0[2, :, :, 1, :] = k[1].reshape(hkv, D // 4, 4)
     v0[2, :, 0, :, 1] = v[1]
     assert np.array_equal(kc, k0) and np.array_equal(vc, v0)
 
@@ -80,7 +85,7 @@ def test_write_strided_token_rows(orc):
     nb, hkv, bs, D = 4, 2, 16, 8
     qkv = rng.standard_normal((5, 3, hkv, D)).astype(np.float32)
     vs = v_slab(bs)
-    kc = np.zeros((nb, hkv, bs, D), dtype=np.float32)
+    kc = np.zeros((nb, hkv, D // 4, bs, 4), dtype=np.float32)
     vc = np.zeros((nb, hkv, bs // vs, D, vs), dtype=np.float32)
     slots = np.array([0, 17, 33, 50, 63])
     flat = np.ascontiguousarray(qkv.reshape(5, -1))
@@ -92,7 +97,7 @@ def test_write_strided_token_rows(orc):
         hkv, D, bs, nb, 0)
     assert rc == 0
     for t, s in enumerate(slots):
-        assert np.array_equal(kc[s // bs, :, s % bs, :], qkv[t, 1])
+        assert np.array_equal(kc[s // bs, :, :, s % bs, :], qkv[t, 1].reshape(hkv, D // 4, 4))
         assert np.array_equal(vc[s // bs, :, (s % bs) // vs, :, s % vs], qkv[t, 2])
 
 
@@ -119,7 +124,7 @@ def test_copy_blocks_bytes_and_decode(orc):
 
 
 def test_copy_blocks_rejects_out_of_range(orc):
-    kp = np.zeros((3, 1, 4, 2), np.float32)
-    vp = np.zeros((3, 1, 1, 2, 4), np.float32)
+    kp = np.zeros((3, 1, 1, 4, 4), np.float32)
+    vp = np.zeros((3, 1, 1, 4, 4), np.float32)
     with pytest.raises(ValueError):
-        orc.copy_blocks(kp, vp, [[0, 3]], 1, 2, 4, "f32")
+        orc.copy_blocks(kp, vp, [[0, 3]], 1, 4, 4, "f32")

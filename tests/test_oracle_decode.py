@@ -25,7 +25,7 @@ MUTANTS = {
     4: "K and V swapped",
     5: "scale dropped",
     6: "off-by-one logical block",
-    7: "V read with the K layout",
+    7: "V read as plain token-major rows",
 }
 
 
@@ -58,7 +58,7 @@ def test_16bit_inputs_match_dense(orc, dtype):
     """16-bit storage: oracle == numpy dense attention on the widened values."""
     rng = np.random.default_rng(11)
     lens = [3, 16, 33]
-    q, Ks, Vs, t, nb, kp, vp = P.random_case(rng, lens, bs=16, D=16)
+    q, Ks, Vs, t, nb, kp, vp = P.random_case(rng, lens, bs=16, D=16, x=8)
     tdt = {"f16": torch.float16, "bf16": torch.bfloat16}[dtype]
 
     def bits(a):

@@ -11,7 +11,7 @@ dataset); no dataset item is reproduced.  Values are N(0, 1) drawn in fp32 and
 rounded to the storage dtype (round-to-nearest-even).
 
 Pool layout (shapes only; the index formula is documented in include/pa.h):
-  K: [num_blocks][Hkv][BS][D]
+  K: [num_blocks][Hkv][D/X][BS][X],  X = 16 / element size (16-byte pieces)
   V: [num_blocks][Hkv][BS/VS][D][VS],  VS = min(BS, 8)
 """
 from __future__ import annotations
@@ -29,8 +29,17 @@ def v_slab(block_size: int) -> int:
     return block_size if block_size < 8 else 8
 
 
-def k_pool_shape(num_blocks, num_kv_heads, block_size, head_dim):
-    return (num_blocks, num_kv_heads, block_size, head_dim)
+ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
+
+
+def k_piece(dtype: str) -> int:
+    """Dims per 16-byte K piece."""
+    return 16 // ELEM_BYTES[dtype]
+
+
+def k_pool_shape(num_blocks, num_kv_heads, block_size, head_dim, dtype):
+    x = k_piece(dtype)
+    return (num_blocks, num_kv_heads, head_dim // x, block_size, x)
 
 
 def v_pool_shape(num_blocks, num_kv_heads, block_size, head_dim):
@@ -162,7 +171,7 @@ def poison_unused(k_cache, v_cache, tables, lens, block_size):
             continue
         blk = int(tables[i, n - 1])
         for off in range(int(L) - (n - 1) * block_size, block_size):
-            k_cache[blk, :, off, :] = float("nan")
+            k_cache[blk, :, :, off, :] = float("nan")
             v_cache[blk, :, off // vs, :, off % vs] = float("nan")
 
 
@@ -198,7 +207,7 @@ def make_decode_case(spec: Spec, device="cpu", poison=True, lens=None, seed=None
         spec.block_size
     B = len(lens)
     q = randn((B, hq, D), spec.dtype, gen, device)
-    k = randn(k_pool_shape(nb, hkv, bs, D), spec.dtype, gen, device)
+    k = randn(k_pool_shape(nb, hkv, bs, D, spec.dtype), spec.dtype, gen, device)
     v = randn(v_pool_shape(nb, hkv, bs, D), spec.dtype, gen, device)
     if poison:
         poison_unused(k, v, tables, lens, bs)
