@@ -164,7 +164,17 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_mfma_kernel(DecodeArgs a
   // d = 32*s + 8*kb + e in both operands.
   constexpr int NC = D / 8;                     // 16-byte K pieces per token
   const int64_t pstride = (int64_t)4 * bs * 16;  // bytes from piece p to p + 4
-  auto issue_k = [&](const Cursor& cu, uint4 (&kr)[2][KN], uint4 (&qr)[KN], int& qitem) {
+  // Loads that carry no data -- K rows of masked tokens, V runs of masked
+  // k-groups, and whole issues past the worker's last group (`live` false)
+  // -- are pointed at bytes already in cache (the first row of the same
+  // tile, or the item's first q row), so they cost no HBM traffic while the
+  // number of loads, and so every wait count, stays fixed.
+  auto cached_addr = [&](const Cursor& cu) {
+    const int64_t head0 = (int64_t)cu.b * a.num_q_heads + (int64_t)cu.h * G;
+    return qbase + head0 * D * EB + ((lane * 16) & (D * EB - 1));
+  };
+  auto issue_k = [&](const Cursor& cu, uint4 (&kr)[2][KN], uint4 (&qr)[KN], int& qitem,
+                     bool live) {
     const int item = cu.item(H);
     if (qitem != item) {
       qitem = item;
@@ -182,23 +192,27 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_mfma_kernel(DecodeArgs a
     }
     tw.ensure(trow, a.max_blocks_per_seq, a.num_blocks, lb0, nb_grp, lane);
     const int64_t g = cu.h;
+    const int nv = cu.L - tok;  // valid tokens of the group (>= 1)
+    const char* cached = cached_addr(cu);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int t = tok + 16 * j + n;
+      const bool tile = live && 16 * j < nv;  // the tile holds a valid token
+      const int t = tok + 16 * j + (16 * j + n < nv ? n : 0);
       const int lb = t / bs;
       int64_t phys = tw.get(lb0);
       for (int q = 1; q < nb_grp; ++q)
         if (lb == lb0 + q) phys = tw.get(lb0 + q);
       const char* kp = kbase + (((phys * hkv + g) * NC + kb) * bs + (t - lb * bs)) * 16;
 #pragma unroll
-      for (int i = 0; i < KN; ++i) kr[j][i] = ld16nt(kp + i * pstride);
+      for (int i = 0; i < KN; ++i) kr[j][i] = ld16nt(tile ? kp + i * pstride : cached);
     }
   };
   // The V token run of k-group kb (8 tokens of one slab row per d tile).  Its
   // group's K was issued earlier, so the table window already covers it.
-  auto issue_v = [&](const Cursor& cu, uint4 (&vr)[MT]) {
+  auto issue_v = [&](const Cursor& cu, uint4 (&vr)[MT], bool live) {
     const int tok = cu.k * kGroup;
     const int lb0 = tok / bs;
+    const bool run = live && kb * 8 < cu.L - tok;  // this k-group's 8 tokens hold data
     const int t = tok + kb * 8;
     const int lb = t / bs;
     int64_t phys = tw.get(lb0);
@@ -207,8 +221,10 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_mfma_kernel(DecodeArgs a
     const int off = t - lb * bs;
     const char* vp =
         vbase + ((((phys * hkv + cu.h) * (bs / VS) + off / VS) * D + n) * VS) * EB;
+    const char* cached = cached_addr(cu);
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) vr[mt] = ld16nt(vp + (int64_t)mt * 16 * VS * EB);
+    for (int mt = 0; mt < MT; ++mt)
+      vr[mt] = ld16nt(run ? vp + (int64_t)mt * 16 * VS * EB : cached);
   };
 
   float m_run = -INFINITY, l_lane = 0.f;
@@ -346,15 +362,14 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_mfma_kernel(DecodeArgs a
     // Pipeline, per group j: qk(j) | issue V(j+1) | pv(j) | issue K(j+2).
     // Each load is issued a full group ahead of its use, yet only three of
     // the four K/V register sets are live at any time.  Issues past the
-    // worker's last group repeat that group's (cached) addresses, keeping the
-    // waits static.
+    // worker's last group read cached bytes instead, keeping the waits static.
     uint4 kA[2][KN], kB[2][KN], vA[MT], vB[MT], qA[KN], qB[KN];
     int qia = -1, qib = -1;
     Cursor c1 = c0;
     next(c1, 1);
-    issue_k(c0, kA, qA, qia);
-    issue_v(c0, vA);
-    issue_k(c1, kB, qB, qib);
+    issue_k(c0, kA, qA, qia, true);
+    issue_v(c0, vA, true);
+    issue_k(c1, kB, qB, qib, 1 < count);
     int j = 0;
     for (;;) {
       Cursor c2 = c1;
@@ -363,9 +378,9 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_mfma_kernel(DecodeArgs a
         uint4 pb;
         int nv;
         qk(c0, kA, qA, j, pb, nv);
-        issue_v(c1, vB);
+        issue_v(c1, vB, j + 1 < count);
         pv(c0, vA, pb, nv, j);
-        issue_k(c2, kA, qA, qia);
+        issue_k(c2, kA, qA, qia, j + 2 < count);
       }
       if (++j >= count) break;
       c0 = c1;
@@ -376,9 +391,9 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_mfma_kernel(DecodeArgs a
         uint4 pb;
         int nv;
         qk(c0, kB, qB, j, pb, nv);
-        issue_v(c1, vA);
+        issue_v(c1, vA, j + 1 < count);
         pv(c0, vB, pb, nv, j);
-        issue_k(c2, kB, qB, qib);
+        issue_k(c2, kB, qB, qib, j + 2 < count);
       }
       if (++j >= count) break;
       c0 = c1;
@@ -391,12 +406,12 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_mfma_kernel(DecodeArgs a
     int qia = -1, qib = -1;
     Cursor c1 = c0;
     next(c1, 1);
-    issue_k(c0, kA, qA, qia);
-    issue_v(c0, vA);
+    issue_k(c0, kA, qA, qia, true);
+    issue_v(c0, vA, true);
     int j = 0;
     for (;;) {
-      issue_k(c1, kB, qB, qib);
-      issue_v(c1, vB);
+      issue_k(c1, kB, qB, qib, j + 1 < count);
+      issue_v(c1, vB, j + 1 < count);
       {
         uint4 pb;
         int nv;
@@ -406,8 +421,8 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_mfma_kernel(DecodeArgs a
       if (++j >= count) break;
       c0 = c1;
       next(c1, j + 1);
-      issue_k(c1, kA, qA, qia);
-      issue_v(c1, vA);
+      issue_k(c1, kA, qA, qia, j + 1 < count);
+      issue_v(c1, vA, j + 1 < count);
       {
         uint4 pb;
         int nv;

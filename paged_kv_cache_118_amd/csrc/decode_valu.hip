@@ -253,8 +253,14 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
   // block (tok + 8j) / BS (BS is 8 or a multiple of 16).  The q slice of the
   // step's item travels with the step's K/V registers (reloaded only when the
   // buffer's item changes).
+  // Loads that carry no data -- K rows of masked tokens, a masked second V
+  // slab, and the whole issue when `live` is false (the pipeline's issue past
+  // a worker's last step) -- are pointed at bytes this wavefront already has
+  // in cache (token 0 of the same instruction, or the item's q row), so they
+  // cost no HBM traffic while the number of loads, and so every wait count,
+  // stays fixed.
   auto issue = [&](const Cursor& cu, uint4 (&kr)[NK], uint4 (&vr)[NK], uint4 (&qr)[NK],
-                   int& qitem) {
+                   int& qitem, bool live) {
     const int item = cu.item(H);
     if (qitem != item) {
       qitem = item;
@@ -274,19 +280,23 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
     const int64_t ph0 = tw.get(lb0), ph1 = tw.get(lb1);
     const int off0 = tok - lb0 * bs, off1 = tok + 8 - lb1 * bs;  // multiples of 8
     const int64_t g = cu.h / group;
+    const int nv = cu.L - tok;  // valid tokens from tok on (>= 1)
+    const char* cached = qbase + (int64_t)item * D * EB + ((lane * 16) & (D * EB - 1));
     {
       // 16-byte K piece c + 4i of token tq: for each i the wavefront reads
       // pieces 4i .. 4i+3 of 16 consecutive offsets, whole 128-byte lines.
-      const bool hi = tq >= 8;
+      const bool kt = tq < nv;
+      const bool hi = kt && tq >= 8;
       const int64_t phys = hi ? ph1 : ph0;
-      const int off = (hi ? off1 : off0) + (tq & 7);
+      const int off = (hi ? off1 : off0) + (kt ? (tq & 7) : 0);
       const char* kp = kbase + (((phys * hkv + g) * (4 * NK) + c) * bs + off) * 16;  // 4*NK pieces per row
       const int64_t pstride = (int64_t)4 * bs * 16;  // 4 pieces further
 #pragma unroll
-      for (int i = 0; i < NK; ++i) kr[i] = ld16nt(kp + i * pstride);
+      for (int i = 0; i < NK; ++i) kr[i] = ld16nt(live ? kp + i * pstride : cached);
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
+      const bool vlive = live && (j == 0 || nv > 8);
       const int64_t phys = j ? ph1 : ph0;
       const int off = j ? off1 : off0;
       const char* vp = vbase + (((phys * hkv + g) * (bs / 8) + off / 8) * D + lane) * (8 * EB);
@@ -294,7 +304,8 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
       for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int u = 0; u < NVR; ++u)
-          vr[(j * R + r) * NVR + u] = ld16nt(vp + (int64_t)r * 64 * 8 * EB + 16 * u);
+          vr[(j * R + r) * NVR + u] =
+              ld16nt(vlive ? vp + (int64_t)r * 64 * 8 * EB + 16 * u : cached);
     }
   };
 
@@ -369,10 +380,10 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
     advance(c1, s_pre, s_len, H, kStep);
     uniform(c1);
   }
-  issue(c0, ka, va, qa, qia);
+  issue(c0, ka, va, qa, qia, true);
   int j = 0;
   for (;;) {
-    issue(c1, kb2, vb2, qb, qib);
+    issue(c1, kb2, vb2, qb, qib, j + 1 < count);
     compute(c0, ka, va, qa, j);
     if (++j >= count) break;
     c0 = c1;
@@ -380,7 +391,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
       advance(c1, s_pre, s_len, H, kStep);
       uniform(c1);
     }
-    issue(c1, ka, va, qa, qia);
+    issue(c1, ka, va, qa, qia, j + 1 < count);
     compute(c0, kb2, vb2, qb, j);
     if (++j >= count) break;
     c0 = c1;
