@@ -51,7 +51,78 @@ def parse():
                     help="only run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--stream-probe", action="store_true",
                     help="only measure plain device read / copy bandwidth (context for peak)")
+    ap.add_argument("--counters-summary", nargs=4, metavar=("FETCH", "WRITE", "CFETCH", "CWRITE"),
+                    help="only summarise four rocprofv3 --pmc output folders (FETCH_SIZE and "
+                         "WRITE_SIZE of this workload, then of --calib-copy-mb 1024) into the "
+                         "traffic record stored under profiles/")
     return ap.parse_args()
+
+
+# ------------------------------------------------------ HBM traffic record --
+# The decode kernels' HBM bytes come from two rocprofv3 --pmc passes
+# (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each scaled by what the same
+# counter reads for a plain 1 GiB device copy.  The record is stored under
+# profiles/ with a hash of the kernel sources; a source change voids it.
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ("decode_valu.hip", "decode_mfma.hip", "decode_merge.hip", "decode_split.h",
+                  "pa_internal.h", "capi.cpp")
+RECORD_TAG = "traffic-record:"
+
+
+def kernel_sources_sha() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "paged_kv_cache_118_amd", "csrc", name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def _pmc_medians(folder: str) -> dict:
+    """Median counter value per pa kernel (and the copy kernels) of one run."""
+    import csv
+    import glob
+    import re
+    vals = {}
+    for path in glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                n = r["Kernel_Name"]
+                m = re.search(r"pa::\(anonymous namespace\)::(\w+)", n)
+                key = m.group(1) if m else ("copy" if "copy" in n.lower() else None)
+                if key:
+                    vals.setdefault(key, []).append(float(r["Counter_Value"]))
+    return {k: float(np.median(v)) for k, v in vals.items()}
+
+
+def counters_summary(args) -> dict:
+    fetch, write, cfetch, cwrite = (_pmc_medians(d) for d in args.counters_summary)
+    copy_kib = 1024 * 1024  # --calib-copy-mb 1024: 1 GiB read and 1 GiB written
+    f_scale = copy_kib / cfetch["copy"]
+    w_scale = copy_kib / cwrite["copy"]
+    kernels = [k for k in fetch if k.startswith("decode_")]
+    per = {k: {"fetch_bytes": round(fetch[k] * f_scale * 1024),
+               "write_bytes": round(write.get(k, 0.0) * w_scale * 1024)} for k in kernels}
+    return {"workload": args.workload, "sources_sha256": kernel_sources_sha(),
+            "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+            "kernels": per,
+            "bytes_per_call": sum(v["fetch_bytes"] + v["write_bytes"] for v in per.values())}
+
+
+def stored_traffic(workload: str):
+    """HBM bytes per pa_decode call from the stored record, or None when no
+    record exists for the workload or the kernel sources changed since."""
+    import glob
+    sha = kernel_sources_sha()
+    for path in sorted(glob.glob(os.path.join(PROFILES, "*.md"))):
+        with open(path) as f:
+            for line in f:
+                line = line.strip().strip("`")
+                if line.startswith(RECORD_TAG):
+                    rec = json.loads(line[len(RECORD_TAG):])
+                    if rec.get("workload") == workload and rec.get("sources_sha256") == sha:
+                        return rec["bytes_per_call"]
+    return None
 
 
 # ----------------------------------------------------------------- workloads --
@@ -217,7 +288,7 @@ class Workload:
         self.decode_alg_bytes = (self.kv_read_bytes + 2 * q_bytes + self.tables.nbytes +
                                  self.lens.nbytes)
         self.decode_seqs = B
-        self.roofline_kernel = "pa_decode"
+        self.roofline_kernel = "pa_decode call (decode kernel + merge kernel)"
         per_step = self.kv_read_bytes + 2 * T * self._tok_bytes()
         self.replicas = self.args.replicas or max(1, int(math.ceil(2e9 / per_step)))
         gen = W.make_generator(sp.seed, dev)
@@ -349,6 +420,9 @@ def build_workload(args, dev):
 
 def main():
     args = parse()
+    if args.counters_summary:
+        print(RECORD_TAG + " " + json.dumps(counters_summary(args)))
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; use --gpus 1"}))
         sys.exit(2)
@@ -420,7 +494,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": stored_traffic(args.workload),
             "kernel": wl.roofline_kernel,
         },
         "host_alloc_us_per_step": wl.host_alloc_us,
