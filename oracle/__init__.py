@@ -19,8 +19,9 @@ What each function follows (web pages on PagedAttention):
   and mutation tests.
 * ``reshape_and_cache`` -- slot = physical block * block_size + offset, the
   flat slot numbering of the kernel pseudocode on vkads.cloudxian.cn "vLLM
-  PagedAttention源码：KV Cache".  Pinned by the D = 1, one-head special case
-  (the pool equals the slot array) and by write-then-decode round trips
+  PagedAttention源码：KV Cache".  Pinned by the one-head, one-piece special
+  case (head_dim 4 in fp32: the K pool, and the V pool with its slabs turned
+  back into rows, are [slot][D] tables) and by write-then-decode round trips
   against numpy dense attention.
 * ``copy_blocks`` -- copy-on-write of whole blocks, section 二 "共享与写时复制"
   of the wq-win page.  Pinned by byte identity of the copied block, untouched
