@@ -1,0 +1,90 @@
+"""Parity at the benchmark's full sizes and launch configuration.
+
+Each case builds the workload exactly as ``bench.py`` does (same specs, seeds,
+allocator-driven tables, partition choice), runs one benchmark step on the GPU
+(copy-on-write copies, cache write, decode), then checks sampled results that
+the oracle can compute one by one:
+
+* decode rows of a sample of sequences (first, longest, shortest and random
+  ones, every q head) against the fp64 oracle on those sequences' blocks;
+* written slots bit for bit against the new token rows;
+* copy-on-write destinations bit for bit against their sources (all offsets
+  except the one the step then wrote).
+"""
+import argparse
+
+import numpy as np
+import pytest
+import torch
+
+import bench
+import workloads as W
+from tests.gpu_util import DEV, TOL, log, max_err, oracle_decode
+
+pytestmark = pytest.mark.gpu
+
+CASES = [("opt13b_decode", None), ("gqa_long", None), ("llama13b_prefix_share", None),
+         ("opt66b_sweep", 8), ("opt66b_sweep", 16), ("opt66b_sweep", 32), ("opt66b_sweep", 128)]
+
+
+def _workload(name, bs):
+    args = argparse.Namespace(workload=name, block_size=bs, partition=None, replicas=1,
+                              no_cpu_baseline=True, cpu_seconds=0.0)
+    return bench.Workload(args, DEV)
+
+
+def _sample(lens, rng, k=4):
+    B = len(lens)
+    picks = {0, int(np.argmax(lens)), int(np.argmin(lens))}
+    picks.update(int(x) for x in rng.choice(B, size=min(k, B), replace=False))
+    return sorted(picks)
+
+
+def _k_row(k_pool, blk, off):
+    hkv = k_pool.shape[1]
+    return k_pool[blk, :, :, off, :].reshape(hkv, -1)
+
+
+def _v_row(v_pool, blk, off, vs):
+    return v_pool[blk, :, off // vs, :, off % vs]
+
+
+@pytest.mark.parametrize("name,bs", CASES)
+def test_full_size_step_parity(name, bs):
+    log(f"[full size] {name} block_size={bs}")
+    wl = _workload(name, bs)
+    sp = wl.spec
+    rng = np.random.default_rng(7)
+    torch.cuda.synchronize()
+    wl.step(0)
+    torch.cuda.synchronize()
+    vs = W.v_slab(sp.block_size)
+
+    # cache write: sampled new tokens
+    T = len(wl.slots)
+    for t in rng.choice(T, size=min(64, T), replace=False):
+        slot = int(wl.slots[t])
+        blk, off = slot // sp.block_size, slot % sp.block_size
+        assert torch.equal(_k_row(wl.k[0], blk, off), wl.k_new[t]), f"K slot {slot}"
+        assert torch.equal(_v_row(wl.v[0], blk, off, vs), wl.v_new[t]), f"V slot {slot}"
+
+    # copy-on-write: destinations equal their sources except the written slot
+    pairs = getattr(wl, "pairs", None)
+    if pairs is not None and len(pairs):
+        written = {}
+        for s in wl.slots:
+            written.setdefault(int(s) // sp.block_size, set()).add(int(s) % sp.block_size)
+        for p in rng.choice(len(pairs), size=min(32, len(pairs)), replace=False):
+            src, dst = (int(x) for x in pairs[p])
+            keep = [o for o in range(sp.block_size) if o not in written.get(dst, ())]
+            for o in keep:
+                assert torch.equal(_k_row(wl.k[0], dst, o), _k_row(wl.k[0], src, o))
+                assert torch.equal(_v_row(wl.v[0], dst, o, vs), _v_row(wl.v[0], src, o, vs))
+
+    # decode: sampled sequences against the oracle
+    seqs = _sample(wl.lens, rng)
+    case = W.DecodeCase(sp, wl.lens, wl.tables, wl.nb, wl.q[0], wl.k[0], wl.v[0])
+    want = oracle_decode(case, seqs=seqs)
+    err = max_err(wl.out, want, seqs=seqs)
+    log(f"  sequences {seqs}: max abs err {err:.3e} (tol {TOL[sp.dtype]})")
+    assert err <= TOL[sp.dtype]
