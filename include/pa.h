@@ -93,16 +93,23 @@ const char* pa_strerror(pa_status s);
  *               L <= max_context_len and L <= max_blocks_per_seq * BS;
  *               positions beyond either bound are ignored.
  *  scale        score scale (1/sqrt(head_dim) for standard attention)
- *  partition_size  how the work is divided among wavefronts:
+ *  partition_size  how the context is split:
  *               0  = token-balanced: all (sequence, head) items are laid end
- *                    to end and every wavefront of one full-chip round takes
- *                    an equal share of the tokens, whatever the lengths;
- *               -1 = one wavefront per (sequence, head) item, nothing split;
- *               >0 = each wavefront takes that many tokens of the stream (a
- *                    multiple of 256).
- *               An item shared by several wavefronts is merged exactly by a
- *               second kernel from fp32 (max, sum, unnormalised output)
- *               partials; results agree across modes within rounding.
+ *                    to end and each of a fixed number of wavefronts per CU
+ *                    (all resident at once) takes an equal share of the
+ *                    tokens, whatever the lengths; an
+ *                    item shared by several wavefronts yields one fp32
+ *                    (max, sum, unnormalised output) partial per wavefront;
+ *               >0 = the same balanced shares, and each sequence's
+ *                    context is cut into partitions of this many tokens (a
+ *                    multiple of 256) from its start: an item longer than
+ *                    one partition yields one partial per partition, or per
+ *                    (partition, wavefront) piece where a partition
+ *                    straddles two shares;
+ *               -1 = one wavefront per (sequence, head) item, nothing split.
+ *               The partials of an item are reduced by a second kernel
+ *               (rescaled to their common maximum: one denominator, as in the
+ *               Z / o equations); results agree across modes within rounding.
  *  workspace    device scratch of at least pa_decode_workspace_bytes(...)
  *               bytes (may be NULL when that size is 0); contents need no
  *               initialisation and are clobbered.  Calls that run
@@ -126,7 +133,8 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
                                  int32_t partition_size, pa_dtype dtype);
 
 /* The split pa_decode uses for these arguments: -1 = one wavefront per
- * item, 0 = token-balanced, > 0 = fixed tokens per wavefront. */
+ * item, 0 = token-balanced, > 0 = token-balanced with partials cut at
+ * partitions of that many tokens. */
 int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t block_size, int32_t max_context_len,
                                  int32_t partition_size, pa_dtype dtype);

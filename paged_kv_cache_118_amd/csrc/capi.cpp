@@ -21,21 +21,24 @@ constexpr int kPartGranule = 256;  // fixed chunks are a multiple of this many t
 constexpr int kMfmaMinGroup = 4;
 // The token-balanced split keeps per-sequence prefix sums in LDS.
 constexpr int kMaxSplitSeqs = 8192;
-// Resident wavefronts per CU of each kernel (its occupancy): one round of
-// workers fills the chip.
-constexpr int kValuWavesPerCu = 16;
-constexpr int kMfmaWavesPerCu = 8;
+// Workers per CU: the decode kernel's occupancy (one round of workers fills
+// the chip), capped for the VALU kernel at kValuWorkersPerCu, or the tuning
+// override PA_VALU_WAVES_PER_CU / PA_MFMA_WAVES_PER_CU.  Every worker
+// boundary inside an item costs one more fp32 partial written and merged, so
+// fewer, longer shares pay off once the CU is kept busy: 8 VALU workers per
+// CU measured about 1% faster than 16 on the OPT-13B-shaped workload.
+constexpr int kValuWorkersPerCu = 8;
 
-// Tuning override of the workers per CU (PA_VALU_WAVES_PER_CU,
-// PA_MFMA_WAVES_PER_CU); the default is the kernel's occupancy.
-int waves_per_cu(bool mfma) {
-  static int v[2] = {-1, -1};
-  int& x = v[mfma ? 1 : 0];
-  if (x < 0) {
-    const char* e = std::getenv(mfma ? "PA_MFMA_WAVES_PER_CU" : "PA_VALU_WAVES_PER_CU");
-    const int def = mfma ? kMfmaWavesPerCu : kValuWavesPerCu;
-    x = (e && std::atoi(e) > 0 && std::atoi(e) <= 64) ? std::atoi(e) : def;
-  }
+int waves_per_cu(bool mfma, pa_dtype dt, int head_dim) {
+  const char* e = std::getenv(mfma ? "PA_MFMA_WAVES_PER_CU" : "PA_VALU_WAVES_PER_CU");
+  if (e && std::atoi(e) > 0 && std::atoi(e) <= 64) return std::atoi(e);
+  static int cache[2][3][5] = {};
+  int dsel = head_dim == 64 ? 0 : head_dim == 128 ? 1 : head_dim == 256 ? 2 : 3;
+  if (dsel > 2) dsel = 3;
+  int& x = cache[mfma ? 1 : 0][(int)dt][dsel];
+  if (x == 0)
+    x = mfma ? decode_mfma_waves_per_cu(dt, head_dim)
+             : std::min(kValuWorkersPerCu, decode_valu_waves_per_cu(dt, head_dim));
   return x;
 }
 
@@ -83,10 +86,10 @@ struct Plan {
   int step;         // tokens per worker step
   int items_per_seq;
   int rows_per_item;
-  int chunk_steps;  // split 1: fixed steps per worker, 0 = balanced
+  int part_steps;   // split 1: steps per partition, 0 = partials per worker segment only
   int num_workers;
   size_t ws_bytes;
-  size_t m_off, l_off, o_off, desc_off;
+  size_t pre_off, ppre_off;
 };
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -100,28 +103,23 @@ Plan make_plan(int num_seqs, int hq, int hkv, int head_dim, int block_size, int 
   p.items_per_seq = p.path == Path::kMfma ? hkv : hq;
   p.rows_per_item = p.path == Path::kMfma ? group : 1;
   const int64_t items = (int64_t)num_seqs * p.items_per_seq;
-  const int64_t max_steps = items * ((int64_t)(len_cap + p.step - 1) / p.step);
+  const int64_t item_steps = ((int64_t)len_cap + p.step - 1) / p.step;
   p.split = (p.path != Path::kGeneric && partition_size >= 0 && len_cap > 0 &&
-             num_seqs <= kMaxSplitSeqs && max_steps < (int64_t)1 << 30)
+             num_seqs <= kMaxSplitSeqs && items * item_steps < (int64_t)1 << 30)
                 ? 1
                 : 0;
   if (!p.split) {
     p.num_workers = (int)items;
     return p;
   }
-  if (partition_size > 0) {
-    p.chunk_steps = std::max(1, partition_size / p.step);
-    p.num_workers = (int)((max_steps + p.chunk_steps - 1) / p.chunk_steps);
-  } else {
-    p.chunk_steps = 0;
-    p.num_workers = device_cus() * waves_per_cu(p.path == Path::kMfma);
-  }
-  const size_t rows = (size_t)(items + p.num_workers) * p.rows_per_item;
-  p.m_off = 0;
-  p.l_off = round_up(rows * 4, 256);
-  p.o_off = p.l_off + round_up(rows * 4, 256);
-  p.desc_off = p.o_off + round_up(rows * head_dim * 4, 256);
-  p.ws_bytes = p.desc_off + round_up((size_t)items * 8, 256);
+  p.part_steps = partition_size > 0 ? std::max(1, partition_size / p.step) : 0;
+  p.num_workers = device_cus() * waves_per_cu(p.path == Path::kMfma, dt, head_dim);
+  const int64_t partitions =
+      p.part_steps ? items * ((item_steps + p.part_steps - 1) / p.part_steps) : items;
+  const size_t slots = (size_t)(partitions + p.num_workers);
+  p.pre_off = round_up(slots * part_record(p.rows_per_item, head_dim) * 4, 256);
+  p.ppre_off = p.pre_off + round_up(((size_t)num_seqs + 1) * 4, 256);
+  p.ws_bytes = p.ppre_off + round_up(((size_t)num_seqs + 1) * 4, 256);
   return p;
 }
 
@@ -160,7 +158,7 @@ int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t 
   const Plan p = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                            max_context_len, partition_size, dtype);
   if (!p.split) return -1;
-  return p.chunk_steps * p.step;
+  return p.part_steps * p.step;
 }
 
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
@@ -223,16 +221,15 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   a.len_cap = len_cap;
   a.num_blocks = num_blocks;
   a.split = p.split;
-  a.chunk_steps = p.chunk_steps;
+  a.part_steps = p.part_steps;
   a.num_workers = p.num_workers;
   if (p.split) {
     if (p.ws_bytes > sized.ws_bytes) return PA_EINVAL;  // cannot happen: len_cap <= max
     if (!workspace || workspace_bytes < p.ws_bytes || !aligned16(workspace)) return PA_EINVAL;
     char* base = static_cast<char*>(workspace);
-    a.ws_m = reinterpret_cast<float*>(base + p.m_off);
-    a.ws_l = reinterpret_cast<float*>(base + p.l_off);
-    a.ws_o = reinterpret_cast<float*>(base + p.o_off);
-    a.ws_desc = reinterpret_cast<int2*>(base + p.desc_off);
+    a.ws_part = reinterpret_cast<float*>(base);
+    a.ws_pre = reinterpret_cast<int32_t*>(base + p.pre_off);
+    a.ws_ppre = reinterpret_cast<int32_t*>(base + p.ppre_off);
   }
 
   if (validate_enabled()) {
@@ -257,7 +254,7 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
     case Path::kGeneric: e = launch_decode_generic(a, dtype, s); break;
   }
   if (e != hipSuccess) return PA_EHIP;
-  if (p.split) e = launch_decode_merge(a, dtype, p.items_per_seq, s);
+  if (p.split) e = launch_decode_merge(a, dtype, p.items_per_seq, p.step, s);
   return hip_status(e);
 }
 

@@ -1,12 +1,15 @@
-// Merge of items that several workers split between them (decode_split.h).
+// Merge of the partials of items that the decode kernels split (decode_split.h).
 //
-// Each worker leaves, per q row of the item, fp32 (m_w, l_w, o_w): its running
-// max (base-2 domain), the sum of exp2(s - m_w) and the unnormalised output.
-// Because every block shares one softmax denominator (wq-win.github.io "079 |
-// vLLM 与 PagedAttention", section 二, the Z / o equations), the exact result is
-// recovered by rescaling to the global max M:
-//   out = sum_w 2^(m_w - M) o_w  /  sum_w 2^(m_w - M) l_w.
-// This kernel also writes the zero rows of empty sequences.
+// Each (partition, worker) piece of a split item left fp32 (m, l, o) per q row
+// of the item: its running max (base-2 domain), the sum of exp2(s - m) and the
+// unnormalised output.  Because every block shares one softmax denominator
+// (wq-win.github.io "079 | vLLM 与 PagedAttention", section 二, the Z / o
+// equations), the exact row is recovered by rescaling to the global max M:
+//   out = sum_i 2^(m_i - M) o_i  /  sum_i 2^(m_i - M) l_i.
+// The pieces an item has follow from the split arithmetic alone (the step
+// prefixes the decode kernel exported, the worker count, the partition size),
+// so nothing but the partials themselves has to be communicated.  This kernel
+// also writes the zero rows of empty sequences.
 #include <math.h>
 
 #include "decode_split.h"
@@ -16,7 +19,6 @@ namespace pa {
 
 namespace {
 
-
 template <typename TT>
 __device__ __forceinline__ void store_out(void* out, int64_t idx, float x) {
   if constexpr (TT::bytes == 4)
@@ -25,28 +27,27 @@ __device__ __forceinline__ void store_out(void* out, int64_t idx, float x) {
     reinterpret_cast<uint16_t*>(out)[idx] = to_bits(TT{}, x);
 }
 
-// One workgroup per item, one thread per output (q row r, dim d); rows x
-// head_dim <= 2048, so a thread takes at most two outputs.  The item's length
-// and descriptor (first worker F, number of workers cnt -- written by worker
-// F) are read together: an empty item gets zero rows, an item one worker
-// covered is already done.  Otherwise each thread loads (m, l, o) of up to
-// kBatch partials back to back and folds them in with an online rescale, so a
-// merge costs one memory round trip per kBatch partials.
+// Partials folded per memory round trip: each thread loads (m, l, o) of up to
+// kBatch pieces back to back, then folds them in with one rescale.
 constexpr int kBatch = 16;
 
-__device__ __forceinline__ void merge_output(const DecodeArgs& a, int64_t slot0, int cnt, int R,
-                                             int r, int d, float& out) {
+// slot_of(k) = slot of the item's k-th piece, k < K.
+template <typename SlotOf>
+__device__ __forceinline__ float merge_output(const DecodeArgs& a, SlotOf slot_of, int K, int R,
+                                              int r, int d) {
   const int D = a.head_dim;
+  const int od = ((d >> 4) * 4 + ((d & 15) >> 2)) * R * 4 + r * 4 + (d & 3);  // within a record
+  const int RS = part_record(R, D);
   float M = -INFINITY, Lt = 0.f, acc = 0.f;
-  for (int w0 = 0; w0 < cnt; w0 += kBatch) {
+  for (int k0 = 0; k0 < K; k0 += kBatch) {
     float m[kBatch], l[kBatch], o[kBatch];
 #pragma unroll
     for (int w = 0; w < kBatch; ++w) {
-      const bool ok = w0 + w < cnt;
-      const int64_t row = (slot0 + w0 + (ok ? w : 0)) * R + r;
-      m[w] = ok ? a.ws_m[row] : -INFINITY;
-      l[w] = ok ? a.ws_l[row] : 0.f;
-      o[w] = ok ? a.ws_o[row * D + d] : 0.f;
+      const bool ok = k0 + w < K;
+      const float* rec = a.ws_part + (int64_t)slot_of(ok ? k0 + w : k0) * RS;
+      m[w] = ok ? rec[R * D + r] : -INFINITY;
+      l[w] = ok ? rec[R * D + 16 + r] : 0.f;
+      o[w] = ok ? rec[od] : 0.f;
     }
     float Mn = M;
 #pragma unroll
@@ -62,52 +63,100 @@ __device__ __forceinline__ void merge_output(const DecodeArgs& a, int64_t slot0,
     }
     M = Mn;
   }
-  out = acc / Lt;
+  return acc / Lt;
 }
 
+// One workgroup per item (b, h), one thread per output (q row r, dim d).
+// LDS: st[0..nw] = first stream step of each of the item's workers (clipped to
+// the item), then the item's slot list.
 template <typename TT>
-__global__ __launch_bounds__(1024) void decode_merge_kernel(DecodeArgs a, int H,
-                                                           int rows_per_item) {
-  const int D = a.head_dim;
-  const int t = threadIdx.x;
+__global__ __launch_bounds__(1024) void decode_merge_kernel(DecodeArgs a, int H, int R) {
+  extern __shared__ int smem[];
+  __shared__ int s_count;
+  const int D = a.head_dim, B = a.num_seqs, C = a.part_steps;
   const int item = blockIdx.x;
   const int b = item / H, h = item - b * H;
-  const int L = clamp_len(a.context_lens[b], a.len_cap);
-  const int2 desc = a.ws_desc[item];
-  const int64_t orow0 = ((int64_t)b * a.num_q_heads + (int64_t)h * rows_per_item) * D;
-  const int R = rows_per_item, total = R * D;
-  for (int i = t; i < total; i += blockDim.x) {
-    float x = 0.f;
-    if (L > 0) {
-      if (desc.y <= 1) continue;  // one worker saw the whole item and wrote it
-      const int r = i / D, d = i - r * D;
-      merge_output(a, (int64_t)item + desc.x, desc.y, R, r, d, x);
+  const int* pre = a.ws_pre;
+  const int n = (pre[b + 1] - pre[b]) / H;
+  const int64_t orow0 = ((int64_t)b * a.num_q_heads + (int64_t)h * R) * D;
+  const int total = R * D;
+  if (n == 0) {  // empty sequence: zero rows
+    for (int t = threadIdx.x; t < total; t += blockDim.x) store_out<TT>(a.out, orow0 + t, 0.f);
+    return;
+  }
+  const Split sp = make_split(a.num_workers, pre[B]);
+  const int64_t S = pre[b] + (int64_t)h * n, E = S + n;
+  const int F = sp.worker_of(S), Lw = sp.worker_of(E - 1);
+  const int np = C > 0 ? (n + C - 1) / C : 1;
+  if (F == Lw && np == 1) return;  // one piece: the decode kernel wrote the row
+  if (C == 0) {  // one piece per worker: slots item + F .. item + Lw
+    const int base = item + F;
+    for (int t = threadIdx.x; t < total; t += blockDim.x) {
+      const int r = t / D, d = t - r * D;
+      store_out<TT>(a.out, orow0 + t,
+                    merge_output(a, [base](int k) { return base + k; }, Lw - F + 1, R, r, d));
     }
-    store_out<TT>(a.out, orow0 + i, x);
+    return;
+  }
+  const int pg0 = a.ws_ppre[b] + h * np;
+  const int nw = Lw - F + 1;
+  int* st = smem;
+  int* slots = smem + nw + 1;
+  for (int i = threadIdx.x; i <= nw; i += blockDim.x)
+    st[i] = (int)(i == 0 ? S : (i == nw ? E : sp.start(F + i)));
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    // Walk the pieces in stream order: piece (p, i) ends at the earlier of
+    // partition p's end and worker F+i's end; slot pg0 + p + F + i.
+    int p = 0, i = 0, k = 0;
+    for (;;) {
+      slots[k++] = pg0 + p + F + i;
+      const int64_t pend = C > 0 ? (S + (int64_t)(p + 1) * C < E ? S + (int64_t)(p + 1) * C : E)
+                                 : E;
+      const int64_t wend = st[i + 1];
+      if (pend >= E && wend >= E) break;
+      if (pend <= wend) ++p;
+      if (wend <= pend) ++i;
+    }
+    s_count = k;
+  }
+  __syncthreads();
+  const int K = s_count;
+  for (int t = threadIdx.x; t < total; t += blockDim.x) {
+    const int r = t / D, d = t - r * D;
+    store_out<TT>(a.out, orow0 + t,
+                  merge_output(a, [slots](int k) { return slots[k]; }, K, R, r, d));
   }
 }
 
 }  // namespace
 
-hipError_t launch_decode_merge(const DecodeArgs& a, pa_dtype dt, int items_per_seq,
-                              hipStream_t s) {
+hipError_t launch_decode_merge(const DecodeArgs& a, pa_dtype dt, int items_per_seq, int step,
+                               hipStream_t s) {
   if (a.num_seqs == 0 || !a.split) return hipSuccess;
-  const int rpi = a.num_q_heads / items_per_seq;
-  const int outputs = rpi * a.head_dim;
+  const int R = a.num_q_heads / items_per_seq;
+  const int outputs = R * a.head_dim;
   const int threads = outputs >= 1024 ? 1024 : (outputs + 63) / 64 * 64;
+  // workers of one item: at most item_steps / kMinChunk + 2; pieces: that
+  // plus the item's partitions
+  const int item_steps = (a.len_cap + step - 1) / step;
+  int nw_max = item_steps / kMinChunk + 2;
+  if (nw_max > a.num_workers + 1) nw_max = a.num_workers + 1;
+  const int np_max = a.part_steps > 0 ? (item_steps + a.part_steps - 1) / a.part_steps : 1;
+  const size_t lds = sizeof(int) * (size_t)(2 * nw_max + np_max + 2);
   dim3 grid(a.num_seqs * items_per_seq);
   switch (dt) {
     case PA_F32:
-      hipLaunchKernelGGL(decode_merge_kernel<F32>, grid, dim3(threads), 0, s, a, items_per_seq,
-                         rpi);
+      hipLaunchKernelGGL(decode_merge_kernel<F32>, grid, dim3(threads), lds, s, a, items_per_seq,
+                         R);
       break;
     case PA_F16:
-      hipLaunchKernelGGL(decode_merge_kernel<F16>, grid, dim3(threads), 0, s, a, items_per_seq,
-                         rpi);
+      hipLaunchKernelGGL(decode_merge_kernel<F16>, grid, dim3(threads), lds, s, a, items_per_seq,
+                         R);
       break;
     case PA_BF16:
-      hipLaunchKernelGGL(decode_merge_kernel<BF16>, grid, dim3(threads), 0, s, a, items_per_seq,
-                         rpi);
+      hipLaunchKernelGGL(decode_merge_kernel<BF16>, grid, dim3(threads), lds, s, a, items_per_seq,
+                         R);
       break;
   }
   return hipGetLastError();

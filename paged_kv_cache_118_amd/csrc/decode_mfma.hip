@@ -98,7 +98,7 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_mfma_kernel(DecodeArgs a
   constexpr int EB = 2;
   constexpr int KN = D / 32;  // uint4 per lane per K tile (= QK k-steps)
   constexpr int MT = D / 16;  // d tiles of O^T
-  extern __shared__ int smem[];  // split 1: s_pre[B+1], s_len[B]
+  extern __shared__ int smem[];  // split 1: s_pre[B+1], s_len[B], s_ppre[B+1]
 
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -108,23 +108,26 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_mfma_kernel(DecodeArgs a
   const int G = a.num_q_heads / a.num_kv_heads;
   const int bs = a.block_size;
   const int64_t hkv = a.num_kv_heads;
+  const int C = a.part_steps;
   int* s_pre = smem;
   int* s_len = smem + B + 1;
+  int* s_ppre = smem + 2 * B + 1;
 
   Cursor c0;
   int count;
   Split sp{};
   int64_t x0 = 0;  // split 1: first stream step of this worker
   if (a.split) {
-    if (wv == 0) wave_scan_steps(a.context_lens, B, H, a.len_cap, kGroup, s_pre, s_len);
+    if (wv == 0)
+      wave_scan_steps(a.context_lens, B, H, a.len_cap, kGroup, C, s_pre, s_len, s_ppre);
     __syncthreads();
+    if (blockIdx.x == 0 && wv == 0) export_prefixes(s_pre, s_ppre, B, C, a.ws_pre, a.ws_ppre);
     const int N = s_pre[B];  // empty sequences get their zero rows from the merge
     if (N == 0) return;
-    sp = make_split(a, N);
+    sp = make_split(a.num_workers, N);
     if (worker >= sp.W) return;
     x0 = sp.start(worker);
-    const int64_t x1 = sp.start(worker + 1);  // fixed chunks: the last one ends at N
-    count = (int)((x1 < N ? x1 : N) - x0);
+    count = (int)(sp.start(worker + 1) - x0);
     c0 = locate(s_pre, s_len, B, H, kGroup, (int)x0);
   } else {
     if (worker >= B * H) return;
@@ -236,16 +239,12 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_mfma_kernel(DecodeArgs a
   // Phase 1 of a group: S^T = K Q^T, online-softmax update, P^T operand.
   auto qk = [&](const Cursor& cu, const uint4 (&kr)[2][KN], const uint4 (&qr)[KN], int j,
                 uint4& pb, int& nvalid) {
-    if (j == 0 || cu.k == 0) {  // a new segment starts
+    if (segment_starts(cu, j, C)) {
       m_run = -INFINITY;
       l_lane = 0.f;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) acc[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
       seg_k0 = cu.k;
-      if (a.split && cu.k == 0 && lane == 0) {  // this worker starts the item
-        const int last = sp.worker_of(x0 + j + cu.n - 1);
-        a.ws_desc[cu.item(H)] = make_int2(worker, last - worker + 1);
-      }
     }
     nvalid = min(kGroup, cu.L - cu.k * kGroup);
     float4_t st[2];
@@ -322,12 +321,11 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_mfma_kernel(DecodeArgs a
     }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma(TT{}, vr[mt], pb, acc[mt]);
-    if (j == count - 1 || cu.k == cu.n - 1) {  // the segment ends here
+    if (segment_ends(cu, j, count - 1, C)) {
       float l_tot = l_lane + __shfl_xor(l_lane, 16);
       l_tot += __shfl_xor(l_tot, 32);
-      const int item = cu.item(H);
       const int64_t orow0 = (int64_t)cu.b * a.num_q_heads + (int64_t)cu.h * G;
-      if (seg_k0 == 0 && cu.k == cu.n - 1) {
+      if (seg_k0 == 0 && cu.k == cu.n - 1) {  // the whole item: final rows
         if (n < G) {
           const int64_t orow = (orow0 + n) * D;
           const float inv = 1.f / l_tot;
@@ -338,16 +336,17 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_mfma_kernel(DecodeArgs a
               store_out<TT>(a.out, orow + mt * 16 + 4 * kb + e, acc[mt][e] * inv);
         }
       } else {
+        // Partial record (pa_internal.h): for each d tile the group's lanes
+        // write one contiguous run of 64 G bytes; then the 128-byte m / l
+        // line, written whole (lanes kb = 2, 3 write its zero half).
+        const int64_t slot = (int64_t)partition_index(cu, H, C, s_ppre) + worker;
+        float* rec = a.ws_part + slot * part_record(G, D);
         if (n < G) {
-          const int64_t row = ((int64_t)item + worker) * G + n;  // slot item + worker
+          float* o = rec + (kb * G + n) * 4;
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
-            *reinterpret_cast<float4_t*>(a.ws_o + row * D + mt * 16 + 4 * kb) = acc[mt];
-          if (kb == 0) {
-            a.ws_m[row] = m_run;
-            a.ws_l[row] = l_tot;
-          }
+          for (int mt = 0; mt < MT; ++mt) *reinterpret_cast<float4_t*>(o + mt * 16 * G) = acc[mt];
         }
+        if (lane < 32) rec[G * D + lane] = (lane & 15) < G ? (lane < 16 ? m_run : l_tot) : 0.f;
       }
     }
   };
@@ -448,9 +447,18 @@ int mfma_sched() {
 }
 
 template <typename TT, int D>
+const void* mfma_fn() {
+  switch (mfma_sched()) {
+    case 1: return reinterpret_cast<const void*>(&decode_mfma_kernel<TT, D, 1, 2>);
+    case 2: return reinterpret_cast<const void*>(&decode_mfma_kernel<TT, D, 0, 3>);
+  }
+  return reinterpret_cast<const void*>(&decode_mfma_kernel<TT, D, 0, 2>);
+}
+
+template <typename TT, int D>
 hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
   dim3 grid((a.num_workers + kWaves - 1) / kWaves);
-  const size_t lds = a.split ? sizeof(int) * (2 * (size_t)a.num_seqs + 1) : 0;
+  const size_t lds = a.split ? sizeof(int) * (3 * (size_t)a.num_seqs + 2) : 0;
   switch (mfma_sched()) {
     case 1:
       hipLaunchKernelGGL((decode_mfma_kernel<TT, D, 1, 2>), grid, dim3(kThreads), lds, s, a);
@@ -480,6 +488,16 @@ bool decode_mfma_supported(pa_dtype dt, int head_dim, int block_size, int group)
   const bool d_ok = head_dim == 64 || head_dim == 128;
   const bool bs_ok = block_size == 8 || block_size == 16 || (block_size % 32 == 0);
   return dt_ok && d_ok && bs_ok && group >= 2 && group <= 16;
+}
+
+int decode_mfma_waves_per_cu(pa_dtype dt, int head_dim) {
+  const void* f = dt == PA_F16 ? (head_dim == 64 ? mfma_fn<F16, 64>() : mfma_fn<F16, 128>())
+                               : (head_dim == 64 ? mfma_fn<BF16, 64>() : mfma_fn<BF16, 128>());
+  int blocks = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, f, kThreads, 0) != hipSuccess ||
+      blocks <= 0)
+    return kWaves;
+  return blocks * kWaves;
 }
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, pa_dtype dt, hipStream_t s) {

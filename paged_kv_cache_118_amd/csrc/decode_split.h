@@ -3,19 +3,24 @@
 // Work items are (sequence b, head h) pairs, h < H (q heads for the MHA
 // kernel, kv heads for the GQA kernel), ordered b-major.  Item (b, h) has
 // n_b = ceil(L_b / STEP) steps of STEP tokens.  Laid end to end the items form
-// one stream of N = sum_b H * n_b steps; worker w (one wavefront) takes steps
-// [start(w), start(w+1)): either W equal shares (start(w) = w*N/W, so shares
-// differ by at most one step) or fixed chunks of C steps.  Every worker
-// therefore streams the same number of K/V bytes regardless of how lengths
-// are distributed, and it prefetches straight across item boundaries.
+// one stream of N = sum_b H * n_b steps; worker w (one wavefront) takes the
+// steps [w*N/W, (w+1)*N/W), so shares differ by at most one step and every
+// worker streams the same number of K/V bytes whatever the lengths.  A worker
+// prefetches straight across item boundaries.
 //
-// A worker that sees all of an item's steps writes the final output row;
-// otherwise it writes its partial (m, l, o) to slot item + w.  That slot is
-// unique: along the stream every new (item, worker) segment increases the
-// item index, the worker index or both.  Item i starting at stream step S_i
-// is shared by the workers F = worker_of(S_i) .. Lw = worker_of(S_i + n - 1);
-// worker F records (F, Lw - F + 1) for the merge kernel, which combines the
-// slots.
+// Segments.  A worker's steps of one item form a segment, which is further
+// cut at partition boundaries when a partition size P = C * STEP is given
+// (item steps [p*C, (p+1)*C) form partition p).  A segment that is a whole
+// item is written as the final output row.  Otherwise it becomes an fp32
+// partial (m, l, o) of the item: running max in the base-2 domain, sum of
+// 2^(s - m), unnormalised output; the merge kernel (decode_merge.hip)
+// combines an item's partials.
+//
+// Slots.  The partial of segment (partition p, worker w) goes to slot
+// pg + w, with pg the stream-order index of the partition over all items
+// (the item index itself when no partition size is given).  Along the stream
+// every new segment increases pg, w or both, so slots are unique; the merge
+// recomputes from the same arithmetic which (p, w) pairs an item has.
 #pragma once
 
 #include "pa_internal.h"
@@ -24,67 +29,76 @@ namespace pa {
 
 __device__ __forceinline__ int clamp_len(int L, int cap) { return L < 0 ? 0 : (L > cap ? cap : L); }
 
-// Exclusive prefix over sequences of H * n_b (LDS s_pre[0..B]) and the
-// clamped lengths (LDS s_len[0..B-1]), computed by ONE wavefront: lane i
-// handles a contiguous run of sequences, then a shuffle scan across lanes.
-// The caller publishes the arrays to the other wavefronts with a barrier.
-// Returns N = s_pre[B] (in every lane).
-__device__ inline int wave_scan_steps(const int32_t* lens, int B, int H, int cap, int step,
-                                      int* s_pre, int* s_len) {
+// s_waitcnt operand: vmcnt 0, expcnt and lgkmcnt left at their maxima (gfx9
+// encoding).
+constexpr int kVmcntZero = 0x0F70;
+
+// Exclusive prefixes over sequences of H * n_b (LDS s_pre[0..B]) and, when
+// C > 0, of H * ceil(n_b / C) (s_ppre[0..B]), plus the clamped lengths
+// (s_len[0..B-1]), computed by ONE wavefront: lane i handles a contiguous run
+// of sequences, then a shuffle scan across lanes.  The caller publishes the
+// arrays to the other wavefronts with a barrier.  Returns N = s_pre[B] (in
+// every lane).
+__device__ inline int wave_scan_steps(const int32_t* lens, int B, int H, int cap, int step, int C,
+                                      int* s_pre, int* s_len, int* s_ppre) {
   const int lane = threadIdx.x & 63;
   const int per = (B + 63) / 64;
   const int j0 = min(lane * per, B), j1 = min(j0 + per, B);
-  int local = 0;
+  int local = 0, plocal = 0;
   for (int j = j0; j < j1; ++j) {
     const int L = clamp_len(lens[j], cap);
     s_len[j] = L;
-    local += H * ((L + step - 1) / step);
+    const int n = (L + step - 1) / step;
+    local += H * n;
+    if (C > 0) plocal += H * ((n + C - 1) / C);
   }
-  int incl = local;
+  int incl = local, pincl = plocal;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
     const int y = __shfl_up(incl, off);
-    if (lane >= off) incl += y;
+    const int py = __shfl_up(pincl, off);
+    if (lane >= off) {
+      incl += y;
+      pincl += py;
+    }
   }
-  int run = incl - local;
+  int run = incl - local, prun = pincl - plocal;
   for (int j = j0; j < j1; ++j) {
+    const int n = (s_len[j] + step - 1) / step;
     s_pre[j] = run;
-    run += H * ((s_len[j] + step - 1) / step);
+    run += H * n;
+    if (C > 0) {
+      s_ppre[j] = prun;
+      prun += H * ((n + C - 1) / C);
+    }
   }
-  if (lane == 63) s_pre[B] = incl;
+  if (lane == 63) {
+    s_pre[B] = incl;
+    if (C > 0) s_ppre[B] = pincl;
+  }
   return __shfl(incl, 63);
 }
 
 // Balanced shares are at least kMinChunk steps, so that a worker's start-up
-// is amortised and an item never has more than n / kMinChunk + 2 partials.
+// is amortised.
 constexpr int kMinChunk = 8;
 
 struct Split {
   int64_t N;  // steps in the stream (> 0)
   int W;      // workers that take steps
-  int C;      // fixed steps per worker, 0 = W equal shares
-  // First step of worker w's share (for w == W: N with equal shares, possibly
-  // past N with fixed chunks -- callers clamp).
-  __device__ __forceinline__ int64_t start(int w) const {
-    return C ? (int64_t)w * C : (int64_t)w * N / W;
-  }
+  // First step of worker w's share (start(W) == N).
+  __device__ __forceinline__ int64_t start(int w) const { return (int64_t)w * N / W; }
   // The worker whose share holds stream step x: the largest w with start(w) <= x.
   __device__ __forceinline__ int worker_of(int64_t x) const {
-    return C ? (int)(x / C) : (int)(((x + 1) * W - 1) / N);
+    return (int)(((x + 1) * W - 1) / N);
   }
 };
 
-__device__ __forceinline__ Split make_split(const DecodeArgs& a, int N) {
+__device__ __forceinline__ Split make_split(int num_workers, int N) {
   Split s;
   s.N = N;
-  if (a.chunk_steps > 0) {
-    s.C = a.chunk_steps;
-    s.W = (N + s.C - 1) / s.C;
-  } else {
-    s.C = 0;
-    const int cap = N / kMinChunk;
-    s.W = a.num_workers < cap ? a.num_workers : (cap > 0 ? cap : 1);
-  }
+  const int cap = N / kMinChunk;
+  s.W = num_workers < cap ? num_workers : (cap > 0 ? cap : 1);
   return s;
 }
 
@@ -94,7 +108,7 @@ struct Cursor {
   __device__ __forceinline__ int item(int H) const { return b * H + h; }
 };
 
-// Cursor of stream step x (flat mode): the sequence with s_pre[b] <= x < s_pre[b+1].
+// Cursor of stream step x: the sequence with s_pre[b] <= x < s_pre[b+1].
 __device__ __forceinline__ Cursor locate(const int* s_pre, const int* s_len, int B, int H,
                                          int step, int x) {
   int lo = 0, hi = B;  // first index with s_pre[idx] > x, searched in [0, B]
@@ -112,7 +126,7 @@ __device__ __forceinline__ Cursor locate(const int* s_pre, const int* s_len, int
   return c;
 }
 
-// Next step of the stream (flat mode: skips empty sequences).
+// Next step of the stream (skips empty sequences).
 __device__ __forceinline__ void advance(Cursor& c, const int* s_pre, const int* s_len, int H,
                                         int step) {
   if (++c.k < c.n) return;
@@ -124,6 +138,34 @@ __device__ __forceinline__ void advance(Cursor& c, const int* s_pre, const int* 
   } while (s_pre[c.b + 1] == s_pre[c.b]);
   c.L = s_len[c.b];
   c.n = (c.L + step - 1) / step;
+}
+
+// Stream-order index of the partition holding the cursor's step (the item
+// index when C == 0).
+__device__ __forceinline__ int partition_index(const Cursor& c, int H, int C, const int* s_ppre) {
+  if (C == 0) return c.item(H);
+  const int np = (c.n + C - 1) / C;
+  return s_ppre[c.b] + c.h * np + c.k / C;
+}
+
+// The step ends a segment of a worker whose last stream step has index
+// `last_j` within its share (j = index of this step within the share).
+__device__ __forceinline__ bool segment_ends(const Cursor& c, int j, int last_j, int C) {
+  return j == last_j || c.k == c.n - 1 || (C > 0 && (c.k + 1) % C == 0);
+}
+__device__ __forceinline__ bool segment_starts(const Cursor& c, int j, int C) {
+  return j == 0 || c.k == 0 || (C > 0 && c.k % C == 0);
+}
+
+// Copies the scan's prefixes to global memory for the merge kernel:
+// pre[0..B] = s_pre, ppre[0..B] = s_ppre (C > 0).  Called by one wavefront
+// after the barrier that published them.
+__device__ inline void export_prefixes(const int* s_pre, const int* s_ppre, int B, int C,
+                                       int* pre, int* ppre) {
+  for (int j = threadIdx.x & 63; j <= B; j += 64) {
+    pre[j] = s_pre[j];
+    if (C > 0) ppre[j] = s_ppre[j];
+  }
 }
 
 }  // namespace pa

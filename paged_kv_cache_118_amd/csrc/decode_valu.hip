@@ -22,7 +22,7 @@
 //      hold the same 8 tokens -- the 16 weights are broadcast with readlane
 //      into scalar registers, and each lane's accumulators are complete sums
 //      needing no cross-lane reduction.
-// Loads for step i+1 are issued before step i is computed, also across item
+// The loads of a batch of steps are issued together, also across item
 // boundaries.  Items split between workers are merged by decode_merge.hip.
 //
 // decode_generic_kernel -- any head_dim <= 256 / block_size / dtype, one
@@ -40,6 +40,8 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kStep = 16;  // tokens per wave step
+// s_waitcnt operand: vmcnt 0, expcnt and lgkmcnt left at their maxima (gfx9 encoding)
+constexpr int kVmcntZero = 0x0F70;
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
@@ -179,14 +181,14 @@ struct TableWindow {
   }
 };
 
-template <typename TT, int D>
+template <typename TT, int D, int NB>
 __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
   constexpr int EB = TT::bytes;
   constexpr int NK = D * EB / 64;  // uint4 per lane per step, K and V alike
   constexpr int R = D / 64;        // slab rows owned by a lane
   constexpr int NVR = VMap<TT, R>::NVR;
   static_assert(R >= 1 && 2 * R * NVR == NK, "unsupported shape");
-  extern __shared__ int smem[];  // split 1: s_pre[B+1], s_len[B]
+  extern __shared__ int smem[];  // split 1: s_pre[B+1], s_len[B], s_ppre[B+1]
 
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -196,23 +198,25 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
   const int bs = a.block_size;
   const int64_t hkv = a.num_kv_heads;
   const int tq = lane >> 2, c = lane & 3;
+  const int C = a.part_steps;
   int* s_pre = smem;
   int* s_len = smem + B + 1;
+  int* s_ppre = smem + 2 * B + 1;
 
   Cursor c0;
   int count;
   Split sp{};
   int64_t x0 = 0;  // split 1: first stream step of this worker
   if (a.split) {
-    if (wv == 0) wave_scan_steps(a.context_lens, B, H, a.len_cap, kStep, s_pre, s_len);
+    if (wv == 0) wave_scan_steps(a.context_lens, B, H, a.len_cap, kStep, C, s_pre, s_len, s_ppre);
     __syncthreads();
+    if (blockIdx.x == 0 && wv == 0) export_prefixes(s_pre, s_ppre, B, C, a.ws_pre, a.ws_ppre);
     const int N = s_pre[B];  // empty sequences get their zero rows from the merge
     if (N == 0) return;
-    sp = make_split(a, N);
+    sp = make_split(a.num_workers, N);
     if (worker >= sp.W) return;
     x0 = sp.start(worker);
-    const int64_t x1 = sp.start(worker + 1);  // fixed chunks: the last one ends at N
-    count = (int)((x1 < N ? x1 : N) - x0);
+    count = (int)(sp.start(worker + 1) - x0);
     c0 = locate(s_pre, s_len, B, H, kStep, (int)x0);
   } else {
     if (worker >= B * H) return;
@@ -317,16 +321,12 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
 
   auto compute = [&](const Cursor& cu, const uint4 (&kr)[NK], uint4 (&vr)[NK],
                      const uint4 (&qr)[NK], int j) {
-    if (j == 0 || cu.k == 0) {  // a new segment starts
+    if (segment_starts(cu, j, C)) {
       m_run = -INFINITY;
       l_lane = 0.f;
 #pragma unroll
       for (int r = 0; r < R; ++r) acc[r] = 0.f;
       seg_k0 = cu.k;
-      if (a.split && cu.k == 0 && lane == 0) {  // this worker starts the item
-        const int last = sp.worker_of(x0 + j + cu.n - 1);
-        a.ws_desc[cu.item(H)] = make_int2(worker, last - worker + 1);
-      }
     }
     const int nvalid = min(kStep, cu.L - cu.k * kStep);
     float d = lane_dot(TT{}, qr, kr);
@@ -351,53 +351,59 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
     for (int r = 0; r < R; ++r) acc[r] *= alpha;
     lane_pv<TT, R, NK>(acc, pt, vr);
 
-    if (j == count - 1 || cu.k == cu.n - 1) {  // the segment ends here
+    if (segment_ends(cu, j, count - 1, C)) {
       const float l_tot = wave_sum(l_lane);
       const int item = cu.item(H);
-      if (seg_k0 == 0 && cu.k == cu.n - 1) {
+      if (seg_k0 == 0 && cu.k == cu.n - 1) {  // the whole item: final row
         const int64_t orow = (int64_t)item * D;
 #pragma unroll
         for (int r = 0; r < R; ++r) store_out<TT>(a.out, orow + lane + 64 * r, acc[r] / l_tot);
       } else {
-        const int64_t slot = (int64_t)item + worker;
+        const int64_t slot = (int64_t)partition_index(cu, H, C, s_ppre) + worker;
+        // partial record (pa_internal.h): o, then the 128-byte m / l line
+        float* rec = a.ws_part + slot * part_record(1, D);
 #pragma unroll
-        for (int r = 0; r < R; ++r) a.ws_o[slot * D + lane + 64 * r] = acc[r];
-        if (lane == 0) {
-          a.ws_m[slot] = m_run;
-          a.ws_l[slot] = l_tot;
-        }
+        for (int r = 0; r < R; ++r) rec[lane + 64 * r] = acc[r];
+        if (lane < 32) rec[D + lane] = lane == 0 ? m_run : (lane == 16 ? l_tot : 0.f);
       }
     }
   };
 
-  // Two register sets: step j+1 is always in flight while step j computes.
-  // The prefetch is unconditional (the last step re-issues its own, cached,
-  // addresses) so the wait before each compute covers only the older set.
-  uint4 ka[NK], va[NK], qa[NK], kb2[NK], vb2[NK], qb[NK];
-  int qia = -1, qib = -1;
-  Cursor c1 = c0;
-  if (count > 1) {
-    advance(c1, s_pre, s_len, H, kStep);
-    uniform(c1);
-  }
-  issue(c0, ka, va, qa, qia, true);
-  int j = 0;
-  for (;;) {
-    issue(c1, kb2, vb2, qb, qib, j + 1 < count);
-    compute(c0, ka, va, qa, j);
-    if (++j >= count) break;
-    c0 = c1;
-    if (j + 1 < count) {
-      advance(c1, s_pre, s_len, H, kStep);
-      uniform(c1);
+  // Steps are processed in batches of NB: the loads of all NB steps are
+  // issued back to back, then the NB steps are computed in order.  A batch's
+  // loads are in flight together while the other wavefronts of the CU
+  // compute, and every load is consumed within the batch that issued it, so
+  // the compiler's wait counts never hold a load of the next batch.  Issues
+  // past the worker's last step read cached bytes (see `issue`).
+  uint4 kr[NB][NK], vr[NB][NK], qr[NB][NK];
+  int qi[NB];
+#pragma unroll
+  for (int u = 0; u < NB; ++u) qi[u] = -1;
+  Cursor cur = c0;
+  for (int j = 0; j < count; j += NB) {
+    Cursor cs[NB];
+    cs[0] = cur;
+#pragma unroll
+    for (int u = 1; u < NB; ++u) {
+      cs[u] = cs[u - 1];
+      if (j + u < count) {
+        advance(cs[u], s_pre, s_len, H, kStep);
+        uniform(cs[u]);
+      }
     }
-    issue(c1, ka, va, qa, qia, j + 1 < count);
-    compute(c0, kb2, vb2, qb, j);
-    if (++j >= count) break;
-    c0 = c1;
-    if (j + 1 < count) {
-      advance(c1, s_pre, s_len, H, kStep);
-      uniform(c1);
+#pragma unroll
+    for (int u = 0; u < NB; ++u) issue(cs[u], kr[u], vr[u], qr[u], qi[u], j + u < count);
+#pragma unroll
+    for (int u = 0; u < NB; ++u)
+      if (j + u < count) compute(cs[u], kr[u], vr[u], qr[u], j + u);
+    // All of the batch's loads have landed here on every path (the ones past
+    // the last step are never consumed); saying so keeps the compiler from
+    // waiting on them inside the next batch's issue.
+    __builtin_amdgcn_s_waitcnt(kVmcntZero);
+    cur = cs[NB - 1];
+    if (j + NB < count) {
+      advance(cur, s_pre, s_len, H, kStep);
+      uniform(cur);
     }
   }
 }
@@ -468,11 +474,25 @@ __global__ __launch_bounds__(64) void decode_generic_kernel(DecodeArgs a) {
   }
 }
 
+// Steps per batch: two while a lane's K / V / q registers of a step fit in
+// 48 VGPRs (16-bit data up to D = 128, fp32 up to D = 64), else one, so
+// that the kernel keeps at least two wavefronts per SIMD.
+template <typename TT, int D>
+constexpr int valu_batch() {
+  return D * TT::bytes <= 256 ? 2 : 1;
+}
+
+template <typename TT, int D>
+const void* valu_fn() {
+  return reinterpret_cast<const void*>(&decode_valu_kernel<TT, D, valu_batch<TT, D>()>);
+}
+
 template <typename TT, int D>
 hipError_t launch_valu_d(const DecodeArgs& a, hipStream_t s) {
   dim3 grid((a.num_workers + kWaves - 1) / kWaves);
-  const size_t lds = a.split ? sizeof(int) * (2 * (size_t)a.num_seqs + 1) : 0;
-  hipLaunchKernelGGL((decode_valu_kernel<TT, D>), grid, dim3(kThreads), lds, s, a);
+  const size_t lds = a.split ? sizeof(int) * (3 * (size_t)a.num_seqs + 2) : 0;
+  hipLaunchKernelGGL((decode_valu_kernel<TT, D, valu_batch<TT, D>()>), grid, dim3(kThreads), lds,
+                     s, a);
   return hipGetLastError();
 }
 
@@ -487,6 +507,26 @@ hipError_t launch_valu_t(const DecodeArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+int decode_valu_waves_per_cu(pa_dtype dt, int head_dim) {
+  const void* f = nullptr;
+  switch (dt) {
+    case PA_F32: f = head_dim == 64 ? valu_fn<F32, 64>() : head_dim == 128 ? valu_fn<F32, 128>()
+                                                                            : valu_fn<F32, 256>();
+      break;
+    case PA_F16: f = head_dim == 64 ? valu_fn<F16, 64>() : head_dim == 128 ? valu_fn<F16, 128>()
+                                                                            : valu_fn<F16, 256>();
+      break;
+    case PA_BF16: f = head_dim == 64 ? valu_fn<BF16, 64>() : head_dim == 128 ? valu_fn<BF16, 128>()
+                                                                              : valu_fn<BF16, 256>();
+      break;
+  }
+  int blocks = 0;
+  if (!f || hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, f, kThreads, 0) != hipSuccess ||
+      blocks <= 0)
+    return kWaves;
+  return blocks * kWaves;
+}
 
 bool decode_valu_supported(pa_dtype dt, int head_dim, int block_size) {
   (void)dt;

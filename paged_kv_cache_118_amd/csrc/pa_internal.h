@@ -79,23 +79,31 @@ struct DecodeArgs {
   int64_t num_blocks;
   // work split (decode_split.h)
   int32_t split;        // 0: one item per worker, 1: token-balanced stream split
-  int32_t chunk_steps;  // split 1: fixed steps per worker, 0 = equal shares
+  int32_t part_steps;   // split 1: steps per partition (partials cut there), 0 = none
   int32_t num_workers;  // wavefronts launched
-  // partials of split items, slot = item + worker (split 1 only); rows of an
-  // item are its q heads (1 for the MHA kernel, the group for the GQA kernel)
-  float* ws_m;          // [slots][rows]
-  float* ws_l;          // [slots][rows]
-  float* ws_o;          // [slots][rows][head_dim]
-  int2* ws_desc;        // [items]: (first worker, number of workers) of the item
+  // split 1: partials (decode_split.h), one record of part_record(rows, D)
+  // floats per slot; rows of an item are its q heads (1 for the MHA kernel,
+  // the group for GQA).  Record layout: o of (row r, dim d) at
+  // ((d/16)*4 + d%16/4)*rows*4 + r*4 + d%4 (for one row simply d), then a
+  // 128-byte tail: m of row r at rows*D + r, l at rows*D + 16 + r, the rest
+  // zero.  A record is written whole by one wavefront, in whole cache lines.
+  float* ws_part;       // [slots][part_record(rows, D)]
+  int32_t* ws_pre;      // [B+1] step prefix per sequence (for the merge)
+  int32_t* ws_ppre;     // [B+1] partition prefix per sequence (part_steps > 0)
 };
 
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_decode_valu(const DecodeArgs& a, pa_dtype dt, hipStream_t s);
 hipError_t launch_decode_mfma(const DecodeArgs& a, pa_dtype dt, hipStream_t s);
 hipError_t launch_decode_generic(const DecodeArgs& a, pa_dtype dt, hipStream_t s);
-hipError_t launch_decode_merge(const DecodeArgs& a, pa_dtype dt, int items_per_seq,
-                              hipStream_t s);
+// Merge of the split items' partials (decode_merge.hip); step = tokens per
+// worker step of the decode kernel that ran.
+hipError_t launch_decode_merge(const DecodeArgs& a, pa_dtype dt, int items_per_seq, int step,
+                               hipStream_t s);
 bool decode_valu_supported(pa_dtype dt, int head_dim, int block_size);
+// Resident wavefronts per CU of the kernel a call with these arguments runs.
+int decode_valu_waves_per_cu(pa_dtype dt, int head_dim);
+int decode_mfma_waves_per_cu(pa_dtype dt, int head_dim);
 bool decode_mfma_supported(pa_dtype dt, int head_dim, int block_size, int group);
 
 hipError_t launch_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,
@@ -106,6 +114,9 @@ hipError_t launch_reshape_and_cache(const void* k, const void* v, void* k_cache,
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs,
                               int32_t num_pairs, int64_t block_bytes, int64_t num_blocks,
                               hipStream_t s);
+
+// Floats per partial record (see DecodeArgs::ws_part); rows <= 16.
+__host__ __device__ inline int part_record(int rows, int head_dim) { return rows * head_dim + 32; }
 
 // Tokens per V slab: V is stored as [block][head][BS/VS][D][VS].
 __host__ __device__ inline int v_slab(int block_size) { return block_size < 8 ? block_size : 8; }

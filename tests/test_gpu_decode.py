@@ -232,10 +232,11 @@ def _decode_ws(case, part, ws):
     return out
 
 
-def test_workspace_reused_without_clearing():
-    """One workspace serves a sequence of calls with other shapes and split
-    modes in between: every call equals the same call on a fresh workspace,
-    bit for bit (nothing a call leaves behind is read by the next)."""
+def test_workspace_reused_across_shapes():
+    """One workspace (starting as garbage) serves a sequence of calls with
+    other shapes and split modes in between: every call equals the same call
+    on a fresh workspace, bit for bit (nothing a call leaves behind is read by
+    the next)."""
     import paged_kv_cache_118_amd as pa
     names = ["opt13b_f16_bs16", "gqa_bf16_g8_bs32", "llama_bf16_bs16", "gqa_f16_g4_bs16"]
     cases = {n: to_dev(W.make_decode_case(SMALL[n], device=DEV)) for n in names}
@@ -265,3 +266,37 @@ def test_item_shared_by_many_workers(spec_name):
     err = max_err(out, oracle_decode(case))
     log(f"  max abs err {err:.3e}")
     assert err <= TOL[spec.dtype]
+
+
+@pytest.mark.parametrize("spec_name,part", [("opt13b_f16_bs16", 0), ("opt13b_f16_bs16", 512),
+                                            ("gqa_bf16_g8_bs32", 0), ("gqa_bf16_g8_bs32", 256),
+                                            ("gqa_f16_g4_bs16", 512)])
+def test_workspace_same_layout_many_calls(spec_name, part):
+    """Calls with one layout reuse one workspace (starting as garbage).
+    Lengths change every call, so the slots an item's pieces use move, and
+    slots left over from the previous call sit between them; every call must
+    equal the same call on a fresh workspace, bit for bit, and the oracle
+    within tolerance."""
+    import paged_kv_cache_118_amd as pa
+    spec = SMALL[spec_name]
+    cap = 3000
+    rng = np.random.default_rng(1180 + part)
+    need = pa.pa_decode_workspace_bytes(spec.num_seqs, spec.num_q_heads, spec.num_kv_heads,
+                                        spec.head_dim, spec.block_size, cap, part,
+                                        W.TORCH_DTYPE[spec.dtype])
+    ws = torch.full((need,), 0x7f, dtype=torch.uint8, device=DEV)
+    for call in range(6):
+        lens = rng.integers(1, cap + 1, size=spec.num_seqs)
+        if call == 3:
+            lens[::2] = rng.integers(1, 40, size=len(lens[::2]))  # many short items
+        case = to_dev(W.make_decode_case(spec.with_(seed=spec.seed + call), device=DEV,
+                                         lens=list(lens)))
+        log(f"[ws same layout] {spec_name} partition={part} call {call}")
+        out = torch.empty_like(case.q)
+        pa.pa_decode(out, case.q, case.k_cache, case.v_cache,
+                     torch.from_numpy(case.tables).to(DEV), torch.from_numpy(case.lens).to(DEV),
+                     spec.scale, spec.block_size, spec.num_kv_heads, cap, partition_size=part,
+                     workspace=ws)
+        fresh = gpu_decode(case, partition_size=part, max_context_len=cap)
+        assert torch.equal(out, fresh)
+        assert max_err(out, oracle_decode(case)) <= TOL[spec.dtype]
