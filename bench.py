@@ -51,6 +51,11 @@ def parse():
                     help="only run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--stream-probe", action="store_true",
                     help="only measure plain device read / copy bandwidth (context for peak)")
+    ap.add_argument("--mfma-summary", metavar="FOLDER",
+                    help="only summarise one rocprofv3 --pmc output folder holding "
+                         "SQ_INSTS_VALU_MFMA_MOPS_<dtype>, SQ_VALU_MFMA_BUSY_CYCLES and "
+                         "GRBM_GUI_ACTIVE of this workload into the MFMA record stored under "
+                         "profiles/")
     ap.add_argument("--counters-summary", nargs=4, metavar=("FETCH", "WRITE", "CFETCH", "CWRITE"),
                     help="only summarise four rocprofv3 --pmc output folders (FETCH_SIZE and "
                          "WRITE_SIZE of this workload, then of --calib-copy-mb 1024) into the "
@@ -103,15 +108,62 @@ def counters_summary(args) -> dict:
     kernels = [k for k in fetch if k.startswith("decode_")]
     per = {k: {"fetch_bytes": round(fetch[k] * f_scale * 1024),
                "write_bytes": round(write.get(k, 0.0) * w_scale * 1024)} for k in kernels}
-    return {"workload": args.workload, "sources_sha256": kernel_sources_sha(),
+    return {"workload": args.workload, "partition": args.partition,
+            "sources_sha256": kernel_sources_sha(),
             "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
             "kernels": per,
             "bytes_per_call": sum(v["fetch_bytes"] + v["write_bytes"] for v in per.values())}
 
 
-def stored_traffic(workload: str):
+MFMA_TAG = "mfma-record:"
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0}  # MI355X dense matrix peak
+
+
+def _pmc_by_counter(folder: str, kernel: str) -> dict:
+    """Median value per counter of one pa kernel over the dispatches of a run."""
+    import csv
+    import glob
+    vals = {}
+    for path in glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if kernel in r["Kernel_Name"]:
+                    vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    return {k: float(np.median(v)) for k, v in vals.items()}
+
+
+def mfma_summary(args) -> dict:
+    """MFMA work of the decode_mfma kernel per dispatch: the MOPS counter
+    counts units of 512 flops."""
+    c = _pmc_by_counter(args.mfma_summary, "decode_mfma_kernel")
+    mops = sum(v for k, v in c.items() if k.startswith("SQ_INSTS_VALU_MFMA_MOPS_"))
+    return {"workload": args.workload, "partition": args.partition,
+            "sources_sha256": kernel_sources_sha(), "mfma_flops_per_call": mops * 512,
+            "mfma_busy_cycles": c.get("SQ_VALU_MFMA_BUSY_CYCLES"),
+            "gui_active_cycles": c.get("GRBM_GUI_ACTIVE"), "counters": c}
+
+
+def stored_mfma(workload: str, partition):
+    """Issued MFMA flops per pa_decode call from the stored record (None when
+    absent or the kernel sources changed)."""
+    import glob
+    sha = kernel_sources_sha()
+    for path in sorted(glob.glob(os.path.join(PROFILES, "*.md"))):
+        with open(path) as f:
+            for line in f:
+                line = line.strip().strip("`")
+                if line.startswith(MFMA_TAG):
+                    rec = json.loads(line[len(MFMA_TAG):])
+                    if rec.get("workload") == workload and rec.get("partition") == partition \
+                            and rec.get("sources_sha256") == sha:
+                        return rec["mfma_flops_per_call"]
+    return None
+
+
+def stored_traffic(workload: str, partition):
     """HBM bytes per pa_decode call from the stored record, or None when no
-    record exists for the workload or the kernel sources changed since."""
+    record exists for the workload (and partition argument) or the kernel
+    sources changed since."""
     import glob
     sha = kernel_sources_sha()
     for path in sorted(glob.glob(os.path.join(PROFILES, "*.md"))):
@@ -120,7 +172,8 @@ def stored_traffic(workload: str):
                 line = line.strip().strip("`")
                 if line.startswith(RECORD_TAG):
                     rec = json.loads(line[len(RECORD_TAG):])
-                    if rec.get("workload") == workload and rec.get("sources_sha256") == sha:
+                    if rec.get("workload") == workload and rec.get("partition") == partition \
+                            and rec.get("sources_sha256") == sha:
                         return rec["bytes_per_call"]
     return None
 
@@ -321,6 +374,8 @@ class Workload:
             B, sp.num_q_heads, sp.num_kv_heads, sp.head_dim, sp.block_size, self.max_ctx,
             self.part, W.TORCH_DTYPE[sp.dtype])
         self.config["replicas"] = self.replicas
+        self.mfma_path = (sp.dtype in ("f16", "bf16") and sp.num_q_heads // sp.num_kv_heads >= 4
+                          and sp.head_dim in (64, 128))
         self.config["kv_read_bytes_per_step"] = self.kv_read_bytes
         if hasattr(self, "unique_kv_bytes"):
             self.config["unique_kv_bytes_per_step"] = self.unique_kv_bytes
@@ -423,6 +478,9 @@ def main():
     if args.counters_summary:
         print(RECORD_TAG + " " + json.dumps(counters_summary(args)))
         return
+    if args.mfma_summary:
+        print(MFMA_TAG + " " + json.dumps(mfma_summary(args)))
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; use --gpus 1"}))
         sys.exit(2)
@@ -497,11 +555,27 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": stored_traffic(args.workload),
+            "traffic": stored_traffic(args.workload, args.partition),
             "kernel": wl.roofline_kernel,
         },
         "host_alloc_us_per_step": wl.host_alloc_us,
     }
+    if wl.mfma_path:
+        # GQA groups run on the matrix cores: the algorithmic flops (q.k and
+        # p.v, 2 per multiply-add) and, from the stored counter record, the
+        # issued ones (the group's rows are padded to 16), against the peak
+        sp = wl.spec
+        alg = 4.0 * sp.head_dim * sp.num_q_heads * float(np.sum(wl.lens.astype(np.int64)))
+        issued = stored_mfma(args.workload, args.partition)
+        peak = MFMA_PEAK_TFLOPS[wl.dtype]
+        rec["mfma"] = {
+            "alg_tflops": round(alg / (dec_ms / 1e3) / 1e12, 2),
+            "alg_frac": round(alg / (dec_ms / 1e3) / 1e12 / peak, 4),
+            "issued_tflops": None if issued is None else round(issued / (dec_ms / 1e3) / 1e12, 2),
+            "issued_frac": None if issued is None else
+            round(issued / (dec_ms / 1e3) / 1e12 / peak, 4),
+            "peak_tflops": peak,
+        }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = wl.cpu_baseline(args.cpu_seconds)
     print(json.dumps(rec), flush=True)
