@@ -49,6 +49,10 @@ def parse():
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--overhead-sweep", action="store_true",
+                    help="only run the paged-vs-contiguous sweep: the OPT-13B-shaped decode "
+                         "over one pool laid out contiguously per sequence and one with "
+                         "shuffled block ids, per context length and block size")
     ap.add_argument("--stream-probe", action="store_true",
                     help="only measure plain device read / copy bandwidth (context for peak)")
     ap.add_argument("--mfma-summary", metavar="FOLDER",
@@ -469,6 +473,81 @@ def stream_probe(torch, gib=4, reps=10):
     return res
 
 
+def overhead_sweep(args, torch):
+    """Cost of paging: the same decode (OPT-13B heads, fp16, 64 sequences of
+    equal length L) over a pool where every sequence's blocks are one
+    contiguous run (identity-like tables) and over one where block ids are a
+    seeded shuffle, per L and block size.  Both layouts hold the same logical
+    K/V, so the outputs are bitwise identical (the reduction order depends on
+    logical positions only); the sweep times b2b pa_decode calls of each.
+    One JSON line per (L, BS), then a summary line."""
+    import paged_kv_cache_118_amd as pa
+    import workloads as W
+    dev = torch.device("cuda:0")
+    sp = W.OPT13B
+    B, H, D = 64, sp.num_q_heads, sp.head_dim
+    out_rows = []
+    for bs in (8, 16, 32, 128):
+        for L in (128, 512, 2048, 4096):
+            lens = np.full(B, L, dtype=np.int32)
+            rng = np.random.default_rng(118_200 + bs + L)
+            ct, nb = W.contiguous_tables(lens, bs)
+            perm = rng.permutation(nb).astype(np.int32)
+            st = np.where(ct >= 0, perm[np.maximum(ct, 0)], -1).astype(np.int32)
+            per_call = int(lens.sum()) * 2 * H * D * 2
+            reps = max(2, int(math.ceil(2e9 / per_call)))
+            gen = W.make_generator(118_300 + bs, dev)
+            k = [W.randn(W.k_pool_shape(nb, H, bs, D, "f16"), "f16", gen, dev) for _ in range(reps)]
+            v = [W.randn(W.v_pool_shape(nb, H, bs, D), "f16", gen, dev) for _ in range(reps)]
+            # the shuffled pool holds the same logical blocks: physical perm[i] = contiguous i
+            inv = np.empty_like(perm)
+            inv[perm] = np.arange(nb, dtype=np.int32)
+            idx = torch.from_numpy(inv.astype(np.int64)).to(dev)
+            ks = [x.index_select(0, idx) for x in k]
+            vs_ = [x.index_select(0, idx) for x in v]
+            q = W.randn((B, H, D), "f16", gen, dev)
+            lens_d = torch.from_numpy(lens).to(dev)
+            res = {}
+            outs = {}
+            for name, tab, kk, vv in (("contiguous", ct, k, v), ("shuffled", st, ks, vs_)):
+                tab_d = torch.from_numpy(tab).to(dev)
+                ws = torch.empty(max(1, pa.pa_decode_workspace_bytes(B, H, H, D, bs, L, 0)),
+                                 dtype=torch.uint8, device=dev)
+                o = torch.empty_like(q)
+
+                def call(r):
+                    pa.pa_decode(o, q, kk[r], vv[r], tab_d, lens_d, sp.scale, bs, H, L,
+                                 partition_size=0, workspace=ws)
+                for r in range(2 * reps):
+                    call(r % reps)
+                torch.cuda.synchronize()
+                outs[name] = o.clone()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                n = max(10, 4 * reps)
+                e0.record()
+                for r in range(n):
+                    call(r % reps)
+                e1.record()
+                torch.cuda.synchronize()
+                res[name] = e0.elapsed_time(e1) * 1e3 / n
+            row = {"block_size": bs, "context": L, "contiguous_us": round(res["contiguous"], 2),
+                   "shuffled_us": round(res["shuffled"], 2),
+                   "shuffled_over_contiguous": round(res["shuffled"] / res["contiguous"], 4),
+                   "contiguous_GBps": round(per_call / res["contiguous"] / 1e3, 1),
+                   "shuffled_GBps": round(per_call / res["shuffled"] / 1e3, 1),
+                   "outputs_bitwise_equal": bool(torch.equal(outs["contiguous"], outs["shuffled"]))}
+            print(json.dumps(row), flush=True)
+            out_rows.append(row)
+            del k, v, ks, vs_
+            torch.cuda.empty_cache()
+    ratios = [r["shuffled_over_contiguous"] for r in out_rows]
+    print(json.dumps({"overhead_sweep": "paged (shuffled) / contiguous decode time",
+                      "min": min(ratios), "max": max(ratios),
+                      "mean": round(float(np.mean(ratios)), 4),
+                      "all_outputs_bitwise_equal": all(r["outputs_bitwise_equal"] for r in out_rows)}),
+          flush=True)
+
+
 def build_workload(args, dev):
     return Workload(args, dev)
 
@@ -498,6 +577,10 @@ def main():
 
     if args.stream_probe:
         print(json.dumps(stream_probe(torch)), flush=True)
+        return
+
+    if args.overhead_sweep:
+        overhead_sweep(args, torch)
         return
 
     dev = torch.device("cuda:0")

@@ -144,6 +144,33 @@ def test_physical_permutation_bitwise_invariant(spec_name):
         assert torch.equal(gpu_decode(a, part), gpu_decode(b, part))
 
 
+@pytest.mark.parametrize("bs", [8, 16, 32, 128])
+def test_contiguous_layout_matches_shuffled(bs):
+    """The paged-vs-contiguous sweep's two layouts: every sequence one
+    contiguous run of the pool, or the same logical blocks at shuffled ids.
+    Outputs are bitwise identical, and equal to the oracle within tolerance."""
+    spec = SMALL["opt13b_f16_bs16"].with_(block_size=bs, num_seqs=5)
+    lens = [1, bs - 1, 3 * bs + 5, 700, 1500]
+    ct, nb = W.contiguous_tables(lens, bs)
+    gen = W.make_generator(1181, DEV)
+    H, D = spec.num_kv_heads, spec.head_dim
+    k = W.randn(W.k_pool_shape(nb, H, bs, D, spec.dtype), spec.dtype, gen, DEV)
+    v = W.randn(W.v_pool_shape(nb, H, bs, D), spec.dtype, gen, DEV)
+    q = W.randn((len(lens), spec.num_q_heads, D), spec.dtype, gen, DEV)
+    a = W.DecodeCase(spec, np.asarray(lens, dtype=np.int32), ct, nb, q, k, v)
+    perm = np.random.default_rng(bs).permutation(nb).astype(np.int32)
+    inv = np.empty_like(perm)
+    inv[perm] = np.arange(nb, dtype=np.int32)
+    idx = torch.from_numpy(inv.astype(np.int64)).to(DEV)
+    st = np.where(ct >= 0, perm[np.maximum(ct, 0)], -1).astype(np.int32)
+    b = W.DecodeCase(spec, a.lens, st, nb, q, k.index_select(0, idx), v.index_select(0, idx))
+    log(f"[contiguous vs shuffled] bs={bs}")
+    for part in (0, -1):
+        oa = gpu_decode(a, part)
+        assert torch.equal(oa, gpu_decode(b, part))
+        assert max_err(oa, oracle_decode(a)) <= TOL[spec.dtype]
+
+
 def test_nan_in_masked_slots_does_not_leak():
     spec = SMALL["opt13b_f16_bs16"]
     a = to_dev(W.make_decode_case(spec, device=DEV, poison=True))

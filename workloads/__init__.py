@@ -127,6 +127,22 @@ def shuffled_tables(lens, block_size, rng, pool_factor=1.25, num_blocks=None, ma
     return tables, int(num_blocks)
 
 
+def contiguous_tables(lens, block_size, max_blocks=None):
+    """Identity-like tables: sequence i's logical blocks are the consecutive
+    physical ids starting after sequence i-1's, so every sequence is one
+    contiguous run of the pool (the layout a non-paged cache would have).
+    Returns (tables, num_blocks)."""
+    need = [blocks_needed(L, block_size) for L in lens]
+    if max_blocks is None:
+        max_blocks = max(1, max(need) if need else 1)
+    tables = np.full((len(lens), max_blocks), -1, dtype=np.int32)
+    cursor = 0
+    for i, n in enumerate(need):
+        tables[i, :n] = np.arange(cursor, cursor + n, dtype=np.int32)
+        cursor += n
+    return tables, max(1, cursor)
+
+
 def slots_for_positions(tables: np.ndarray, seq_pos, block_size: int) -> np.ndarray:
     """Slot of each (seq, position) pair: physical block * BS + offset."""
     out = np.empty(len(seq_pos), dtype=np.int64)
