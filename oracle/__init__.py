@@ -17,6 +17,14 @@ What each function follows (web pages on PagedAttention):
   with weights 1:2:4), numpy dense attention on identity tables, invariants
   (physical permutation, block size, NaN in masked slots, GQA == repeated MHA)
   and mutation tests.
+* ``prefill`` -- chunked prefill, section 4.2 ("Chunked Prefill的解决方案") of
+  the zhy-blog.vercel.app vLLM post: a chunk's query tokens are the last ones
+  of their sequence's context and attend causally (mask by position in the
+  whole prompt) through the block table.  Pinned by: one-token chunks equal
+  the decode oracle bit for bit; the first prompt token returns v_0; a whole
+  prompt equals numpy dense causal attention; a prompt's last tokens do not
+  depend on how the earlier part was chunked; mutation tests (no causal mask,
+  mask off by one).
 * ``reshape_and_cache`` -- slot = physical block * block_size + offset, the
   flat slot numbering of the kernel pseudocode on vkads.cloudxian.cn "vLLM
   PagedAttention源码：KV Cache".  Pinned by the one-head, one-piece special
@@ -73,6 +81,9 @@ class Oracle:
         lib.oracle_decode.restype = i32
         lib.oracle_decode.argtypes = [vp, vp, vp, vp, vp, vp, f64, i32, i32, i32, i32, i32,
                                       i32, i64, i32, i32]
+        lib.oracle_prefill.restype = i32
+        lib.oracle_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, f64, i32, i32, i32, i32, i32,
+                                       i32, i64, i32]
         lib.oracle_reshape_and_cache.restype = i32
         lib.oracle_reshape_and_cache.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i32, i32,
                                                  i32, i64, i32]
@@ -120,6 +131,31 @@ class Oracle:
                                     DTYPE_CODE[dtype], int(nthreads))
         if rc != 0:
             raise ValueError(f"oracle_decode rejected its inputs (rc={rc})")
+        return out
+
+    # -- chunked prefill -------------------------------------------------
+    def prefill(self, q, k_cache, v_cache, block_tables, context_lens, query_start, scale,
+                block_size, num_kv_heads, dtype, num_blocks=None):
+        """fp64 output [num_tokens][num_q_heads][head_dim]: sequence i's query
+        tokens query_start[i] .. query_start[i+1]-1 are the last ones of its
+        context and attend causally (see pa_oracle.c)."""
+        q = self._c(q)
+        k_cache, v_cache = self._c(k_cache), self._c(v_cache)
+        bt = self._c(np.asarray(block_tables, dtype=np.int32))
+        cl = self._c(np.asarray(context_lens, dtype=np.int32))
+        qs = self._c(np.asarray(query_start, dtype=np.int32))
+        T, hq, D = q.shape
+        if num_blocks is None:
+            num_blocks = k_cache.size // (num_kv_heads * block_size * D)
+        out = np.zeros((T, hq, D), dtype=np.float64)
+        maxb = bt.shape[1] if bt.ndim == 2 else 0
+        rc = self.lib.oracle_prefill(self._ptr(out), self._ptr(q), self._ptr(k_cache),
+                                     self._ptr(v_cache), self._ptr(bt), self._ptr(cl),
+                                     self._ptr(qs), float(scale), int(block_size),
+                                     int(num_kv_heads), int(len(cl)), int(hq), int(D), int(maxb),
+                                     int(num_blocks), DTYPE_CODE[dtype])
+        if rc != 0:
+            raise ValueError(f"oracle_prefill rejected its inputs (rc={rc})")
         return out
 
     # -- cache ops -------------------------------------------------------

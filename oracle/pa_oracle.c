@@ -280,6 +280,91 @@ int oracle_decode(double* out, const void* q, const void* k_cache, const void* v
   return rc;
 }
 
+/* Chunked-prefill oracle (zhy-blog.vercel.app vLLM post, section 4.2 "Chunked
+ * Prefill的解决方案": a prompt is processed in chunks, each chunk attends to the
+ * KV cache its predecessors wrote, and its attention mask follows the chunk's
+ * position in the whole prompt; query rows as in the forward of [P1] section 3,
+ * [num_tokens][num_heads][head_size]).
+ *
+ * Sequence i owns query tokens query_start[i] .. query_start[i+1]-1; they are
+ * the last ql_i tokens of its context, so token t sits at position
+ * p = L_i - ql_i + (t - query_start[i]) with L_i = context_lens[i] (their K/V
+ * are already in the pools).  Token t, q-head h attends causally to positions
+ * 0 .. p through the block table, one softmax over all of them (the Z / o
+ * equations of [P5] section 二 restricted to u <= p), two-pass max-subtracted
+ * form.  out: [num_tokens][num_q_heads][head_dim] doubles.  Returns 0, or -1
+ * on a malformed size / table. */
+static int prefill_one(const void* q, const void* kc, const void* vc, const int32_t* tables,
+                       double scale, int bs, int hkv, int hq, int D, int maxb, int64_t nblocks,
+                       int dtype, int64_t t, int last, int seq, int h, double* scores,
+                       double* out) {
+  int g = h / (hq / hkv);
+  const int64_t qrow = (t * hq + h) * (int64_t)D;
+  for (int d = 0; d < D; ++d) out[d] = 0.0;
+  if (last < 0) return 0;
+  if (last / bs >= maxb) return -1;
+  for (int u = 0; u <= last; ++u) {
+    int64_t blk = tables[(int64_t)seq * maxb + u / bs];
+    if (blk < 0 || blk >= nblocks) return -1;
+    double dot = 0.0;
+    for (int d = 0; d < D; ++d)
+      dot += load_elem(q, dtype, qrow + d) *
+             load_elem(kc, dtype, k_index(blk, g, u % bs, d, hkv, bs, D, k_piece(dtype)));
+    scores[u] = scale * dot;
+  }
+  double m = -INFINITY;
+  for (int u = 0; u <= last; ++u) m = scores[u] > m ? scores[u] : m;
+  double z = 0.0;
+  for (int u = 0; u <= last; ++u) {
+    scores[u] = exp(scores[u] - m);
+    z += scores[u];
+  }
+  for (int u = 0; u <= last; ++u) {
+    int64_t blk = tables[(int64_t)seq * maxb + u / bs];
+    for (int d = 0; d < D; ++d)
+      out[d] += scores[u] * load_elem(vc, dtype, v_index(blk, g, u % bs, d, hkv, bs, D));
+  }
+  for (int d = 0; d < D; ++d) out[d] /= z;
+  return 0;
+}
+
+int oracle_prefill(double* out, const void* q, const void* k_cache, const void* v_cache,
+                   const int32_t* block_tables, const int32_t* context_lens,
+                   const int32_t* query_start, double scale, int block_size, int num_kv_heads,
+                   int num_seqs, int num_q_heads, int head_dim, int max_blocks_per_seq,
+                   int64_t num_blocks, int dtype) {
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      num_q_heads % num_kv_heads != 0 || head_dim % k_piece(dtype) != 0)
+    return -1;
+  double* scores = (double*)malloc(sizeof(double) * ((size_t)max_blocks_per_seq * block_size + 1));
+  if (!scores) return -2;
+  int rc = 0;
+  for (int i = 0; i < num_seqs && rc == 0; ++i) {
+    int qs = query_start[i], ql = query_start[i + 1] - query_start[i], L = context_lens[i];
+    if (ql < 0 || ql > L) {
+      rc = -1;
+      break;
+    }
+    for (int r = 0; r < ql && rc == 0; ++r) {
+      int64_t t = (int64_t)qs + r;
+      int pos = L - ql + r; /* the token's position in its sequence */
+#if ORACLE_MUTANT == 8      /* mutant: no causal mask, every row sees the whole context */
+      int last = L - 1;
+#elif ORACLE_MUTANT == 9    /* mutant: causal mask off by one, own position excluded */
+      int last = pos - 1;
+#else
+      int last = pos;
+#endif
+      for (int h = 0; h < num_q_heads && rc == 0; ++h)
+        rc = prefill_one(q, k_cache, v_cache, block_tables, scale, block_size, num_kv_heads,
+                         num_q_heads, head_dim, max_blocks_per_seq, num_blocks, dtype, t, last,
+                         i, h, scores, out + (t * num_q_heads + h) * (int64_t)head_dim);
+    }
+  }
+  free(scores);
+  return rc;
+}
+
 /* Cache-write oracle: token t's K and V rows ([Hkv][D], token stride given in
  * elements) go to slot slot_mapping[t] = physical block * BS + offset ([P4]
  * pseudocode's flat slot numbering).  Bits are copied, no arithmetic.  A
