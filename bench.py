@@ -53,6 +53,10 @@ def parse():
                     help="only run the paged-vs-contiguous sweep: the OPT-13B-shaped decode "
                          "over one pool laid out contiguously per sequence and one with "
                          "shuffled block ids, per context length and block size")
+    ap.add_argument("--prefill", action="store_true",
+                    help="opt66b_sweep only: time chunked-prefill attention of the step's 16 "
+                         "chunk writers (256 query tokens each, causal over their whole "
+                         "context) instead of the decode step")
     ap.add_argument("--stream-probe", action="store_true",
                     help="only measure plain device read / copy bandwidth (context for peak)")
     ap.add_argument("--mfma-summary", metavar="FOLDER",
@@ -321,9 +325,13 @@ class Workload:
             tables, lens_now = a.block_tables(dec, maxb)
             return np.concatenate(slots), tables, lens_now
 
-        _, (slots, tables, lens_now) = self._alloc_step(build, step)
+        a, (slots, tables, lens_now) = self._alloc_step(build, step)
         self.lens, self.tables, self.slots, self.nb = lens_now, tables, slots, nb
         self.decode_idx = dec
+        # the chunk writers' own tables and contexts (their chunk is the last
+        # 256 positions): what chunked-prefill attention reads
+        self.writer_tables, self.writer_lens = a.block_tables(writers, maxb)
+        self.chunk = chunk
         self.config = {"workload": sp.name, "num_seqs": B, "chunk_writers": n_chunk,
                        "chunk_tokens": chunk, "decode_seqs": int(len(dec)),
                        "q_heads": sp.num_q_heads, "kv_heads": sp.num_kv_heads,
@@ -548,6 +556,60 @@ def overhead_sweep(args, torch):
           flush=True)
 
 
+def prefill_run(args, torch, wl):
+    """Chunked-prefill attention of the 66B sweep's chunk writers: 16
+    sequences x 256 query tokens, each causal over its whole context, timed as
+    back-to-back pa_prefill calls on the stream (pools replicated as for the
+    decode step).  Algorithmic flops: q.k and p.v, 4 D per (query, q head,
+    visible key); bytes: the K/V of every writer's context, read once."""
+    pa, W, sp = wl.pa, wl.W, wl.spec
+    dev = wl.dev
+    B, H, D = len(wl.writer_lens), sp.num_q_heads, sp.head_dim
+    ql = wl.chunk
+    T = B * ql
+    gen = W.make_generator(sp.seed + 99, dev)
+    q = W.randn((T, H, D), sp.dtype, gen, dev)
+    out = torch.empty_like(q)
+    qs = torch.arange(0, T + 1, ql, dtype=torch.int32, device=dev)
+    tables = torch.from_numpy(wl.writer_tables).to(dev)
+    lens = torch.from_numpy(wl.writer_lens).to(dev)
+    maxctx = int(wl.writer_lens.max())
+
+    def call(r):
+        pa.pa_prefill(out, q, wl.k[r], wl.v[r], tables, lens, qs, sp.scale, sp.block_size,
+                      sp.num_kv_heads, ql, maxctx)
+    for i in range(args.warmup):
+        call(i % wl.replicas)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        call(i % wl.replicas)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    ctx = wl.writer_lens.astype(np.int64)
+    visible = float(np.sum([np.sum(np.arange(L - ql + 1, L + 1)) for L in ctx]))
+    flops = 4.0 * D * H * visible
+    kv_bytes = int(ctx.sum()) * wl._tok_bytes()
+    peak = MFMA_PEAK_TFLOPS[wl.dtype]
+    tflops = flops / (ms / 1e3) / 1e12
+    rec = {
+        "metric": "chunked_prefill_attention_TFLOPs", "value": round(tflops, 2),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_call": round(ms, 5), "higher_is_better": True, "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": "opt66b_sweep chunk writers", "seqs": B, "query_tokens": ql,
+                   "q_heads": H, "kv_heads": sp.num_kv_heads, "head_dim": D,
+                   "block_size": sp.block_size, "contexts": [int(x) for x in ctx]},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": None},
+        "kv_bytes_per_call": kv_bytes,
+        "kv_GBps_if_read_once": round(kv_bytes / (ms / 1e3) / 1e9, 1),
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def build_workload(args, dev):
     return Workload(args, dev)
 
@@ -586,6 +648,12 @@ def main():
     dev = torch.device("cuda:0")
     wl = build_workload(args, dev)
     torch.cuda.synchronize()
+    if args.prefill:
+        if args.workload != "opt66b_sweep":
+            print(json.dumps({"error": "--prefill needs --workload opt66b_sweep"}))
+            sys.exit(2)
+        prefill_run(args, torch, wl)
+        return
 
     for i in range(args.warmup):
         wl.step(i % wl.replicas)

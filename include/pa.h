@@ -140,6 +140,36 @@ int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t 
                                  int32_t partition_size, pa_dtype dtype);
 
 /* ------------------------------------------------------------------------
+ * pa_prefill -- chunked-prefill attention over the paged cache.
+ *
+ * A prompt processed in chunks (zhy-blog.vercel.app, vLLM post, section 4.2
+ * "Chunked Prefill的解决方案"): sequence b's query tokens query_start[b] ..
+ * query_start[b+1]-1 are the last ql_b of its L_b = context_lens[b] positions,
+ * already written to the pools (pa_reshape_and_cache), so the token at index
+ * r of the chunk sits at position p = L_b - ql_b + r.  Token p, q head h
+ * attends to positions 0 .. p only (the mask follows the token's place in the
+ * whole prompt) through the block table, with one softmax over all of them
+ * ([P5] section 二, restricted to u <= p); kv head h / (Hq / Hkv).  fp32
+ * accumulation; output rounded to nearest-even in `dtype`.
+ *
+ *  out, q        [num_tokens][num_q_heads][head_dim] of dtype (device); rows
+ *                packed as in [P1] section 3's forward
+ *  query_start   [num_seqs + 1] int32 (device): query_start[0] = 0, non-
+ *                decreasing; ql_b = query_start[b+1] - query_start[b] must not
+ *                exceed max_query_len nor L_b (rows of a sequence with
+ *                ql_b > L_b are left unwritten)
+ *  block_tables, context_lens, pools, scale: as pa_decode
+ * Supported: f16 / bf16, head_dim 64 or 128, block_size 8, 16 or a multiple
+ * of 32 (PA_ENOTSUP otherwise).  No workspace.
+ * ---------------------------------------------------------------------- */
+pa_status pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* block_tables, const int32_t* context_lens,
+                     const int32_t* query_start, float scale, int32_t block_size,
+                     int32_t num_kv_heads, int32_t num_seqs, int32_t num_q_heads,
+                     int32_t head_dim, int32_t max_blocks_per_seq, int32_t max_query_len,
+                     int32_t max_context_len, int64_t num_blocks, pa_dtype dtype, void* stream);
+
+/* ------------------------------------------------------------------------
  * pa_reshape_and_cache -- write new tokens' K and V rows into their slots.
  *
  * Token t (row k[t*k_token_stride ...], [num_kv_heads][head_dim] contiguous,

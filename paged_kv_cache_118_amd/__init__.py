@@ -40,6 +40,8 @@ def _load():
                             i32, i32, vp, sz, vp]),
         "pa_decode_workspace_bytes": (sz, [i32, i32, i32, i32, i32, i32, i32, i32]),
         "pa_decode_partition_size": (i32, [i32, i32, i32, i32, i32, i32, i32, i32]),
+        "pa_prefill": (i32, [vp, vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, i32, i32, i32, i32,
+                             i32, i64, i32, vp]),
         "pa_reshape_and_cache": (i32, [vp, vp, vp, vp, vp, i32, i64, i64, i32, i32, i32, i64,
                                        i32, vp]),
         "pa_copy_blocks": (i32, [vp, vp, vp, i32, i32, i32, i32, i64, i32, vp]),
@@ -66,6 +68,7 @@ _lib = _load()
 
 # every symbol include/pa.h declares (checked by the CPU test suite)
 EXPORTED = ("pa_strerror", "pa_decode", "pa_decode_workspace_bytes", "pa_decode_partition_size",
+            "pa_prefill",
             "pa_reshape_and_cache", "pa_copy_blocks", "pa_alloc_create", "pa_alloc_destroy",
             "pa_alloc_add_seq", "pa_alloc_fork", "pa_alloc_append", "pa_alloc_free_seq",
             "pa_alloc_block_tables", "pa_alloc_num_free", "pa_alloc_refcount",
@@ -194,6 +197,34 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, block
                           _dev_ptr(context_lens, "context_lens"), float(scale), block_size,
                           num_kv_heads, B, hq, D, block_tables.shape[1], int(max_context_len),
                           nb, dt, int(partition_size), ws_ptr, ws_len, _stream(stream)))
+    return out
+
+
+def pa_prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start, scale,
+               block_size, num_kv_heads, max_query_len, max_context_len, stream=None):
+    """Chunked-prefill attention (see pa.h): q / out [num_tokens, Hq, D];
+    sequence b's query rows are query_start[b] .. query_start[b+1]-1 (int32
+    device tensor of num_seqs + 1), the last ones of its context."""
+    T, hq, D = q.shape
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q in shape and dtype")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("pools must have q's dtype")
+    nb = _check_pools(k_cache, v_cache, num_kv_heads, block_size, D)
+    B = context_lens.shape[0]
+    for name, t, shape in (("block_tables", block_tables, None), ("context_lens", context_lens,
+                                                                   (B,)),
+                           ("query_start", query_start, (B + 1,))):
+        if t.dtype != torch.int32 or (shape is not None and tuple(t.shape) != shape):
+            raise ValueError(f"{name} must be int32 of the right shape")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [num_seqs, max_blocks]")
+    _check(_lib.pa_prefill(_dev_ptr(out, "out"), _dev_ptr(q, "q"), _dev_ptr(k_cache, "k_cache"),
+                           _dev_ptr(v_cache, "v_cache"), _dev_ptr(block_tables, "block_tables"),
+                           _dev_ptr(context_lens, "context_lens"),
+                           _dev_ptr(query_start, "query_start"), float(scale), block_size,
+                           num_kv_heads, B, hq, D, block_tables.shape[1], int(max_query_len),
+                           int(max_context_len), nb, _dtype_code(q), _stream(stream)))
     return out
 
 

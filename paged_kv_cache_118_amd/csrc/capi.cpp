@@ -258,6 +258,65 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   return hip_status(e);
 }
 
+pa_status pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* block_tables, const int32_t* context_lens,
+                     const int32_t* query_start, float scale, int32_t block_size,
+                     int32_t num_kv_heads, int32_t num_seqs, int32_t num_q_heads,
+                     int32_t head_dim, int32_t max_blocks_per_seq, int32_t max_query_len,
+                     int32_t max_context_len, int64_t num_blocks, pa_dtype dtype, void* stream) {
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      block_size <= 0 || max_blocks_per_seq < 0 || max_query_len < 0 || max_context_len < 0 ||
+      num_blocks <= 0)
+    return PA_EINVAL;
+  if (!dtype_ok(dtype)) return PA_ENOTSUP;
+  if (num_q_heads % num_kv_heads != 0 || !std::isfinite(scale)) return PA_EINVAL;
+  if (!prefill_supported(dtype, head_dim, block_size)) return PA_ENOTSUP;
+  if (num_seqs == 0 || max_query_len == 0) return PA_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start)
+    return PA_EINVAL;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    return PA_EINVAL;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int len_cap = (int)std::min<int64_t>((int64_t)max_context_len,
+                                             (int64_t)max_blocks_per_seq * block_size);
+  if (validate_enabled()) {
+    std::vector<int32_t> lens, tab, qs;
+    if (!copy_to_host(lens, context_lens, (size_t)num_seqs, s)) return PA_EHIP;
+    if (!copy_to_host(qs, query_start, (size_t)num_seqs + 1, s)) return PA_EHIP;
+    if (!copy_to_host(tab, block_tables, (size_t)num_seqs * max_blocks_per_seq, s))
+      return PA_EHIP;
+    if (qs[0] != 0) return PA_EVALIDATE;
+    for (int b = 0; b < num_seqs; ++b) {
+      const int ql = qs[b + 1] - qs[b];
+      if (ql < 0 || ql > max_query_len || lens[b] < ql || lens[b] > len_cap) return PA_EVALIDATE;
+      const int nb = (lens[b] + block_size - 1) / block_size;
+      for (int j = 0; j < nb; ++j) {
+        const int32_t e = tab[(size_t)b * max_blocks_per_seq + j];
+        if (e < 0 || e >= num_blocks) return PA_EVALIDATE;
+      }
+    }
+  }
+  PrefillArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.query_start = query_start;
+  a.scale_log2e = scale * 1.4426950408889634f;
+  a.block_size = block_size;
+  a.num_kv_heads = num_kv_heads;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.head_dim = head_dim;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.max_query_len = max_query_len;
+  a.len_cap = len_cap;
+  a.num_blocks = num_blocks;
+  return hip_status(launch_prefill(a, dtype, s));
+}
+
 pa_status pa_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,
                                const int64_t* slot_mapping, int32_t num_tokens,
                                int64_t k_token_stride, int64_t v_token_stride,

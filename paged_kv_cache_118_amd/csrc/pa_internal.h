@@ -92,6 +92,30 @@ struct DecodeArgs {
   int32_t* ws_ppre;     // [B+1] partition prefix per sequence (part_steps > 0)
 };
 
+// ----------------------------------------------------------- prefill args --
+struct PrefillArgs {
+  void* out;                   // [num_tokens][num_q_heads][head_dim]
+  const void* q;               // [num_tokens][num_q_heads][head_dim]
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* query_start;  // [num_seqs + 1]
+  float scale_log2e;
+  int32_t block_size;
+  int32_t num_kv_heads;
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t head_dim;
+  int32_t max_blocks_per_seq;
+  int32_t max_query_len;
+  int32_t len_cap;             // min(max_context_len, max_blocks_per_seq * block_size)
+  int64_t num_blocks;
+};
+
+hipError_t launch_prefill(const PrefillArgs& a, pa_dtype dt, hipStream_t s);
+bool prefill_supported(pa_dtype dt, int head_dim, int block_size);
+
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_decode_valu(const DecodeArgs& a, pa_dtype dt, hipStream_t s);
 hipError_t launch_decode_mfma(const DecodeArgs& a, pa_dtype dt, hipStream_t s);

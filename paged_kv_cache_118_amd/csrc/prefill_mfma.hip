@@ -1,0 +1,286 @@
+// Paged chunked-prefill attention on the gfx950 matrix cores.
+//
+// A prompt processed in chunks (zhy-blog.vercel.app vLLM post, section 4.2
+// "Chunked Prefill的解决方案"): the chunk's query tokens are the last ql tokens
+// of their sequence's context (their K/V already written to the pool), and
+// each attends to the cache through the block table with a mask set by its
+// position in the whole prompt: token at position p sees positions 0 .. p.
+// One softmax over all of them (the Z / o equations of wq-win.github.io "079 |
+// vLLM 与 PagedAttention", section 二), evaluated online in the base-2 domain.
+// Query rows are packed [num_tokens][num_q_heads][head_dim] as in the forward
+// of gitcode.csdn.net "vLLM 推理引擎：PagedAttention 与 KVCache 管理", section 3.
+//
+// Unlike decode, each K/V element now meets many queries, so the work is a
+// real dense contraction.  A wavefront owns 16 query rows of one q head; a
+// workgroup holds four consecutive 16-row tiles of the same head, and all
+// workgroups reading one kv head's K/V run on one XCD at about the same
+// time, so the cache lines of a key group come from HBM about once and are
+// served to the others from L2 (plain, temporal loads).  With lane = 16*kb + n and v_mfma_f32_16x16x32:
+//   S^T = K Q^T  : A = 16 keys x 32 dims (16-byte K pieces, as in decode),
+//                  B = Q^T (query row n), two 16-key tiles per 32-key group;
+//                  lane (n, kb) gets query n's scores of keys 4kb .. 4kb+3
+//                  and 16+4kb .. 16+4kb+3.
+//   O^T += V^T P^T : A = 16 dims x 32 keys (one 16-byte row of an 8-token V
+//                  slab per k-group), B = P^T gathered with four lane permutes.
+// The mask compares each key's position with the lane's query position, so
+// only the groups that reach past the tile's first row pay for it.
+#include <math.h>
+
+#include "pa_internal.h"
+
+namespace pa {
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRows = 16;  // query rows per wavefront
+constexpr int kKeys = 32;  // keys per step
+
+__device__ __forceinline__ uint4 ld16(const char* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+
+__device__ __forceinline__ float4_t mfma(F16, const uint4& a, const uint4& b, float4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a),
+                                                __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ float4_t mfma(BF16, const uint4& a, const uint4& b, float4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf168_t, a),
+                                                 __builtin_bit_cast(bf168_t, b), c, 0, 0, 0);
+}
+template <typename TT>
+__device__ __forceinline__ uint32_t pack2(TT t, float lo, float hi) {
+  return (uint32_t)to_bits(t, lo) | ((uint32_t)to_bits(t, hi) << 16);
+}
+
+// Lane i holds the physical id of logical block base + i (0 for entries past
+// the row or outside the pool: such blocks only feed masked keys).
+struct TableWindow {
+  int base = 0x7fffffff;
+  int entry = 0;
+  __device__ __forceinline__ void ensure(const int32_t* row, int nblk, int64_t num_blocks, int lb,
+                                         int n, int lane) {
+    if (lb < base || lb + n - base > 64) {
+      base = lb;
+      const int idx = lb + lane;
+      const int e = idx < nblk ? row[idx] : 0;
+      entry = (e < 0 || (int64_t)e >= num_blocks) ? 0 : e;
+    }
+  }
+  __device__ __forceinline__ int get(int lb) const {
+    return __builtin_amdgcn_readlane(entry, lb - base);
+  }
+};
+
+template <typename TT, int D>
+__global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
+  constexpr int VS = 8;       // V slab width (tokens)
+  constexpr int EB = 2;
+  constexpr int KN = D / 32;  // k-steps of S^T
+  constexpr int MT = D / 16;  // d tiles of O^T
+  constexpr int NC = D / 8;   // 16-byte K pieces per token
+
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15, kb = lane >> 4;
+  const int G = a.num_q_heads / a.num_kv_heads;
+  // XCD-aware order: workgroups are dealt to the 8 XCDs round-robin by id, so
+  // every workgroup of one (sequence, kv head) unit -- its q heads and query
+  // tiles, which read the same K/V -- gets ids of one residue mod 8 (the same
+  // XCD and L2) and consecutive in time.
+  const int tpg = (a.max_query_len + kWaves * kRows - 1) / (kWaves * kRows);
+  const int sub_n = G * tpg;  // workgroups per unit
+  const int id = blockIdx.x;
+  const int unit = (id / 8 / sub_n) * 8 + id % 8;
+  const int sub = (id / 8) % sub_n;
+  if (unit >= a.num_seqs * a.num_kv_heads) return;
+  const int seq = unit / a.num_kv_heads;
+  const int h = (unit % a.num_kv_heads) * G + sub / tpg;
+  const int tile = (sub % tpg) * kWaves + wv;
+  const int qs = a.query_start[seq];
+  const int ql = a.query_start[seq + 1] - qs;
+  int L = a.context_lens[seq];
+  L = L < 0 ? 0 : (L > a.len_cap ? a.len_cap : L);
+  const int r0 = tile * kRows;
+  if (ql <= 0 || ql > L || r0 >= ql) return;  // (ql > L is a caller error: rows left alone)
+  const int nrows = ql - r0 < kRows ? ql - r0 : kRows;
+  const int pos0 = L - ql + r0;          // position of the tile's first row
+  const int last = pos0 + nrows - 1;     // position of its last valid row
+  const int mypos = pos0 + (n < nrows ? n : nrows - 1);  // this lane's query position
+  const int64_t g = h / G;
+  const int64_t hkv = a.num_kv_heads;
+  const int bs = a.block_size;
+  const int nb_grp = bs >= kKeys ? 1 : kKeys / bs;  // blocks one group touches
+
+  const char* kbase = reinterpret_cast<const char*>(a.k_cache);
+  const char* vbase = reinterpret_cast<const char*>(a.v_cache);
+  const char* qbase = reinterpret_cast<const char*>(a.q);
+  const int32_t* trow = a.block_tables + (int64_t)seq * a.max_blocks_per_seq;
+
+  // Q^T operand: query row n of the tile, dims 32 s + 8 kb .. +7 (zero for
+  // rows past the chunk).
+  uint4 qr[KN];
+  {
+    const int64_t row = (int64_t)qs + r0 + (n < nrows ? n : 0);
+    const char* qp = qbase + ((row * a.num_q_heads + h) * D + kb * 8) * EB;
+#pragma unroll
+    for (int s = 0; s < KN; ++s) qr[s] = n < nrows ? ld16(qp + 64 * s) : make_uint4(0, 0, 0, 0);
+  }
+  const char* cached = qbase + ((int64_t)qs * a.num_q_heads + h) * D * EB +
+                       ((lane * 16) & (D * EB - 1));  // bytes this wavefront holds in cache
+
+  float m_run = -INFINITY, l_lane = 0.f;
+  float4_t acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  TableWindow tw;
+  const int64_t pstride = (int64_t)4 * bs * 16;  // bytes from K piece p to p + 4
+  const int ngroups = last / kKeys + 1;
+  // One group at a time: a second (prefetch) register set measured slower
+  // (it costs occupancy); the other resident wavefronts cover the latency.
+  for (int grp = 0; grp < ngroups; ++grp) {
+    const int tok = grp * kKeys;
+    const int nv = last + 1 - tok;  // keys of the group at positions <= last (>= 1)
+    const int lb0 = tok / bs;
+    tw.ensure(trow, a.max_blocks_per_seq, a.num_blocks, lb0, nb_grp, lane);
+    // K: two 16-key tiles; lane (n, kb) loads key 16 j + n, pieces kb + 4 i.
+    uint4 kr[2][KN];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const bool live = 16 * j < nv;
+      const int t = tok + 16 * j + (16 * j + n < nv ? n : 0);
+      const int lb = t / bs;
+      int64_t phys = tw.get(lb0);
+      for (int q = 1; q < nb_grp; ++q)
+        if (lb == lb0 + q) phys = tw.get(lb0 + q);
+      const char* kp = kbase + (((phys * hkv + g) * NC + kb) * bs + (t - lb * bs)) * 16;
+#pragma unroll
+      for (int i = 0; i < KN; ++i) kr[j][i] = ld16(live ? kp + i * pstride : cached);
+    }
+    // V: the 8-token run of k-group kb, one 16-byte slab row per d tile.
+    uint4 vr[MT];
+    {
+      const bool run = kb * 8 < nv;
+      const int t = tok + kb * 8;
+      const int lb = t / bs;
+      int64_t phys = tw.get(lb0);
+      for (int q = 1; q < nb_grp; ++q)
+        if (lb == lb0 + q) phys = tw.get(lb0 + q);
+      const int off = t - lb * bs;
+      const char* vp = vbase + ((((phys * hkv + g) * (bs / VS) + off / VS) * D + n) * VS) * EB;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        vr[mt] = ld16(run ? vp + (int64_t)mt * 16 * VS * EB : cached);
+    }
+
+    float4_t st[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      st[j] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < KN; ++i) st[j] = mfma(TT{}, kr[j][i], qr[i], st[j]);
+    }
+    float sc[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sc[e] = st[0][e] * a.scale_log2e;
+      sc[4 + e] = st[1][e] * a.scale_log2e;
+    }
+    if (tok + kKeys - 1 > pos0) {  // the group reaches past the tile's first row
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {  // key of sc[e]: 4 kb + e, then 16 + 4 kb + e - 4
+        const int u = tok + (e < 4 ? 4 * kb + e : 12 + 4 * kb + e);
+        if (u > mypos) sc[e] = -INFINITY;  // select: keys past `last` may be NaN
+      }
+    }
+    float mx = sc[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sc[e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);  // finite: key 0 is in every row's range
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    float pw[8], psum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      pw[e] = __builtin_amdgcn_exp2f(sc[e] - m_new);
+      psum += pw[e];
+    }
+    l_lane = l_lane * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] *= alpha;
+    // P^T operand: lane kb needs keys 8 kb .. 8 kb + 7 of query n, the 4-key
+    // runs of tile kb / 2 held by k-groups 2 (kb % 2) and 2 (kb % 2) + 1.
+    const uint32_t t0a = pack2(TT{}, pw[0], pw[1]), t0b = pack2(TT{}, pw[2], pw[3]);
+    const uint32_t t1a = pack2(TT{}, pw[4], pw[5]), t1b = pack2(TT{}, pw[6], pw[7]);
+    const bool ev = (kb & 1) == 0;
+    const int p1 = ((kb & 1) << 1) | (kb >> 1);
+    const int src1 = (n + 16 * p1) * 4, src2 = (n + 16 * (p1 ^ 1)) * 4;
+    const uint32_t a0 = __builtin_amdgcn_ds_bpermute(src1, ev ? t0a : t1a);
+    const uint32_t a1 = __builtin_amdgcn_ds_bpermute(src1, ev ? t0b : t1b);
+    const uint32_t b0 = __builtin_amdgcn_ds_bpermute(src2, ev ? t1a : t0a);
+    const uint32_t b1 = __builtin_amdgcn_ds_bpermute(src2, ev ? t1b : t0b);
+    const uint4 pb = kb < 2 ? make_uint4(a0, a1, b0, b1) : make_uint4(b0, b1, a0, a1);
+    if (nv < kKeys) {  // zero V of keys past `last` (their bits may be NaN)
+      const int keep = min(max(nv - kb * 8, 0), 8);
+      uint32_t m4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        m4[i] = ((2 * i < keep) ? 0xffffu : 0u) | ((2 * i + 1 < keep) ? 0xffff0000u : 0u);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        vr[mt].x &= m4[0];
+        vr[mt].y &= m4[1];
+        vr[mt].z &= m4[2];
+        vr[mt].w &= m4[3];
+      }
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma(TT{}, vr[mt], pb, acc[mt]);
+  }
+
+  float l_tot = l_lane + __shfl_xor(l_lane, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+  if (n < nrows) {
+    const float inv = 1.f / l_tot;
+    uint16_t* out = reinterpret_cast<uint16_t*>(a.out) +
+                    (((int64_t)qs + r0 + n) * a.num_q_heads + h) * D + 4 * kb;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) out[mt * 16 + e] = to_bits(TT{}, acc[mt][e] * inv);
+  }
+}
+
+template <typename TT, int D>
+hipError_t launch_d(const PrefillArgs& a, hipStream_t s) {
+  const int64_t tpg = (a.max_query_len + kWaves * kRows - 1) / (kWaves * kRows);
+  const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads;
+  const int64_t wgs = (units + 7) / 8 * 8 * (a.num_q_heads / a.num_kv_heads) * tpg;
+  if (wgs > 0x7fffffff) return hipErrorInvalidValue;
+  dim3 grid((unsigned)wgs);
+  hipLaunchKernelGGL((prefill_mfma_kernel<TT, D>), grid, dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool prefill_supported(pa_dtype dt, int head_dim, int block_size) {
+  const bool dt_ok = dt == PA_F16 || dt == PA_BF16;
+  const bool d_ok = head_dim == 64 || head_dim == 128;
+  const bool bs_ok = block_size == 8 || block_size == 16 || (block_size % 32 == 0);
+  return dt_ok && d_ok && bs_ok;
+}
+
+hipError_t launch_prefill(const PrefillArgs& a, pa_dtype dt, hipStream_t s) {
+  if (a.num_seqs == 0 || a.max_query_len == 0) return hipSuccess;
+  if (dt == PA_F16) return a.head_dim == 64 ? launch_d<F16, 64>(a, s) : launch_d<F16, 128>(a, s);
+  if (dt == PA_BF16)
+    return a.head_dim == 64 ? launch_d<BF16, 64>(a, s) : launch_d<BF16, 128>(a, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa

@@ -88,3 +88,43 @@ def test_full_size_step_parity(name, bs):
     err = max_err(wl.out, want, seqs=seqs)
     log(f"  sequences {seqs}: max abs err {err:.3e} (tol {TOL[sp.dtype]})")
     assert err <= TOL[sp.dtype]
+
+
+@pytest.mark.parametrize("bs", [16, 128])
+def test_full_size_chunked_prefill_parity(bs):
+    """The 66B sweep's 16 chunk writers (256 query tokens each, causal over
+    contexts up to 8448 tokens), launched as ``bench.py --prefill`` does, after
+    the step wrote the chunks: the last 3 query rows of three writers (every
+    q head) against the fp64 oracle on those rows alone."""
+    import oracle
+    import paged_kv_cache_118_amd as pa
+    log(f"[full size] opt66b_sweep chunked prefill block_size={bs}")
+    wl = _workload("opt66b_sweep", bs)
+    sp = wl.spec
+    torch.cuda.synchronize()
+    wl.step(0)
+    ql = wl.chunk
+    B = len(wl.writer_lens)
+    T = B * ql
+    gen = W.make_generator(sp.seed + 99, DEV)
+    q = W.randn((T, sp.num_q_heads, sp.head_dim), sp.dtype, gen, DEV)
+    out = torch.empty_like(q)
+    qs = torch.arange(0, T + 1, ql, dtype=torch.int32, device=DEV)
+    pa.pa_prefill(out, q, wl.k[0], wl.v[0], torch.from_numpy(wl.writer_tables).to(DEV),
+                  torch.from_numpy(wl.writer_lens).to(DEV), qs, sp.scale, sp.block_size,
+                  sp.num_kv_heads, ql, int(wl.writer_lens.max()))
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    lens = wl.writer_lens
+    rows = 3
+    for s in sorted({0, int(np.argmax(lens)), int(np.argmin(lens))}):
+        case = W.DecodeCase(sp, lens[s:s + 1].copy(), wl.writer_tables[s:s + 1].copy(), wl.nb,
+                            q, wl.k[0], wl.v[0])
+        from tests.gpu_util import subset_for_oracle
+        _, kb, vb, t, _ = subset_for_oracle(case, [0])
+        qrows = W.to_numpy_bits(q[(s + 1) * ql - rows:(s + 1) * ql])
+        want = oracle.get().prefill(qrows, kb, vb, t, lens[s:s + 1], np.array([0, rows], np.int32),
+                                    sp.scale, sp.block_size, sp.num_kv_heads, sp.dtype)
+        err = max_err(out[(s + 1) * ql - rows:(s + 1) * ql], want)
+        log(f"  writer {s} (context {int(lens[s])}): max abs err {err:.3e}")
+        assert err <= TOL[sp.dtype]
