@@ -57,6 +57,10 @@ def parse():
                     help="opt66b_sweep only: time chunked-prefill attention of the step's 16 "
                          "chunk writers (256 query tokens each, causal over their whole "
                          "context) instead of the decode step")
+    ap.add_argument("--swap", action="store_true",
+                    help="only time pa_swap_blocks: half of the workload's blocks out to a "
+                         "pinned host pool and back, against a plain device-to-host copy "
+                         "of the same bytes")
     ap.add_argument("--stream-probe", action="store_true",
                     help="only measure plain device read / copy bandwidth (context for peak)")
     ap.add_argument("--mfma-summary", metavar="FOLDER",
@@ -610,6 +614,60 @@ def prefill_run(args, torch, wl):
     print(json.dumps(rec), flush=True)
 
 
+def swap_run(args, torch, wl):
+    """Swap of half of the workload's pool blocks (seeded choice) to a pinned
+    host pool and back to other device ids, each direction timed over
+    back-to-back calls; the byte count is K + V of every moved block.  Context:
+    torch's own copy of the same number of contiguous bytes to pinned memory."""
+    pa, W, sp = wl.pa, wl.W, wl.spec
+    dev = wl.dev
+    nb = wl.nb
+    n = nb // 2
+    rng = np.random.default_rng(sp.seed + 5)
+    src = rng.choice(nb, size=n, replace=False)
+    host_ids = rng.permutation(n)
+    back = rng.choice(nb, size=n, replace=False)
+    hk = torch.empty((n,) + tuple(wl.k[0].shape[1:]), dtype=wl.k[0].dtype, pin_memory=True)
+    hv = torch.empty((n,) + tuple(wl.v[0].shape[1:]), dtype=wl.v[0].dtype, pin_memory=True)
+    out_pairs = torch.from_numpy(np.stack([src, host_ids], 1).astype(np.int64)).to(dev)
+    in_pairs = torch.from_numpy(np.stack([host_ids, back], 1).astype(np.int64)).to(dev)
+    k2, v2 = torch.empty_like(wl.k[0]), torch.empty_like(wl.v[0])
+    moved = 2 * n * wl.k[0][0].numel() * wl.k[0].element_size()
+    res = {}
+    for name, fn in (("swap_out", lambda: pa.pa_swap_blocks(wl.k[0], wl.v[0], hk, hv, out_pairs,
+                                                            sp.block_size)),
+                     ("swap_in", lambda: pa.pa_swap_blocks(hk, hv, k2, v2, in_pairs,
+                                                           sp.block_size))):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = max(3, args.steps // 10)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        res[name] = {"ms": round(ms, 4), "GBps": round(moved / (ms / 1e3) / 1e9, 2)}
+    ok = bool(torch.equal(k2[torch.from_numpy(back).to(dev)],
+                          wl.k[0][torch.from_numpy(src).to(dev)]))
+    flat = wl.k[0].view(-1)[: moved // wl.k[0].element_size()]
+    hflat = torch.empty(flat.numel(), dtype=flat.dtype, pin_memory=True)
+    hflat.copy_(flat, non_blocking=True)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(3):
+        hflat.copy_(flat, non_blocking=True)
+    e1.record()
+    torch.cuda.synchronize()
+    d2h = moved / (e0.elapsed_time(e1) / 3 / 1e3) / 1e9
+    print(json.dumps({"metric": "swap_blocks_GBps", "workload": args.workload,
+                      "blocks_moved": int(n), "bytes_moved": int(moved),
+                      "block_bytes": int(moved // n), **res, "round_trip_bitwise_ok": ok,
+                      "torch_contiguous_d2h_GBps": round(d2h, 2)}), flush=True)
+
+
 def build_workload(args, dev):
     return Workload(args, dev)
 
@@ -648,6 +706,9 @@ def main():
     dev = torch.device("cuda:0")
     wl = build_workload(args, dev)
     torch.cuda.synchronize()
+    if args.swap:
+        swap_run(args, torch, wl)
+        return
     if args.prefill:
         if args.workload != "opt66b_sweep":
             print(json.dumps({"error": "--prefill needs --workload opt66b_sweep"}))

@@ -189,6 +189,28 @@ pa_status pa_reshape_and_cache(const void* k, const void* v, void* k_cache, void
                                int64_t num_blocks, pa_dtype dtype, void* stream);
 
 /* ------------------------------------------------------------------------
+ * pa_swap_blocks -- move whole blocks between two pools of the same layout,
+ * typically the device pool and a pinned host pool: the swap that preempts a
+ * sequence group when device memory runs short and brings its cache back
+ * later (deepinsea.top, "PagedAttention 内存管理深度解析", part "Swap 机制";
+ * [P5] section 三, the swap-out / swap-in steps of each iteration).
+ *
+ * For each pair p, every byte of block src_dst_pairs[2p] of (src_k, src_v)
+ * (all heads, all BS slots) is copied to block src_dst_pairs[2p+1] of
+ * (dst_k, dst_v), on `stream`, by a kernel that reads and writes through the
+ * pointers.  Every pointer must therefore be device memory or pinned host
+ * memory mapped at the same address (e.g. hipHostMalloc, torch pin_memory);
+ * anything else, such as pageable host memory, is PA_EINVAL and nothing runs.
+ * Destinations must be distinct.  Pairs with an id outside its pool are
+ * skipped (PA_VALIDATE=1: PA_EVALIDATE).
+ *  src_dst_pairs  [num_pairs][2] int64, device or pinned host memory
+ * ---------------------------------------------------------------------- */
+pa_status pa_swap_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
+                         const int64_t* src_dst_pairs, int32_t num_pairs, int64_t src_num_blocks,
+                         int64_t dst_num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, pa_dtype dtype, void* stream);
+
+/* ------------------------------------------------------------------------
  * pa_copy_blocks -- copy-on-write of whole blocks ([P5] section 二, part
  * "共享与写时复制"; [P1] / [P3] copy-on-write).
  *

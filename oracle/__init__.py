@@ -34,6 +34,11 @@ What each function follows (web pages on PagedAttention):
 * ``copy_blocks`` -- copy-on-write of whole blocks, section 二 "共享与写时复制"
   of the wq-win page.  Pinned by byte identity of the copied block, untouched
   bytes elsewhere, and decode through the copy.
+* ``swap_blocks`` -- whole-block copies between two pools (device and host),
+  the "Swap 机制" part of deepinsea.top "PagedAttention 内存管理深度解析".
+  Pinned by byte identity of every moved block, untouched bytes elsewhere in
+  the destination, and a swap-out / swap-in round trip that restores the
+  original pool's blocks at new ids.
 * ``alloc_ref.BlockPool`` -- ref-counted pool per section 三 of the wq-win page
   and the BlockManager of deepinsea.top "PagedAttention 内存管理深度解析".
   Pinned by the two worked allocation examples of the wq-win page (stored in
@@ -89,6 +94,8 @@ class Oracle:
                                                  i32, i64, i32]
         lib.oracle_copy_blocks.restype = i32
         lib.oracle_copy_blocks.argtypes = [vp, vp, vp, i32, i32, i32, i32, i64, i32]
+        lib.oracle_swap_blocks.restype = i32
+        lib.oracle_swap_blocks.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i32, i32, i32, i32]
         lib.oracle_half_to_double.restype = f64
         lib.oracle_half_to_double.argtypes = [ctypes.c_uint16]
         lib.oracle_bf16_to_double.restype = f64
@@ -186,6 +193,20 @@ class Oracle:
                                          DTYPE_CODE[dtype])
         if rc != 0:
             raise ValueError(f"oracle_copy_blocks rejected its inputs (rc={rc})")
+
+
+    def swap_blocks(self, src_k, src_v, dst_k, dst_v, pairs, num_kv_heads, head_dim, block_size,
+                    dtype):
+        """Writes into ``dst_k`` / ``dst_v`` in place (numpy arrays)."""
+        p = self._c(np.asarray(pairs, dtype=np.int64).reshape(-1, 2))
+        per = num_kv_heads * block_size * head_dim
+        rc = self.lib.oracle_swap_blocks(self._ptr(self._c(src_k)), self._ptr(self._c(src_v)),
+                                         self._ptr(self._c(dst_k)), self._ptr(self._c(dst_v)),
+                                         self._ptr(p), int(p.shape[0]), int(src_k.size // per),
+                                         int(dst_k.size // per), int(num_kv_heads), int(head_dim),
+                                         int(block_size), DTYPE_CODE[dtype])
+        if rc != 0:
+            raise ValueError(f"oracle_swap_blocks rejected its inputs (rc={rc})")
 
 
 _default: Oracle | None = None

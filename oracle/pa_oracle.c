@@ -419,6 +419,33 @@ int oracle_copy_blocks(void* k_cache, void* v_cache, const int64_t* src_dst_pair
   return 0;
 }
 
+/* Swap oracle (deepinsea.top "PagedAttention 内存管理深度解析", "Swap 机制"):
+ * for each (src, dst) pair every element of block src of the source pools is
+ * copied to block dst of the destination pools, in pair order.  Bits only.
+ * Returns -1 for an id beyond its pool. */
+int oracle_swap_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
+                       const int64_t* src_dst_pairs, int num_pairs, int64_t src_blocks,
+                       int64_t dst_blocks, int num_kv_heads, int head_dim, int block_size,
+                       int dtype) {
+  size_t es = elem_bytes(dtype);
+  if (head_dim % k_piece(dtype) != 0) return -1;
+  for (int p = 0; p < num_pairs; ++p) {
+    int64_t src = src_dst_pairs[2 * p], dst = src_dst_pairs[2 * p + 1];
+    if (src < 0 || dst < 0 || src >= src_blocks || dst >= dst_blocks) return -1;
+    for (int h = 0; h < num_kv_heads; ++h)
+      for (int off = 0; off < block_size; ++off)
+        for (int d = 0; d < head_dim; ++d) {
+          int64_t ks = k_index(src, h, off, d, num_kv_heads, block_size, head_dim, k_piece(dtype));
+          int64_t kd = k_index(dst, h, off, d, num_kv_heads, block_size, head_dim, k_piece(dtype));
+          int64_t vs = v_index(src, h, off, d, num_kv_heads, block_size, head_dim);
+          int64_t vd = v_index(dst, h, off, d, num_kv_heads, block_size, head_dim);
+          memcpy((char*)dst_k + es * kd, (const char*)src_k + es * ks, es);
+          memcpy((char*)dst_v + es * vd, (const char*)src_v + es * vs, es);
+        }
+  }
+  return 0;
+}
+
 /* Exposed so tests can check the widening against numpy's own fp16 decode. */
 double oracle_half_to_double(uint16_t h) { return half_bits_to_double(h); }
 double oracle_bf16_to_double(uint16_t b) { return bf16_bits_to_double(b); }

@@ -45,6 +45,7 @@ def _load():
         "pa_reshape_and_cache": (i32, [vp, vp, vp, vp, vp, i32, i64, i64, i32, i32, i32, i64,
                                        i32, vp]),
         "pa_copy_blocks": (i32, [vp, vp, vp, i32, i32, i32, i32, i64, i32, vp]),
+        "pa_swap_blocks": (i32, [vp, vp, vp, vp, vp, i32, i64, i64, i32, i32, i32, i32, vp]),
         "pa_alloc_create": (vp, [i64, i32, ctypes.c_uint64]),
         "pa_alloc_destroy": (None, [vp]),
         "pa_alloc_add_seq": (i32, [vp, i64, i32]),
@@ -68,7 +69,7 @@ _lib = _load()
 
 # every symbol include/pa.h declares (checked by the CPU test suite)
 EXPORTED = ("pa_strerror", "pa_decode", "pa_decode_workspace_bytes", "pa_decode_partition_size",
-            "pa_prefill",
+            "pa_prefill", "pa_swap_blocks",
             "pa_reshape_and_cache", "pa_copy_blocks", "pa_alloc_create", "pa_alloc_destroy",
             "pa_alloc_add_seq", "pa_alloc_fork", "pa_alloc_append", "pa_alloc_free_seq",
             "pa_alloc_block_tables", "pa_alloc_num_free", "pa_alloc_refcount",
@@ -261,6 +262,30 @@ def pa_copy_blocks(k_cache, v_cache, src_dst_pairs, block_size, stream=None):
     _check(_lib.pa_copy_blocks(_dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"),
                                _dev_ptr(src_dst_pairs, "src_dst_pairs"), src_dst_pairs.shape[0],
                                hkv, D, block_size, nb, _dtype_code(k_cache), _stream(stream)))
+
+
+def pa_swap_blocks(src_k, src_v, dst_k, dst_v, src_dst_pairs, block_size, stream=None):
+    """Copy whole blocks from (src_k, src_v) to (dst_k, dst_v), pools of one
+    layout that may live on the device or in pinned host memory; pairs int64
+    [P, 2] on the device or pinned.  Pageable host tensors are refused."""
+    if src_dst_pairs.dtype != torch.int64 or src_dst_pairs.dim() != 2 or \
+            src_dst_pairs.shape[1] != 2:
+        raise ValueError("src_dst_pairs must be int64 [num_pairs, 2]")
+    for name, t in (("src_k", src_k), ("src_v", src_v), ("dst_k", dst_k), ("dst_v", dst_v),
+                    ("src_dst_pairs", src_dst_pairs)):
+        if not (t.is_cuda or t.is_pinned()):
+            raise ValueError(f"{name} must be a device tensor or pinned host memory")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    hkv, D = src_v.shape[1], src_v.shape[3]
+    ns = _check_pools(src_k, src_v, hkv, block_size, D)
+    nd = _check_pools(dst_k, dst_v, hkv, block_size, D)
+    if src_k.dtype != dst_k.dtype:
+        raise ValueError("source and destination pools must have one dtype")
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    _check(_lib.pa_swap_blocks(ptr(src_k), ptr(src_v), ptr(dst_k), ptr(dst_v),
+                               ptr(src_dst_pairs), src_dst_pairs.shape[0], ns, nd, hkv, D,
+                               block_size, _dtype_code(src_k), _stream(stream)))
 
 
 # ------------------------------------------------------------ allocator --

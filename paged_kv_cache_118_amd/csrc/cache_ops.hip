@@ -99,6 +99,30 @@ __global__ __launch_bounds__(kThreads) void copy_blocks_kernel(char* __restrict_
   }
 }
 
+// Whole-block copies between two pools of the same layout (the swap of
+// blocks between device memory and pinned host memory): block src of the
+// source pools to block dst of the destination pools, K and V.  Ids outside
+// either pool skip the pair.
+__global__ __launch_bounds__(kThreads) void swap_blocks_kernel(
+    const char* __restrict__ src_k, const char* __restrict__ src_v, char* __restrict__ dst_k,
+    char* __restrict__ dst_v, const int64_t* __restrict__ pairs, int64_t block_bytes,
+    int64_t src_blocks, int64_t dst_blocks) {
+  const int64_t src = pairs[2 * blockIdx.y], dst = pairs[2 * blockIdx.y + 1];
+  if (src < 0 || dst < 0 || src >= src_blocks || dst >= dst_blocks) return;
+  const int64_t n16 = block_bytes / 16;
+  const uint4* ks = reinterpret_cast<const uint4*>(src_k + src * block_bytes);
+  const uint4* vs = reinterpret_cast<const uint4*>(src_v + src * block_bytes);
+  uint4* kd = reinterpret_cast<uint4*>(dst_k + dst * block_bytes);
+  uint4* vd = reinterpret_cast<uint4*>(dst_v + dst * block_bytes);
+  for (int64_t i = blockIdx.x * (int64_t)kThreads + threadIdx.x; i < n16;
+       i += (int64_t)gridDim.x * kThreads) {
+    const uint4 a = ks[i];
+    const uint4 b = vs[i];
+    kd[i] = a;
+    vd[i] = b;
+  }
+}
+
 template <int TT>
 void launch_rc(const void* k, const void* v, void* k_cache, void* v_cache, const int64_t* slots,
                int32_t num_tokens, int64_t k_stride, int64_t v_stride, int32_t hkv, int32_t D,
@@ -142,6 +166,20 @@ hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs
   dim3 grid(gx, num_pairs);
   hipLaunchKernelGGL(copy_blocks_kernel, grid, dim3(kThreads), 0, s, (char*)k_cache,
                      (char*)v_cache, pairs, block_bytes, num_blocks);
+  return hipGetLastError();
+}
+
+hipError_t launch_swap_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
+                              const int64_t* pairs, int32_t num_pairs, int64_t block_bytes,
+                              int64_t src_blocks, int64_t dst_blocks, hipStream_t s) {
+  if (num_pairs == 0) return hipSuccess;
+  const int64_t n16 = block_bytes / 16;
+  int gx = (int)((n16 + kThreads * 4 - 1) / (kThreads * 4));
+  if (gx < 1) gx = 1;
+  dim3 grid(gx, num_pairs);
+  hipLaunchKernelGGL(swap_blocks_kernel, grid, dim3(kThreads), 0, s, (const char*)src_k,
+                     (const char*)src_v, (char*)dst_k, (char*)dst_v, pairs, block_bytes,
+                     src_blocks, dst_blocks);
   return hipGetLastError();
 }
 

@@ -123,6 +123,19 @@ Plan make_plan(int num_seqs, int hq, int hkv, int head_dim, int block_size, int 
   return p;
 }
 
+// True when a kernel may dereference p: device memory, or pinned host memory
+// mapped at the same address (pageable host memory is refused).
+bool device_accessible(const void* p) {
+  hipPointerAttribute_t at{};
+  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  const bool kind = at.type == hipMemoryTypeDevice || at.type == hipMemoryTypeHost ||
+                    at.type == hipMemoryTypeManaged || at.type == hipMemoryTypeUnified;
+  return kind && at.devicePointer == p;
+}
+
 pa_status hip_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_EHIP; }
 
 template <typename T>
@@ -349,6 +362,39 @@ pa_status pa_reshape_and_cache(const void* k, const void* v, void* k_cache, void
   return hip_status(launch_reshape_and_cache(k, v, k_cache, v_cache, slot_mapping, num_tokens,
                                              k_token_stride, v_token_stride, num_kv_heads,
                                              head_dim, block_size, num_blocks, es, s));
+}
+
+pa_status pa_swap_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
+                         const int64_t* src_dst_pairs, int32_t num_pairs, int64_t src_num_blocks,
+                         int64_t dst_num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, pa_dtype dtype, void* stream) {
+  if (num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      src_num_blocks <= 0 || dst_num_blocks <= 0)
+    return PA_EINVAL;
+  if (!dtype_ok(dtype)) return PA_ENOTSUP;
+  const int64_t block_bytes = (int64_t)num_kv_heads * block_size * head_dim * elem_bytes(dtype);
+  if (block_bytes % 16 != 0) return PA_ENOTSUP;
+  if (num_pairs == 0) return PA_OK;
+  if (!src_k || !src_v || !dst_k || !dst_v || !src_dst_pairs) return PA_EINVAL;
+  if (!aligned16(src_k) || !aligned16(src_v) || !aligned16(dst_k) || !aligned16(dst_v))
+    return PA_EINVAL;
+  // every pointer the kernel reads or writes must be mapped for the device
+  if (!device_accessible(src_k) || !device_accessible(src_v) || !device_accessible(dst_k) ||
+      !device_accessible(dst_v) || !device_accessible(src_dst_pairs))
+    return PA_EINVAL;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (validate_enabled()) {
+    std::vector<int64_t> pr;
+    if (!copy_to_host(pr, src_dst_pairs, (size_t)num_pairs * 2, s)) return PA_EHIP;
+    std::unordered_set<int64_t> dsts;
+    for (int i = 0; i < num_pairs; ++i) {
+      const int64_t a = pr[2 * i], b = pr[2 * i + 1];
+      if (a < 0 || b < 0 || a >= src_num_blocks || b >= dst_num_blocks) return PA_EVALIDATE;
+      if (!dsts.insert(b).second) return PA_EVALIDATE;
+    }
+  }
+  return hip_status(launch_swap_blocks(src_k, src_v, dst_k, dst_v, src_dst_pairs, num_pairs,
+                                       block_bytes, src_num_blocks, dst_num_blocks, s));
 }
 
 pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* src_dst_pairs,

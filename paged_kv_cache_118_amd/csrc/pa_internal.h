@@ -135,6 +135,9 @@ hipError_t launch_reshape_and_cache(const void* k, const void* v, void* k_cache,
                                     int64_t v_stride, int32_t num_kv_heads, int32_t head_dim,
                                     int32_t block_size, int64_t num_blocks, int elem_bytes,
                                     hipStream_t s);
+hipError_t launch_swap_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
+                              const int64_t* pairs, int32_t num_pairs, int64_t block_bytes,
+                              int64_t src_blocks, int64_t dst_blocks, hipStream_t s);
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs,
                               int32_t num_pairs, int64_t block_bytes, int64_t num_blocks,
                               hipStream_t s);

@@ -91,6 +91,18 @@ def test_cache_ops_reject_bad_args():
 
 
 # ------------------------------------------------------------ allocator --
+def test_swap_blocks_refuses_memory_the_device_cannot_map():
+    """Host buffers that are not pinned (here numpy arrays) are refused
+    before anything is launched."""
+    lib = pa.lib()
+    buf = np.zeros(4096, dtype=np.uint8)
+    p = buf.ctypes.data
+    pairs = np.zeros(2, dtype=np.int64)
+    assert lib.pa_swap_blocks(p, p, p, p, pairs.ctypes.data, 1, 1, 1, 2, 128, 16, 1, None) == -1
+    assert lib.pa_swap_blocks(p, p, p, p, pairs.ctypes.data, 0, 1, 1, 2, 128, 16, 1, None) == 0
+    assert lib.pa_swap_blocks(p, p, p, p, pairs.ctypes.data, -1, 1, 1, 2, 128, 16, 1, None) == -1
+
+
 def test_alloc_example1():
     g = G["example1"]
     a = pa.BlockAllocator(64, g["block_size"], shuffle_seed=7)

@@ -1,5 +1,5 @@
-"""pa_reshape_and_cache and pa_copy_blocks on the GPU: bit-exact against the
-oracle over the whole pools."""
+"""pa_reshape_and_cache, pa_copy_blocks and pa_swap_blocks on the GPU:
+bit-exact against the oracle over the whole pools."""
 import numpy as np
 import pytest
 import torch
@@ -128,3 +128,63 @@ except pa.PAError as e:
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env,
                        timeout=120, cwd=ROOT)
     assert r.stdout.split("\n")[:2] == ["status -5", "status -5"], r.stdout + r.stderr
+
+
+def _pinned_like_pool(shape, dtype, fill_bits):
+    t = torch.empty(shape, dtype=W.TORCH_DTYPE[dtype], pin_memory=True)
+    t.view(torch.int16 if dtype != "f32" else torch.int32).fill_(fill_bits)
+    return t
+
+
+@pytest.mark.parametrize("dtype,hkv,D,bs", [("f16", 40, 128, 16), ("bf16", 8, 128, 32),
+                                            ("f32", 2, 64, 8)])
+def test_swap_out_and_in_bit_exact(dtype, hkv, D, bs):
+    """Device pool -> pinned host pool (swap out), then host -> other device
+    ids (swap in): both destinations equal the oracle's bit for bit over the
+    whole pool, and decode through the swapped-in blocks equals decode through
+    the originals."""
+    log(f"[swap] {dtype} hkv={hkv} D={D} bs={bs}")
+    nb, nh = 24, 10
+    rng = np.random.default_rng(5)
+    kc, vc = _pool(nb, hkv, bs, D, dtype, 11)
+    hk = _pinned_like_pool(W.k_pool_shape(nh, hkv, bs, D, dtype), dtype, 0x3C01)
+    hv = _pinned_like_pool(W.v_pool_shape(nh, hkv, bs, D), dtype, 0x3C01)
+    src = rng.choice(nb, size=6, replace=False)
+    dst = rng.choice(nh, size=6, replace=False)
+    out_pairs = np.stack([src, dst], axis=1).astype(np.int64)
+    want_k, want_v = W.to_numpy_bits(hk).copy(), W.to_numpy_bits(hv).copy()
+    oracle.get().swap_blocks(W.to_numpy_bits(kc), W.to_numpy_bits(vc), want_k, want_v, out_pairs,
+                             hkv, D, bs, dtype)
+    pa.pa_swap_blocks(kc, vc, hk, hv, torch.from_numpy(out_pairs).to(DEV), bs)
+    torch.cuda.synchronize()
+    assert np.array_equal(W.to_numpy_bits(hk), want_k)
+    assert np.array_equal(W.to_numpy_bits(hv), want_v)
+    # swap in to fresh ids of a second device pool; pairs from pinned memory
+    k2, v2 = _pool(nb, hkv, bs, D, dtype, 12)
+    back = rng.choice(nb, size=6, replace=False)
+    in_pairs = torch.from_numpy(np.stack([dst, back], axis=1).astype(np.int64)).pin_memory()
+    want2_k, want2_v = W.to_numpy_bits(k2).copy(), W.to_numpy_bits(v2).copy()
+    oracle.get().swap_blocks(want_k, want_v, want2_k, want2_v, in_pairs.numpy(), hkv, D, bs,
+                             dtype)
+    pa.pa_swap_blocks(hk, hv, k2, v2, in_pairs, bs)
+    torch.cuda.synchronize()
+    assert np.array_equal(W.to_numpy_bits(k2), want2_k)
+    assert np.array_equal(W.to_numpy_bits(v2), want2_v)
+    for s, b in zip(src, back):
+        assert torch.equal(k2[int(b)], kc[int(s)]) and torch.equal(v2[int(b)], vc[int(s)])
+
+
+def test_swap_refuses_pageable_host_memory():
+    """A pageable host pool is refused by the binding, and by the C entry
+    point itself, before anything runs."""
+    hkv, D, bs = 2, 128, 16
+    kc, vc = _pool(4, hkv, bs, D, "f16", 13)
+    hk = torch.zeros(W.k_pool_shape(4, hkv, bs, D, "f16"), dtype=torch.float16)
+    hv = torch.zeros(W.v_pool_shape(4, hkv, bs, D), dtype=torch.float16)
+    pairs = torch.tensor([[0, 1]], dtype=torch.int64, device=DEV)
+    with pytest.raises(ValueError):
+        pa.pa_swap_blocks(kc, vc, hk, hv, pairs, bs)
+    rc = pa.lib().pa_swap_blocks(kc.data_ptr(), vc.data_ptr(), hk.data_ptr(), hv.data_ptr(),
+                                 pairs.data_ptr(), 1, 4, 4, hkv, D, bs, 1, None)
+    assert rc == -1
+    assert (hk == 0).all() and (hv == 0).all()

@@ -128,3 +128,31 @@ def test_copy_blocks_rejects_out_of_range(orc):
     vp = np.zeros((3, 1, 1, 4, 4), np.float32)
     with pytest.raises(ValueError):
         orc.copy_blocks(kp, vp, [[0, 3]], 1, 4, 4, "f32")
+
+
+def test_swap_blocks_bytes_and_round_trip(orc):
+    """Swap oracle: every moved block arrives bit for bit, the rest of the
+    destination is untouched, and swapping out then back in at new ids
+    restores the original blocks."""
+    rng = np.random.default_rng(21)
+    hkv, D, bs, dt = 2, 16, 4, "f16"
+    x = 8
+    ns, nh = 9, 5
+    src_k = rng.integers(0, 65535, size=(ns, hkv, D // x, bs, x), dtype=np.uint16)
+    src_v = rng.integers(0, 65535, size=(ns, hkv, 1, D, bs), dtype=np.uint16)
+    host_k = np.full((nh, hkv, D // x, bs, x), 0x7E01, dtype=np.uint16)
+    host_v = np.full((nh, hkv, 1, D, bs), 0x7E01, dtype=np.uint16)
+    out_pairs = np.array([[7, 0], [2, 3], [4, 1]], dtype=np.int64)
+    orc.swap_blocks(src_k, src_v, host_k, host_v, out_pairs, hkv, D, bs, dt)
+    for s, d in out_pairs:
+        assert np.array_equal(host_k[d], src_k[s]) and np.array_equal(host_v[d], src_v[s])
+    for d in set(range(nh)) - set(out_pairs[:, 1].tolist()):
+        assert (host_k[d] == 0x7E01).all() and (host_v[d] == 0x7E01).all()
+    back_k = np.zeros_like(src_k)
+    back_v = np.zeros_like(src_v)
+    in_pairs = np.array([[0, 5], [3, 8], [1, 0]], dtype=np.int64)
+    orc.swap_blocks(host_k, host_v, back_k, back_v, in_pairs, hkv, D, bs, dt)
+    for (s, _), (_, d) in zip(out_pairs, in_pairs):
+        assert np.array_equal(back_k[d], src_k[s]) and np.array_equal(back_v[d], src_v[s])
+    with pytest.raises(ValueError):
+        orc.swap_blocks(src_k, src_v, host_k, host_v, np.array([[0, nh]]), hkv, D, bs, dt)
