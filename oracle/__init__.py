@@ -43,6 +43,17 @@ What each function follows (web pages on PagedAttention):
   and the BlockManager of deepinsea.top "PagedAttention 内存管理深度解析".
   Pinned by the two worked allocation examples of the wq-win page (stored in
   ``tests/golden/``) and by the tail-waste bound of its section 二.
+* ``alloc_ref.PrefixCachingPool`` -- automatic prefix caching, section 2.2 (5)
+  of the zhy-blog.vercel.app vLLM post (blocks keyed by their tokens and all
+  tokens before them, reused by later requests) and question 2 of the wq-win
+  page's self-test (reuse only for the same prefix).  Pinned by
+  ``tests/prefix_cache_pins.py``: a caller simulation that checks every
+  sequence reads the K/V of its own tokens through its table after each of
+  hundreds of random requests, appends, forks and releases with constant
+  eviction; maximal reuse against a brute-force search of the history; tiny
+  hand-derived eviction scenarios; and mutation tests (key without the
+  prefix, salt ignored, newest-first or evict-before-free, forward release,
+  no revive, no retention, partial blocks cached, no reuse).
 
 No function here is "parity unpinned".
 """

@@ -14,7 +14,29 @@ A plain Python model of the ref-counted KV block pool, written from:
   a new block is taken only when the next token crosses a block boundary.
 
 Readings where the pages are silent: the pool is shuffled once from a seed and
-then used LIFO; a failed request changes nothing (all-or-nothing).
+then used LIFO; a failed request changes nothing (all-or-nothing); releasing a
+sequence drops its blocks from the last to the first.
+
+``PrefixCachingPool`` adds automatic prefix caching, written from the
+zhy-blog.vercel.app vLLM post, section 2.2 (5) ("自动前缀缓存"): every cached
+block sits in one table under a key made of its own tokens and all the tokens
+before it, and a new request looks its blocks up there and reuses the ones it
+finds; and from the wq-win page's self-test ("自测：从内存图推导服务行为"),
+question 2: KV may be reused only for the same prefix under the same
+conditions, equal tokens at one place are not enough.  Readings where the pages are silent (the plainest ones the rest
+supports):
+
+* only full blocks are cached (a partially filled block is still written, the
+  wq-win page's section 二 shares only blocks that are full and no longer
+  rewritten); a block enters the table when it becomes full;
+* the key of block i is (salt, every token of positions 0 .. (i+1)*BS - 1);
+  the salt stands for "the same conditions" (model, adapter, ...);
+* a request reuses the longest run of its leading full blocks that are in the
+  table, and stops at the first one that is not;
+* a cached block whose count drops to 0 stays in the table, evictable; free
+  blocks are taken first, and only when none is left is the evictable block
+  released longest ago evicted (least recently used); a block that fills with
+  a key already in the table stays private to its sequence.
 """
 from __future__ import annotations
 
@@ -49,11 +71,14 @@ class BlockPool:
         if self.ref[b] == 0:
             self.free.append(b)
 
+    def num_free(self) -> int:
+        return len(self.free)
+
     def add_seq(self, seq: int, n_tokens: int) -> None:
         need = self.blocks_for(n_tokens)
         if seq in self.tables:
             raise KeyError(seq)
-        if need > len(self.free):
+        if need > self.num_free():
             raise OutOfBlocks(seq)
         self.tables[seq] = [self._take() for _ in range(need)]
         self.lens[seq] = n_tokens
@@ -74,7 +99,7 @@ class BlockPool:
         table, L, bs = self.tables[seq], self.lens[seq], self.block_size
         need_new = self.blocks_for(L + n_tokens) - len(table)
         cow = n_tokens > 0 and L % bs != 0 and self.ref[table[-1]] > 1
-        if need_new + (1 if cow else 0) > len(self.free):
+        if need_new + (1 if cow else 0) > self.num_free():
             raise OutOfBlocks(seq)
         pairs = []
         if cow:
@@ -92,15 +117,132 @@ class BlockPool:
         return slots, pairs
 
     def free_seq(self, seq: int) -> None:
-        for b in self.tables.pop(seq):
+        for b in reversed(self.tables.pop(seq)):
             self._drop(b)
         del self.lens[seq]
-
-    def num_free(self) -> int:
-        return len(self.free)
 
     def slots_reserved(self, seq: int) -> int:
         return len(self.tables[seq]) * self.block_size
 
     def tail_waste(self, seq: int) -> int:
         return self.slots_reserved(seq) - self.lens[seq]
+
+
+class PrefixCachingPool(BlockPool):
+    """BlockPool with automatic prefix caching (see the module docstring)."""
+
+    def __init__(self, num_blocks: int, block_size: int, shuffle_seed: int | None = None):
+        super().__init__(num_blocks, block_size, shuffle_seed)
+        self.cached: dict[tuple, int] = {}   # key -> block holding that prefix
+        self.key_of: dict[int, tuple] = {}   # block -> its key, for table entries
+        self.evictable: list[int] = []       # table entries at count 0, oldest first
+        self.tokens: dict[int, list | None] = {}  # None: tokens unknown, not cached
+        self.salt: dict[int, int] = {}
+
+    def key(self, salt: int, tokens, i: int) -> tuple:
+        """Key of block i: the salt and every token up to the end of block i."""
+        return (salt, tuple(tokens[:(i + 1) * self.block_size]))
+
+    def num_free(self) -> int:
+        return len(self.free) + len(self.evictable)
+
+    def _take(self) -> int:
+        if self.free:
+            b = self.free.pop()
+        else:  # evict the entry released longest ago
+            b = self.evictable.pop(0)
+            del self.cached[self.key_of.pop(b)]
+        self.ref[b] = 1
+        return b
+
+    def _drop(self, b: int) -> None:
+        self.ref[b] -= 1
+        if self.ref[b] == 0:
+            (self.evictable if b in self.key_of else self.free).append(b)
+
+    def _revive(self, b: int) -> None:
+        """A request reuses table entry b: one more reference; an entry at
+        count 0 leaves the evictable list."""
+        if self.ref[b] == 0:
+            self.evictable.remove(b)
+        self.ref[b] += 1
+
+    def _register(self, key: tuple, b: int) -> None:
+        if key not in self.cached:
+            self.cached[key] = b
+            self.key_of[b] = key
+
+    def add_seq(self, seq: int, n_tokens: int) -> None:
+        super().add_seq(seq, n_tokens)
+        self.tokens[seq] = None
+
+    def add_seq_tokens(self, seq: int, tokens, salt: int = 0) -> int:
+        """New sequence whose prompt is ``tokens``.  Returns how many leading
+        tokens already have their K / V in reused blocks (a multiple of BS)."""
+        if seq in self.tables:
+            raise KeyError(seq)
+        tokens = list(tokens)
+        bs, n = self.block_size, len(tokens)
+        hits = []
+        for i in range(n // bs):
+            b = self.cached.get(self.key(salt, tokens, i))
+            if b is None:
+                break
+            hits.append(b)
+        need = self.blocks_for(n) - len(hits)
+        revived = sum(1 for b in hits if self.ref[b] == 0)
+        if need > self.num_free() - revived:
+            raise OutOfBlocks(seq)
+        for b in hits:
+            self._revive(b)
+        table = list(hits)
+        for i in range(len(hits), self.blocks_for(n)):
+            b = self._take()
+            table.append(b)
+            if (i + 1) * bs <= n:
+                self._register(self.key(salt, tokens, i), b)
+        self.tables[seq] = table
+        self.lens[seq] = n
+        self.tokens[seq] = tokens
+        self.salt[seq] = salt
+        return len(hits) * bs
+
+    def fork(self, parent: int, child: int) -> None:
+        super().fork(parent, child)
+        t = self.tokens[parent]
+        self.tokens[child] = None if t is None else list(t)
+        self.salt[child] = self.salt.get(parent, 0)
+
+    def append(self, seq: int, n_tokens: int):
+        """Append without tokens: the sequence's later blocks are not cached."""
+        out = super().append(seq, n_tokens)
+        self.tokens[seq] = None
+        return out
+
+    def append_tokens(self, seq: int, tokens):
+        """Append known tokens; every block they fill enters the table."""
+        tokens = list(tokens)
+        L = self.lens[seq]
+        slots, pairs = super().append(seq, len(tokens))
+        if self.tokens[seq] is not None:
+            self.tokens[seq].extend(tokens)
+            bs = self.block_size
+            for p in range(L, L + len(tokens)):
+                if (p + 1) % bs == 0:
+                    i = p // bs
+                    self._register(self.key(self.salt[seq], self.tokens[seq], i),
+                                   self.tables[seq][i])
+        return slots, pairs
+
+    def free_seq(self, seq: int) -> None:
+        super().free_seq(seq)
+        del self.tokens[seq]
+        self.salt.pop(seq, None)
+
+    def reset_cache(self) -> None:
+        """Forget every table entry; evictable blocks become free (oldest
+        release first onto the free list)."""
+        self.free.extend(self.evictable)
+        self.evictable = []
+        self.cached.clear()
+        self.key_of.clear()
