@@ -61,6 +61,10 @@ def parse():
                     help="only time pa_swap_blocks: half of the workload's blocks out to a "
                          "pinned host pool and back, against a plain device-to-host copy "
                          "of the same bytes")
+    ap.add_argument("--prefix-cache", action="store_true",
+                    help="automatic prefix caching on the LLaMA-13B prefix-sharing prompts: "
+                         "host admission cost, and one iteration's K/V writes + chunked "
+                         "prefill with reuse vs recomputing every prompt")
     ap.add_argument("--stream-probe", action="store_true",
                     help="only measure plain device read / copy bandwidth (context for peak)")
     ap.add_argument("--mfma-summary", metavar="FOLDER",
@@ -668,6 +672,145 @@ def swap_run(args, torch, wl):
                       "torch_contiguous_d2h_GBps": round(d2h, 2)}), flush=True)
 
 
+def prefix_cache_run(args, torch):
+    """Automatic prefix caching on the LLaMA-13B prefix-sharing workload: 256
+    prompts (32 groups of 8 sharing a 512-token prefix, tails of U[1, 512]
+    tokens, random arrival order) admitted in one iteration.
+
+    Host: microseconds per prompt for libpa's allocator to admit it (block
+    hashes, table lookups, allocation; the ctypes call included), over fresh
+    allocators.  GPU: the iteration's K / V writes (pa_reshape_and_cache) and
+    chunked-prefill attention (pa_prefill) with reuse -- only positions after
+    the reused blocks are written and queried -- against recomputing every
+    prompt whole, each timed as back-to-back iterations with HIP events on the
+    stream they run on; the rows both compute are compared."""
+    import paged_kv_cache_118_amd as pa
+    import workloads as W
+    from paged_kv_cache_118_amd.schedule import admit
+    sp = W.LLAMA13B_SHARE
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(sp.seed + 40)
+    prompts, groups, tails = W.share_prompts(sp, rng)
+    bs, plen = sp.block_size, sp.lengths[2]
+    n = len(prompts)
+    ids = np.arange(n)
+    blocks_plain = sum(-(-len(p) // bs) for p in prompts)
+
+    # host admission
+    reps, host_s = 5, []
+    for r in range(reps):
+        a = pa.BlockAllocator(blocks_plain, bs, shuffle_seed=r + 1)
+        t0 = time.perf_counter()
+        ad = admit(a, ids, prompts)
+        host_s.append(time.perf_counter() - t0)
+    blocks_cached = blocks_plain - a.num_free()
+    host_us = float(np.median(host_s)) / n * 1e6
+
+    # device inputs, identical for both paths
+    gen = W.make_generator(sp.seed + 41, dev)
+    kv = W.ShareKV(sp, groups, tails, gen, dev, plen)
+    L = np.array([len(p) for p in prompts], dtype=np.int64)
+    qfull = W.randn((n, int(L.max()), sp.num_q_heads, sp.head_dim), sp.dtype, gen, dev)
+
+    def setup(cached):
+        if cached:
+            a = pa.BlockAllocator(blocks_plain, bs, shuffle_seed=7)
+            d = admit(a, ids, prompts)
+            rs, rp, slots, qs, lens = d.row_seq, d.row_pos, d.slots, d.query_start, d.lens
+            nb = blocks_plain
+        else:
+            a = pa.BlockAllocator(blocks_plain, bs, shuffle_seed=8)
+            for i, m in enumerate(L):
+                a.add_seq(i, int(m))
+            rs = np.repeat(ids, L)
+            rp = np.concatenate([np.arange(m) for m in L])
+            lens = L.astype(np.int32)
+            qs = np.concatenate([[0], np.cumsum(L)]).astype(np.int32)
+            nb = blocks_plain
+            slots = None
+        mb = int(-(-L.max() // bs))
+        tables, _ = a.block_tables(ids, mb)
+        if slots is None:
+            slots = tables[rs, rp // bs].astype(np.int64) * bs + rp % bs
+        w = slots >= 0
+        pidx = torch.from_numpy(rs).to(dev)
+        pos = torch.from_numpy(rp).to(dev)
+        wm = torch.from_numpy(w).to(dev)
+        wk, wv = kv.rows(pidx[wm], pos[wm])
+        kc = torch.empty(W.k_pool_shape(nb, sp.num_kv_heads, bs, sp.head_dim, sp.dtype),
+                         dtype=W.TORCH_DTYPE[sp.dtype], device=dev)
+        vc = torch.empty(W.v_pool_shape(nb, sp.num_kv_heads, bs, sp.head_dim),
+                         dtype=W.TORCH_DTYPE[sp.dtype], device=dev)
+        q = qfull[pidx, pos].contiguous()
+        st = dict(wk=wk, wv=wv, kc=kc, vc=vc, q=q, out=torch.empty_like(q),
+                  slots=torch.from_numpy(slots[w]).to(dev), tables=torch.from_numpy(tables).to(dev),
+                  lens=torch.from_numpy(lens.astype(np.int32)).to(dev),
+                  qs=torch.from_numpy(qs).to(dev), mql=int(np.diff(qs).max()),
+                  rows=int(len(rs)), written=int(w.sum()), rs=rs, rp=rp,
+                  visible=float(np.sum(rp + 1)))
+        return st
+
+    def run(st):
+        pa.pa_reshape_and_cache(st["wk"], st["wv"], st["kc"], st["vc"], st["slots"], bs)
+        pa.pa_prefill(st["out"], st["q"], st["kc"], st["vc"], st["tables"], st["lens"], st["qs"],
+                      sp.scale, bs, sp.num_kv_heads, st["mql"], int(L.max()))
+
+    res = {}
+    outs = {}
+    for name, cached in (("reuse", True), ("recompute", False)):
+        st = setup(cached)
+        for _ in range(max(1, args.warmup // 5)):
+            run(st)
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        k = max(3, args.steps // 5)
+        e0.record(stream)
+        for _ in range(k):
+            run(st)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / k
+        # prefill alone, for its MFMA roofline
+        e0.record(stream)
+        for _ in range(k):
+            pa.pa_prefill(st["out"], st["q"], st["kc"], st["vc"], st["tables"], st["lens"],
+                          st["qs"], sp.scale, bs, sp.num_kv_heads, st["mql"], int(L.max()))
+        e1.record(stream)
+        torch.cuda.synchronize()
+        pms = e0.elapsed_time(e1) / k
+        flops = 4.0 * sp.head_dim * sp.num_q_heads * st["visible"]
+        res[name] = {"ms_per_iteration": round(ms, 4), "prefill_ms": round(pms, 4),
+                     "rows_queried": st["rows"], "rows_written": st["written"],
+                     "prefill_TFLOPs": round(flops / (pms / 1e3) / 1e12, 1)}
+        outs[name] = (st["out"], st["rs"], st["rp"])
+        del st
+    o_r, rs_r, rp_r = outs["reuse"]
+    o_f, rs_f, rp_f = outs["recompute"]
+    start = np.concatenate([[0], np.cumsum(L)])
+    at = torch.from_numpy(start[rs_r] + rp_r).to(dev)
+    diff = float((o_r.double() - o_f[at].double()).abs().max())
+    peak = MFMA_PEAK_TFLOPS[sp.dtype]
+    tf = res["reuse"]["prefill_TFLOPs"]
+    print(json.dumps({
+        "metric": "prefix_cache_iteration_speedup",
+        "value": round(res["recompute"]["ms_per_iteration"] / res["reuse"]["ms_per_iteration"], 3),
+        "unit": "x", "higher_is_better": True, "dtype": sp.dtype, "data": "synthetic",
+        "config": {"workload": "llama13b_prefix_share admission", "prompts": n,
+                   "groups": int(groups.max()) + 1, "prefix_tokens": plen,
+                   "tail_tokens": [int(sp.lengths[3]), int(sp.lengths[4])],
+                   "q_heads": sp.num_q_heads, "kv_heads": sp.num_kv_heads,
+                   "head_dim": sp.head_dim, "block_size": bs},
+        "prompt_tokens": int(L.sum()), "tokens_reused": int(ad.cached.sum()),
+        "reuse_fraction": round(float(ad.cached.sum()) / float(L.sum()), 4),
+        "blocks_held_with_reuse": int(blocks_cached), "blocks_held_without": int(blocks_plain),
+        "host_admission_us_per_prompt": round(host_us, 2),
+        **res, "max_abs_diff_reuse_vs_recompute": diff,
+        "roofline": {"bound": "mfma", "achieved": tf, "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(tf / peak, 4), "traffic": None},
+    }), flush=True)
+
+
 def build_workload(args, dev):
     return Workload(args, dev)
 
@@ -701,6 +844,10 @@ def main():
 
     if args.overhead_sweep:
         overhead_sweep(args, torch)
+        return
+
+    if args.prefix_cache:
+        prefix_cache_run(args, torch)
         return
 
     dev = torch.device("cuda:0")

@@ -258,8 +258,9 @@ pa_status pa_alloc_fork(pa_alloc* a, int64_t parent_id, int64_t child_id);
 pa_status pa_alloc_append(pa_alloc* a, int64_t seq_id, int32_t n_tokens, int64_t* slots_out,
                           int64_t* cow_pairs_out, int32_t* n_cow_out);
 
-/* Drop the sequence: each of its blocks loses one reference; blocks at 0 are
- * reclaimed. */
+/* Drop the sequence, from its last block to its first: each block loses one
+ * reference; a block at 0 is reclaimed (a prefix-cache entry stays cached,
+ * evictable, see below). */
 pa_status pa_alloc_free_seq(pa_alloc* a, int64_t seq_id);
 
 /* Host rows for pa_decode: tables_out [n][max_blocks] (padded with -1) and
@@ -267,12 +268,71 @@ pa_status pa_alloc_free_seq(pa_alloc* a, int64_t seq_id);
 pa_status pa_alloc_block_tables(const pa_alloc* a, const int64_t* seq_ids, int32_t n,
                                  int32_t max_blocks, int32_t* tables_out, int32_t* lens_out);
 
+/* Blocks a request can take: free ones plus evictable cache entries. */
 int64_t pa_alloc_num_free(const pa_alloc* a);
 /* Reference count of a physical block (-1 for an out-of-range id). */
 int32_t pa_alloc_refcount(const pa_alloc* a, int64_t block);
 /* Length / number of blocks of a sequence (-1 if unknown). */
 int32_t pa_alloc_seq_len(const pa_alloc* a, int64_t seq_id);
 int32_t pa_alloc_seq_num_blocks(const pa_alloc* a, int64_t seq_id);
+
+/* ------------------------------------------------------------------------
+ * Automatic prefix caching (zhy-blog.vercel.app, vLLM post, section 2.2 (5)
+ * "自动前缀缓存": every cached block sits in one table under a hash of its
+ * own tokens and all tokens before it; a new request looks its blocks up
+ * and reuses the ones found.  wq-win.github.io "079 | vLLM 与 PagedAttention",
+ * self-test question 2: only the same prefix under the same conditions may
+ * share K/V.)
+ *
+ * Rules (readings of the pages where they are silent):
+ *  - Only full blocks are cached.  Block i of a sequence whose tokens are
+ *    known is identified by d_i = pa_prefix_block_hash(d_{i-1}, salt, its BS
+ *    tokens), d_{-1} = NULL: a chain over (salt, tokens 0 .. (i+1)*BS - 1).
+ *    The salt stands for "the same conditions" (model, adapter, ...).
+ *  - A block enters the table when it becomes full (at pa_alloc_add_seq_tokens
+ *    for the prompt's full blocks, at pa_alloc_append_tokens for a block the
+ *    new tokens fill), unless its prefix already has an entry.  The caller
+ *    must write the K/V of every slot it reserved (pa_reshape_and_cache)
+ *    before any other sequence can read it, i.e. within the same iteration.
+ *  - A request reuses the longest run of its leading full blocks that have
+ *    entries (one more reference each) and stops at the first that has none.
+ *  - An entry whose count drops to 0 stays in the table, evictable.  Free
+ *    blocks are taken first; when none is left, the evictable entry released
+ *    longest ago is evicted (least recently used) and its block reused.
+ * Sequences made by pa_alloc_add_seq, and any sequence after a plain
+ * pa_alloc_append, have unknown tokens and add nothing to the table.  Table
+ * memory (about 50 bytes per block) is allocated on the first call that
+ * needs it.
+ * ---------------------------------------------------------------------- */
+
+/* New sequence whose prompt is tokens[0 .. num_tokens-1].  On success
+ * *num_cached_out = the number of leading tokens whose K/V already sits in
+ * reused blocks (a multiple of BS, possibly num_tokens): the caller computes
+ * and writes only the positions from there on.  All or nothing on
+ * PA_ENOMEM; PA_ENOENT if seq_id is taken. */
+pa_status pa_alloc_add_seq_tokens(pa_alloc* a, int64_t seq_id, const int32_t* tokens,
+                                  int32_t num_tokens, uint64_t salt, int32_t* num_cached_out);
+
+/* pa_alloc_append for known tokens (same slots, copy-on-write pair and
+ * errors); blocks the tokens fill enter the table. */
+pa_status pa_alloc_append_tokens(pa_alloc* a, int64_t seq_id, const int32_t* tokens,
+                                 int32_t n_tokens, int64_t* slots_out, int64_t* cow_pairs_out,
+                                 int32_t* n_cow_out);
+
+/* Entries in the table (in use or evictable), and evictable entries alone. */
+int64_t pa_alloc_num_cached(const pa_alloc* a);
+int64_t pa_alloc_num_evictable(const pa_alloc* a);
+
+/* Forget every entry; evictable blocks return to the free list, oldest
+ * release first (so the most recent is taken first). */
+pa_status pa_alloc_reset_prefix_cache(pa_alloc* a);
+
+/* The block identity: SHA-256 (FIPS 180-4) of parent (32 bytes; NULL = 32
+ * zero bytes) | salt (8 bytes, little-endian) | each token (4 bytes, little-
+ * endian), written to digest_out[0..31].  Exposed so that a caller can key
+ * its own structures (e.g. route requests by prefix) the same way. */
+pa_status pa_prefix_block_hash(const uint8_t* parent, uint64_t salt, const int32_t* tokens,
+                               int32_t num_tokens, uint8_t* digest_out);
 
 #ifdef __cplusplus
 }

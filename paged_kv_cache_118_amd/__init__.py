@@ -57,6 +57,12 @@ def _load():
         "pa_alloc_refcount": (i32, [vp, i64]),
         "pa_alloc_seq_len": (i32, [vp, i64]),
         "pa_alloc_seq_num_blocks": (i32, [vp, i64]),
+        "pa_alloc_add_seq_tokens": (i32, [vp, i64, vp, i32, ctypes.c_uint64, vp]),
+        "pa_alloc_append_tokens": (i32, [vp, i64, vp, i32, vp, vp, vp]),
+        "pa_alloc_num_cached": (i64, [vp]),
+        "pa_alloc_num_evictable": (i64, [vp]),
+        "pa_alloc_reset_prefix_cache": (i32, [vp]),
+        "pa_prefix_block_hash": (i32, [vp, ctypes.c_uint64, vp, i32, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -73,7 +79,9 @@ EXPORTED = ("pa_strerror", "pa_decode", "pa_decode_workspace_bytes", "pa_decode_
             "pa_reshape_and_cache", "pa_copy_blocks", "pa_alloc_create", "pa_alloc_destroy",
             "pa_alloc_add_seq", "pa_alloc_fork", "pa_alloc_append", "pa_alloc_free_seq",
             "pa_alloc_block_tables", "pa_alloc_num_free", "pa_alloc_refcount",
-            "pa_alloc_seq_len", "pa_alloc_seq_num_blocks")
+            "pa_alloc_seq_len", "pa_alloc_seq_num_blocks", "pa_alloc_add_seq_tokens",
+            "pa_alloc_append_tokens", "pa_alloc_num_cached", "pa_alloc_num_evictable",
+            "pa_alloc_reset_prefix_cache", "pa_prefix_block_hash")
 
 
 def lib():
@@ -296,13 +304,14 @@ class BlockAllocator:
         self._h = _lib.pa_alloc_create(num_blocks, block_size, shuffle_seed)
         if not self._h:
             raise ValueError("pa_alloc_create failed")
+        self._destroy = _lib.pa_alloc_destroy  # still reachable at interpreter exit
         self.block_size = block_size
         self.num_blocks = num_blocks
 
     def __del__(self):
         h = getattr(self, "_h", None)
         if h:
-            _lib.pa_alloc_destroy(h)
+            self._destroy(h)
             self._h = None
 
     def add_seq(self, seq_id: int, num_tokens: int) -> None:
@@ -344,3 +353,44 @@ class BlockAllocator:
 
     def seq_num_blocks(self, seq_id: int) -> int:
         return int(_lib.pa_alloc_seq_num_blocks(self._h, seq_id))
+
+    # ---- automatic prefix caching
+    def add_seq_tokens(self, seq_id: int, tokens, salt: int = 0) -> int:
+        """New sequence with prompt ``tokens``; returns how many leading
+        tokens already have their K/V in reused blocks."""
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        n = ctypes.c_int32(0)
+        _check(_lib.pa_alloc_add_seq_tokens(self._h, seq_id, t.ctypes.data_as(ctypes.c_void_p),
+                                            len(t), salt, ctypes.byref(n)))
+        return n.value
+
+    def append_tokens(self, seq_id: int, tokens):
+        """As ``append`` for known tokens; blocks they fill become cached."""
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        slots = np.empty(max(len(t), 1), dtype=np.int64)
+        pair = np.empty(2, dtype=np.int64)
+        n = ctypes.c_int32(0)
+        _check(_lib.pa_alloc_append_tokens(self._h, seq_id, t.ctypes.data_as(ctypes.c_void_p),
+                                           len(t), slots.ctypes.data_as(ctypes.c_void_p),
+                                           pair.ctypes.data_as(ctypes.c_void_p),
+                                           ctypes.byref(n)))
+        return slots[:len(t)], ((int(pair[0]), int(pair[1])) if n.value else None)
+
+    def num_cached(self) -> int:
+        return int(_lib.pa_alloc_num_cached(self._h))
+
+    def num_evictable(self) -> int:
+        return int(_lib.pa_alloc_num_evictable(self._h))
+
+    def reset_prefix_cache(self) -> None:
+        _check(_lib.pa_alloc_reset_prefix_cache(self._h))
+
+
+def prefix_block_hash(parent, salt: int, tokens) -> bytes:
+    """SHA-256 block identity of pa_prefix_block_hash (parent: 32 bytes or
+    None)."""
+    t = np.ascontiguousarray(tokens, dtype=np.int32)
+    out = (ctypes.c_uint8 * 32)()
+    par = None if parent is None else (ctypes.c_uint8 * 32).from_buffer_copy(bytes(parent))
+    _check(_lib.pa_prefix_block_hash(par, salt, t.ctypes.data_as(ctypes.c_void_p), len(t), out))
+    return bytes(out)

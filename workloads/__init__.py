@@ -243,3 +243,50 @@ def new_token_rows(num_tokens, num_kv_heads, head_dim, dtype, gen, device):
     k = randn((num_tokens, num_kv_heads, head_dim), dtype, gen, device)
     v = randn((num_tokens, num_kv_heads, head_dim), dtype, gen, device)
     return k, v
+
+
+def share_prompts(spec: Spec, rng: np.random.Generator, vocab: int = 32000):
+    """Prompts of a prefix-sharing workload, lengths ("share", group, prefix,
+    lo, hi): num_seqs / group groups, each with its own random prefix of
+    ``prefix`` token ids, and every member with its own random tail of
+    U[lo, hi] ids; returned in a random arrival order as (list of int32
+    arrays, group of each prompt, tail length of each prompt)."""
+    _, group, plen, lo, hi = spec.lengths
+    G = spec.num_seqs // group
+    prefixes = [rng.integers(0, vocab, size=plen).astype(np.int32) for _ in range(G)]
+    groups = np.repeat(np.arange(G), group)
+    tails = rng.integers(lo, hi + 1, size=len(groups)).astype(np.int32)
+    order = rng.permutation(len(groups))
+    groups, tails = groups[order], tails[order]
+    prompts = [np.concatenate([prefixes[g], rng.integers(0, vocab, size=t).astype(np.int32)])
+               for g, t in zip(groups, tails)]
+    return prompts, groups.astype(np.int32), tails
+
+
+class ShareKV:
+    """K / V rows of the prefix-sharing prompts: row (prompt i, position p) is
+    the group's prefix row p for p < prefix, else prompt i's own tail row.
+    Every prompt of a group thus has the same K / V over the shared prefix,
+    as a model would compute for equal tokens, and its own afterwards."""
+
+    def __init__(self, spec: Spec, groups, tails, gen, device, plen: int):
+        hkv, D, dt = spec.num_kv_heads, spec.head_dim, spec.dtype
+        G = int(groups.max()) + 1 if len(groups) else 0
+        self.plen, self.groups = plen, torch.from_numpy(np.asarray(groups, np.int64)).to(device)
+        mt = max(1, int(np.max(tails)) if len(tails) else 1)
+        self.pk = randn((G, plen, hkv, D), dt, gen, device)
+        self.pv = randn((G, plen, hkv, D), dt, gen, device)
+        self.tk = randn((len(groups), mt + 1, hkv, D), dt, gen, device)
+        self.tv = randn((len(groups), mt + 1, hkv, D), dt, gen, device)
+
+    def rows(self, prompt_idx, positions):
+        """(K, V) rows [T][Hkv][D] for the given prompt indices and positions
+        (int64 device tensors)."""
+        pre = positions < self.plen
+        g = self.groups[prompt_idx]
+        pp = positions.clamp(max=self.plen - 1)
+        tp = (positions - self.plen).clamp(min=0)
+        m = pre[:, None, None]
+        k = torch.where(m, self.pk[g, pp], self.tk[prompt_idx, tp])
+        v = torch.where(m, self.pv[g, pp], self.tv[prompt_idx, tp])
+        return k.contiguous(), v.contiguous()
