@@ -16,63 +16,113 @@ constexpr int kThreads = 256;
 
 // One workgroup = TT consecutive tokens of one kv head, 8*TT threads (TT = 32
 // for large writes, 8 for decode-sized ones so more CUs share the stores).
+// The K and V rows of the TT tokens are first staged in LDS by 16-byte loads
+// running along each row (so a wavefront reads whole cache lines), then:
 //  K: the pool stores 16-byte pieces [D/X][BS][X]; piece c of a token row is
-//     one 16-byte copy.  Threads take tokens fastest, so consecutive slots of
-//     one block write one contiguous run per piece.
-//  V: the pool stores 8-token slabs [D][VS]; rows are staged in LDS and each
-//     lane then writes one token's element, so lanes with consecutive slots
-//     write consecutive addresses of a slab row.
+//     one 16-byte store, threads taking tokens fastest, so consecutive slots
+//     of one block fill one contiguous run per piece.
+//  V: the pool stores 8-token slabs [D][VS].  Where the call writes all eight
+//     slots of a slab (consecutive tokens at slots 8k .. 8k+7, the common case
+//     for prompt chunks), each slab row -- the 8 tokens' element d -- is
+//     gathered from LDS and written as whole 16-byte pieces; the tokens of
+//     partly written slabs store their elements one by one, lanes taking
+//     tokens fastest.
 template <int ES, int TT>
 __global__ __launch_bounds__(8 * TT) void reshape_and_cache_kernel(
     const char* __restrict__ k, const char* __restrict__ v, char* __restrict__ k_cache,
     char* __restrict__ v_cache, const int64_t* __restrict__ slots, int32_t num_tokens,
     int64_t k_stride, int64_t v_stride, int32_t hkv, int32_t D, int32_t bs, int64_t num_blocks) {
   using E = typename std::conditional<ES == 4, uint32_t, uint16_t>::type;
-  extern __shared__ __align__(16) char smem[];
-  const int row_bytes = D * ES;
-  const int lds_stride = row_bytes + 4;  // pad: consecutive tokens hit different banks
-  const int h = blockIdx.y;
   constexpr int NT = 8 * TT;
+  extern __shared__ __align__(16) char smem[];
+  const int row_bytes = D * ES;            // a multiple of 16
+  const int pitch = row_bytes + 16;        // LDS row pitch (16-byte aligned, skewed banks)
+  char* sk = smem;
+  char* sv = smem + TT * pitch;
+  int64_t* sslot = reinterpret_cast<int64_t*>(smem + 2 * TT * pitch);
+  int* slead = reinterpret_cast<int*>(sslot + TT);  // token leads a fully written slab
+  int* scov = slead + TT;                          // token lies in such a slab
+  __shared__ int s_leaders[TT / 8 + 1];
+  __shared__ int s_nlead;
+  const int h = blockIdx.y;
   const int t0 = blockIdx.x * TT;
   const int nt = min(TT, num_tokens - t0);
   const int64_t max_slot = num_blocks * (int64_t)bs;
   const int vs = v_slab(bs);
-
-  // K pieces (and V rows into LDS): one 16-byte piece per thread per iteration.
   const int chunks = row_bytes / 16;
-  for (int i = threadIdx.x; i < nt * chunks; i += NT) {
-    const int c = i / nt, tt = i - c * nt;
+
+  if (threadIdx.x < nt) sslot[threadIdx.x] = slots[t0 + threadIdx.x];
+  if (threadIdx.x == 0) s_nlead = 0;
+  for (int i = threadIdx.x; i < nt * chunks; i += NT) {  // lanes along a row
+    const int tt = i / chunks, c = i - tt * chunks;
     const int64_t t = t0 + tt;
-    const int64_t slot = slots[t];
     const uint4 kv = *reinterpret_cast<const uint4*>(k + (t * k_stride + (int64_t)h * D) * ES +
                                                       c * 16);
     const uint4 vv = *reinterpret_cast<const uint4*>(v + (t * v_stride + (int64_t)h * D) * ES +
                                                       c * 16);
-    // LDS row pitch is 4-byte aligned only: store as four dwords
-    uint32_t* dst = reinterpret_cast<uint32_t*>(smem + tt * lds_stride + c * 16);
-    dst[0] = vv.x;
-    dst[1] = vv.y;
-    dst[2] = vv.z;
-    dst[3] = vv.w;
+    *reinterpret_cast<uint4*>(sk + tt * pitch + c * 16) = kv;
+    *reinterpret_cast<uint4*>(sv + tt * pitch + c * 16) = vv;
+  }
+  __syncthreads();
+  if (threadIdx.x < nt) {
+    const int tt = threadIdx.x;
+    const int64_t s0 = sslot[tt];
+    bool lead = vs == 8 && s0 >= 0 && s0 + 7 < max_slot && (s0 & 7) == 0 && tt + 8 <= nt;
+    for (int j = 1; lead && j < 8; ++j) lead = sslot[tt + j] == s0 + j;
+    slead[tt] = lead;
+    if (lead) s_leaders[atomicAdd(&s_nlead, 1)] = tt;
+  }
+  __syncthreads();
+  if (threadIdx.x < nt) {
+    const int tt = threadIdx.x;
+    int cov = 0;
+    for (int j = 0; j < 8 && j <= tt; ++j) cov |= slead[tt - j] && sslot[tt] == sslot[tt - j] + j;
+    scov[tt] = cov;
+  }
+
+  // K pieces: tokens fastest.
+  for (int i = threadIdx.x; i < nt * chunks; i += NT) {
+    const int c = i / nt, tt = i - c * nt;
+    const int64_t slot = sslot[tt];
     if (slot >= 0 && slot < max_slot) {
       const int64_t blk = slot / bs;
       const int off = (int)(slot - blk * bs);
-      *reinterpret_cast<uint4*>(k_cache + (((blk * hkv + h) * chunks + c) * bs + off) * 16) = kv;
+      *reinterpret_cast<uint4*>(k_cache + (((blk * hkv + h) * chunks + c) * bs + off) * 16) =
+          *reinterpret_cast<const uint4*>(sk + tt * pitch + c * 16);
     }
   }
   __syncthreads();
 
-  // V elements: lane = token (fastest), threads stride over d.
+  // V, fully written slabs: one 16-byte piece (8 tokens x 16 / (8 ES) dims)
+  // per thread, dims fastest so a wavefront writes one contiguous run.
+  constexpr int PPR = 8 * ES / 16;  // 16-byte pieces per slab row
+  const int nl = s_nlead;
+  for (int i = threadIdx.x; i < nl * D * PPR; i += NT) {
+    const int li = i / (D * PPR), r = i - li * (D * PPR);
+    const int d = r / PPR, half = r - d * PPR;  // pieces of a row: tokens 0-3 / 4-7 for fp32
+    const int tt = s_leaders[li];
+    const int64_t slot = sslot[tt];
+    const int64_t blk = slot / bs;
+    const int off = (int)(slot - blk * bs);
+    E e[16 / ES];
+#pragma unroll
+    for (int u = 0; u < 16 / ES; ++u)
+      e[u] = *reinterpret_cast<const E*>(sv + (tt + half * (16 / ES) + u) * pitch + d * ES);
+    char* dst = v_cache + ((((blk * hkv + h) * (bs / 8) + off / 8) * D + d) * 8) * ES + half * 16;
+    *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(e);
+  }
+
+  // V, tokens of partly written slabs: element by element, tokens fastest.
   const int tt = threadIdx.x % TT;
   const int dgrp = threadIdx.x / TT;
-  if (tt >= nt) return;
-  const int64_t slot = slots[t0 + tt];
+  if (tt >= nt || scov[tt]) return;
+  const int64_t slot = sslot[tt];
   if (slot < 0 || slot >= max_slot) return;
   const int64_t blk = slot / bs;
   const int off = (int)(slot - blk * bs);
   E* vdst = reinterpret_cast<E*>(v_cache) + ((blk * hkv + h) * (bs / vs) + off / vs) * (int64_t)D * vs +
             off % vs;
-  const E* src = reinterpret_cast<const E*>(smem + tt * lds_stride);
+  const E* src = reinterpret_cast<const E*>(sv + tt * pitch);
   for (int d = dgrp; d < D; d += NT / TT) vdst[(int64_t)d * vs] = src[d];
 }
 
@@ -128,7 +178,8 @@ void launch_rc(const void* k, const void* v, void* k_cache, void* v_cache, const
                int32_t num_tokens, int64_t k_stride, int64_t v_stride, int32_t hkv, int32_t D,
                int32_t bs, int64_t num_blocks, int es, hipStream_t s) {
   dim3 grid((num_tokens + TT - 1) / TT, hkv);
-  const size_t lds = (size_t)TT * (D * es + 4);
+  // K and V rows, slots, two flags per token
+  const size_t lds = (size_t)TT * (2 * (D * es + 16) + 8 + 8);
   if (es == 4)
     hipLaunchKernelGGL((reshape_and_cache_kernel<4, TT>), grid, dim3(8 * TT), lds, s,
                        (const char*)k, (const char*)v, (char*)k_cache, (char*)v_cache, slots,

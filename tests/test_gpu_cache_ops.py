@@ -47,6 +47,55 @@ def test_reshape_and_cache_bit_exact(dtype, hkv, D, bs, T):
     assert np.array_equal(W.to_numpy_bits(vc), vr)
 
 
+def _runs_of_slots(rng, nb, bs, T):
+    """Slots as a prompt chunk lays them out: runs of consecutive slots inside
+    blocks (whole 8-token slabs, runs that start and end mid-slab), a few
+    scattered single slots, a few padding tokens and one out-of-range slot."""
+    blocks = rng.permutation(nb)
+    out, bi = [], 0
+    while len(out) < T:
+        b = int(blocks[bi % nb]); bi += 1
+        start = int(rng.choice([0, 0, 3, 8, 5])) % bs
+        n = int(rng.integers(1, bs - start + 1))
+        out.extend(b * bs + start + j for j in range(n))
+    out = np.array(out[:T], dtype=np.int64)
+    _, first = np.unique(out, return_index=True)
+    keep = np.zeros(T, dtype=bool)
+    keep[first] = True
+    out[~keep] = -1  # a block drawn twice: later repeats become padding
+    out[rng.random(T) < 0.03] = -1
+    out[T // 2] = nb * bs + 1
+    return out
+
+
+@pytest.mark.parametrize("dtype,hkv,D,bs,T", [
+    ("f16", 8, 128, 16, 2000),
+    ("bf16", 4, 128, 32, 1500),
+    ("f16", 4, 64, 8, 1100),
+    ("f32", 2, 64, 16, 1050),
+    ("bf16", 2, 256, 128, 1300),
+    ("f16", 2, 128, 4, 1024),
+    ("f16", 8, 128, 16, 300),
+])
+def test_reshape_and_cache_runs_bit_exact(dtype, hkv, D, bs, T):
+    """Large writes of consecutive slots (the whole-slab path) mixed with
+    partial slabs and scattered slots: bit-exact against the oracle."""
+    log(f"[write runs] {dtype} hkv={hkv} D={D} bs={bs} T={T}")
+    rng = np.random.default_rng(T + bs)
+    nb = -(-T // bs) * 3 + 4
+    slots = _runs_of_slots(rng, nb, bs, T)
+    kc, vc = _pool(nb, hkv, bs, D, dtype, 7)
+    k, v = W.new_token_rows(T, hkv, D, dtype, W.make_generator(8, DEV), DEV)
+    kr, vr = W.to_numpy_bits(kc).copy(), W.to_numpy_bits(vc).copy()
+    ok = np.where(slots >= nb * bs, -1, slots)
+    oracle.get().reshape_and_cache(W.to_numpy_bits(k), W.to_numpy_bits(v), kr, vr, ok, hkv, D, bs,
+                                   dtype)
+    pa.pa_reshape_and_cache(k, v, kc, vc, torch.from_numpy(slots).to(DEV), bs)
+    torch.cuda.synchronize()
+    assert np.array_equal(W.to_numpy_bits(kc), kr)
+    assert np.array_equal(W.to_numpy_bits(vc), vr)
+
+
 def test_reshape_and_cache_strided_rows():
     """k and v as views into a fused [T][3][Hkv][D] buffer (token stride 3*Hkv*D)."""
     T, hkv, D, bs, nb = 50, 4, 128, 16, 8
