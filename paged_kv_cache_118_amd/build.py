@@ -29,6 +29,12 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
+# Per-source code generation options.  The chunked-prefill kernel keeps its
+# MFMA accumulators in ordinary VGPRs: with accumulation registers the compiler
+# copied all of them to VGPRs on every key group.
+EXTRA_FLAGS = {"prefill_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _compile(src: str, obj: str) -> None:
     is_hip = src.endswith(".hip")
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall",
@@ -36,6 +42,7 @@ def _compile(src: str, obj: str) -> None:
     if is_hip:
         cmd[1:1] = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                     "-ffp-contract=fast", "-munsafe-fp-atomics"]
+        cmd[1:1] = EXTRA_FLAGS.get(os.path.basename(src), [])
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

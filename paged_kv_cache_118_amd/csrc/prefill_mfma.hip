@@ -59,6 +59,13 @@ __device__ __forceinline__ uint32_t pack2(TT t, float lo, float hi) {
 struct TableWindow {
   int base = 0x7fffffff;
   int entry = 0;
+  __device__ __forceinline__ void load(const int32_t* row, int nblk, int64_t num_blocks, int lb,
+                                       int lane) {
+    base = lb;
+    const int idx = lb + lane;
+    const int e = idx < nblk ? row[idx] : 0;
+    entry = (e < 0 || (int64_t)e >= num_blocks) ? 0 : e;
+  }
   __device__ __forceinline__ void ensure(const int32_t* row, int nblk, int64_t num_blocks, int lb,
                                          int n, int lane) {
     if (lb < base || lb + n - base > 64) {
@@ -73,7 +80,16 @@ struct TableWindow {
   }
 };
 
-template <typename TT, int D>
+// Slack of the running maximum (base-2 exponent): the output accumulators are
+// rescaled only when a row's maximum grows by more than this, so the weights
+// exp2(s - m) stay below 2^kSlack -- harmless in fp32 sums and 16-bit P
+// (relative precision does not depend on magnitude) -- and most key groups
+// skip the rescale altogether.
+constexpr float kSlack = 8.f;
+
+// NBG = physical blocks one 32-key group spans: 4 (block size 8), 2 (16),
+// 1 (a multiple of 32).
+template <typename TT, int D, int NBG>
 __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
   constexpr int VS = 8;       // V slab width (tokens)
   constexpr int EB = 2;
@@ -110,8 +126,13 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
   const int mypos = pos0 + (n < nrows ? n : nrows - 1);  // this lane's query position
   const int64_t g = h / G;
   const int64_t hkv = a.num_kv_heads;
-  const int bs = a.block_size;
-  const int nb_grp = bs >= kKeys ? 1 : kKeys / bs;  // blocks one group touches
+  // block size: a compile-time constant for groups spanning 2 or 4 blocks
+  constexpr int BSC = NBG == 4 ? 8 : NBG == 2 ? 16 : 0;
+  const int bs = BSC ? BSC : a.block_size;
+  const int64_t kblock = (int64_t)hkv * NC * bs * 16;  // bytes of one block of the K pool
+  const int64_t vblock = (int64_t)hkv * D * bs * EB;   // ... and of the V pool
+  const int64_t khead = g * NC * bs * 16, vhead = g * D * bs * EB;
+  const int pstride = 4 * bs * 16;  // bytes from K piece p to p + 4
 
   const char* kbase = reinterpret_cast<const char*>(a.k_cache);
   const char* vbase = reinterpret_cast<const char*>(a.v_cache);
@@ -127,8 +148,6 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
 #pragma unroll
     for (int s = 0; s < KN; ++s) qr[s] = n < nrows ? ld16(qp + 64 * s) : make_uint4(0, 0, 0, 0);
   }
-  const char* cached = qbase + ((int64_t)qs * a.num_q_heads + h) * D * EB +
-                       ((lane * 16) & (D * EB - 1));  // bytes this wavefront holds in cache
 
   float m_run = -INFINITY, l_lane = 0.f;
   float4_t acc[MT];
@@ -136,45 +155,62 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
   for (int mt = 0; mt < MT; ++mt) acc[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
 
   TableWindow tw;
-  const int64_t pstride = (int64_t)4 * bs * 16;  // bytes from K piece p to p + 4
   const int ngroups = last / kKeys + 1;
-  // One group at a time: a second (prefetch) register set measured slower
-  // (it costs occupancy); the other resident wavefronts cover the latency.
-  for (int grp = 0; grp < ngroups; ++grp) {
-    const int tok = grp * kKeys;
-    const int nv = last + 1 - tok;  // keys of the group at positions <= last (>= 1)
-    const int lb0 = tok / bs;
-    tw.ensure(trow, a.max_blocks_per_seq, a.num_blocks, lb0, nb_grp, lane);
-    // K: two 16-key tiles; lane (n, kb) loads key 16 j + n, pieces kb + 4 i.
-    uint4 kr[2][KN];
+  // Keys past `last` are loaded from `last`'s own position instead (valid,
+  // finite data; their scores are masked), so every load is a plain load of
+  // the pool.  Only a V slab that reaches past the context can hold bytes
+  // that were never written (NaN in tests): those elements are zeroed.
+  const bool vtail = (last | (VS - 1)) >= L;
+
+  // Loads of group grp into (kr, vr).  K: two 16-key tiles, lane (n, kb)
+  // loads key 16 j + n, pieces kb + 4 i.  V: the 8-token run of k-group kb,
+  // one 16-byte slab row per d tile.  A group past the window (issued to
+  // keep the pipeline's load count fixed) reloads `last`'s keys.
+  // Lane parts of the load addresses (bytes within a block's head run).
+  const uint32_t klane = (uint32_t)kb * bs * 16;  // K piece kb of offset 0
+  const uint32_t vlane = (uint32_t)n * VS * EB;   // V slab row d = n of slab 0
+
+  auto issue = [&](int grp, int gend, uint4 (&kr)[2][KN], uint4 (&vr)[MT]) {
+    // uniform: the group's first key, its block and offset there, and the
+    // last key the tile needs relative to it
+    const int tok = (grp < gend ? grp : gend - 1) * kKeys;
+    const int lb0 = BSC ? tok / BSC : tok / bs;
+    const uint32_t o0 = (uint32_t)(tok - lb0 * bs);  // 0 unless NBG == 1
+    const uint32_t lim = (uint32_t)(last - tok);
+    // the head's run in each block the group spans (uniform pointers)
+    const char* kblk[NBG];
+    const char* vblk[NBG];
+#pragma unroll
+    for (int q = 0; q < NBG; ++q) {
+      const int64_t ph = tw.get(lb0 + q);
+      kblk[q] = kbase + ph * kblock + khead;
+      vblk[q] = vbase + ph * vblock + vhead;
+    }
+    auto pick = [&](const char* const (&b)[NBG], uint32_t rel) {  // block of key tok + rel
+      const char* p = b[0];
+      if constexpr (NBG > 1) {
+#pragma unroll
+        for (int u = 1; u < NBG; ++u) p = rel >= (uint32_t)(u * BSC) ? b[u] : p;
+      }
+      return p;
+    };
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const bool live = 16 * j < nv;
-      const int t = tok + 16 * j + (16 * j + n < nv ? n : 0);
-      const int lb = t / bs;
-      int64_t phys = tw.get(lb0);
-      for (int q = 1; q < nb_grp; ++q)
-        if (lb == lb0 + q) phys = tw.get(lb0 + q);
-      const char* kp = kbase + (((phys * hkv + g) * NC + kb) * bs + (t - lb * bs)) * 16;
+      const uint32_t rel = min((uint32_t)(16 * j + n), lim);
+      const uint32_t off = NBG == 1 ? o0 + rel : rel & (uint32_t)(BSC - 1);
+      const char* kp = pick(kblk, rel) + (klane + off * 16);
 #pragma unroll
-      for (int i = 0; i < KN; ++i) kr[j][i] = ld16(live ? kp + i * pstride : cached);
+      for (int i = 0; i < KN; ++i) kr[j][i] = ld16(kp + i * pstride);
     }
-    // V: the 8-token run of k-group kb, one 16-byte slab row per d tile.
-    uint4 vr[MT];
-    {
-      const bool run = kb * 8 < nv;
-      const int t = tok + kb * 8;
-      const int lb = t / bs;
-      int64_t phys = tw.get(lb0);
-      for (int q = 1; q < nb_grp; ++q)
-        if (lb == lb0 + q) phys = tw.get(lb0 + q);
-      const int off = t - lb * bs;
-      const char* vp = vbase + ((((phys * hkv + g) * (bs / VS) + off / VS) * D + n) * VS) * EB;
+    const uint32_t relv = min((uint32_t)(VS * kb), lim & ~(uint32_t)(VS - 1));
+    const uint32_t offv = NBG == 1 ? o0 + relv : relv & (uint32_t)(BSC - 1);
+    const char* vp = pick(vblk, relv) + (vlane + offv / VS * (D * VS * EB));
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        vr[mt] = ld16(run ? vp + (int64_t)mt * 16 * VS * EB : cached);
-    }
+    for (int mt = 0; mt < MT; ++mt) vr[mt] = ld16(vp + mt * 16 * VS * EB);
+  };
 
+  auto compute = [&](int grp, const uint4 (&kr)[2][KN], uint4 (&vr)[MT]) {
+    const int tok = grp * kKeys;
     float4_t st[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -192,7 +228,7 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {  // key of sc[e]: 4 kb + e, then 16 + 4 kb + e - 4
         const int u = tok + (e < 4 ? 4 * kb + e : 12 + 4 * kb + e);
-        if (u > mypos) sc[e] = -INFINITY;  // select: keys past `last` may be NaN
+        if (u > mypos) sc[e] = -INFINITY;  // select: masked scores may be NaN
       }
     }
     float mx = sc[0];
@@ -200,18 +236,22 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
     for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sc[e]);
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);  // finite: key 0 is in every row's range
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    float pw[8], psum = 0.f;
+    // mx is finite: key 0 is in every row's range, and the first group of
+    // every row reaches here with m_run = -inf
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + kSlack) != 0) {
+      const float m_new = mx > m_run + kSlack ? mx : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_lane *= alpha;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[mt] *= alpha;
+      m_run = m_new;
+    }
+    float pw[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      pw[e] = __builtin_amdgcn_exp2f(sc[e] - m_new);
-      psum += pw[e];
+      pw[e] = __builtin_amdgcn_exp2f(sc[e] - m_run);
+      l_lane += pw[e];
     }
-    l_lane = l_lane * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[mt] *= alpha;
     // P^T operand: lane kb needs keys 8 kb .. 8 kb + 7 of query n, the 4-key
     // runs of tile kb / 2 held by k-groups 2 (kb % 2) and 2 (kb % 2) + 1.
     const uint32_t t0a = pack2(TT{}, pw[0], pw[1]), t0b = pack2(TT{}, pw[2], pw[3]);
@@ -224,8 +264,8 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
     const uint32_t b0 = __builtin_amdgcn_ds_bpermute(src2, ev ? t1a : t0a);
     const uint32_t b1 = __builtin_amdgcn_ds_bpermute(src2, ev ? t1b : t0b);
     const uint4 pb = kb < 2 ? make_uint4(a0, a1, b0, b1) : make_uint4(b0, b1, a0, a1);
-    if (nv < kKeys) {  // zero V of keys past `last` (their bits may be NaN)
-      const int keep = min(max(nv - kb * 8, 0), 8);
+    if (vtail && tok + kKeys > last) {  // zero V of positions past `last` in this group
+      const int keep = min(max(last + 1 - tok - kb * VS, 0), VS);
       uint32_t m4[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -240,6 +280,27 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
     }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma(TT{}, vr[mt], pb, acc[mt]);
+  };
+
+  // The keys are walked in windows of the 64 blocks one table load covers;
+  // inside a window, two register sets alternate so that the loads of the
+  // next group are in flight while the current one is computed.  Every
+  // window issues its groups' loads in the same fixed pattern (a group past
+  // the window reloads the last one and is never computed), which keeps the
+  // compiler's wait counts exact.
+  constexpr int kGpw = 64 / NBG;  // groups per window (64 blocks, less one group's spill)
+  const int gpw = NBG == 1 ? 64 * bs / kKeys : kGpw;
+  uint4 kr0[2][KN], vr0[MT], kr1[2][KN], vr1[MT];
+  for (int w0 = 0; w0 < ngroups; w0 += gpw) {
+    const int w1 = ngroups < w0 + gpw ? ngroups : w0 + gpw;
+    tw.load(trow, a.max_blocks_per_seq, a.num_blocks, w0 * kKeys / bs, lane);
+    issue(w0, w1, kr0, vr0);
+    for (int grp = w0; grp < w1; grp += 2) {
+      issue(grp + 1, w1, kr1, vr1);
+      compute(grp, kr0, vr0);
+      issue(grp + 2, w1, kr0, vr0);
+      if (grp + 1 < w1) compute(grp + 1, kr1, vr1);
+    }
   }
 
   float l_tot = l_lane + __shfl_xor(l_lane, 16);
@@ -255,15 +316,22 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
   }
 }
 
-template <typename TT, int D>
-hipError_t launch_d(const PrefillArgs& a, hipStream_t s) {
+template <typename TT, int D, int NBG>
+hipError_t launch_g(const PrefillArgs& a, hipStream_t s) {
   const int64_t tpg = (a.max_query_len + kWaves * kRows - 1) / (kWaves * kRows);
   const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads;
   const int64_t wgs = (units + 7) / 8 * 8 * (a.num_q_heads / a.num_kv_heads) * tpg;
   if (wgs > 0x7fffffff) return hipErrorInvalidValue;
   dim3 grid((unsigned)wgs);
-  hipLaunchKernelGGL((prefill_mfma_kernel<TT, D>), grid, dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((prefill_mfma_kernel<TT, D, NBG>), grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
+}
+
+template <typename TT, int D>
+hipError_t launch_d(const PrefillArgs& a, hipStream_t s) {
+  if (a.block_size == 8) return launch_g<TT, D, 4>(a, s);
+  if (a.block_size == 16) return launch_g<TT, D, 2>(a, s);
+  return launch_g<TT, D, 1>(a, s);
 }
 
 }  // namespace
