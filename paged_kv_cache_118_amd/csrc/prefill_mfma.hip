@@ -12,10 +12,11 @@
 //
 // Unlike decode, each K/V element now meets many queries, so the work is a
 // real dense contraction.  A wavefront owns 16 query rows of one q head; a
-// workgroup holds four consecutive 16-row tiles of the same head, and all
-// workgroups reading one kv head's K/V run on one XCD at about the same
-// time, so the cache lines of a key group come from HBM about once and are
-// served to the others from L2 (plain, temporal loads).  With lane = 16*kb + n and v_mfma_f32_16x16x32:
+// workgroup holds four consecutive 16-row tiles of the same head and stages
+// each key group's K/V once in LDS for all four; all workgroups reading one
+// kv head's K/V run on one XCD at about the same time, so the cache lines of
+// a key group come from HBM about once and are served to the others from L2
+// (plain, temporal loads).  With lane = 16*kb + n and v_mfma_f32_16x16x32:
 //   S^T = K Q^T  : A = 16 keys x 32 dims (16-byte K pieces, as in decode),
 //                  B = Q^T (query row n), two 16-key tiles per 32-key group;
 //                  lane (n, kb) gets query n's scores of keys 4kb .. 4kb+3
@@ -89,6 +90,17 @@ constexpr float kSlack = 8.f;
 
 // NBG = physical blocks one 32-key group spans: 4 (block size 8), 2 (16),
 // 1 (a multiple of 32).
+//
+// The four wavefronts of a workgroup hold 64 consecutive query rows of one q
+// head and need the same keys, so each 32-key group's K and V are loaded from
+// the pool once per workgroup, by all 256 threads (16-byte loads, whole cache
+// lines), into LDS, and every wavefront reads its MFMA operands from there.
+// Two LDS buffers alternate: while the wavefronts compute group g from one,
+// the loads of group g + 1 are in flight in registers and are written to the
+// other buffer at the top of the next step; one barrier per group.
+//   K in LDS: 32 rows [key][D], pitch D*2 + 16 bytes (the 16 keys one
+//             operand read touches fall in distinct banks);
+//   V in LDS: 4 slabs of 8 keys, [slab][D][8], as in the pool.
 template <typename TT, int D, int NBG>
 __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
   constexpr int VS = 8;       // V slab width (tokens)
@@ -96,9 +108,18 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
   constexpr int KN = D / 32;  // k-steps of S^T
   constexpr int MT = D / 16;  // d tiles of O^T
   constexpr int NC = D / 8;   // 16-byte K pieces per token
+  constexpr int KP = D * EB + 16;          // LDS pitch of a K row
+  constexpr int VSP = D * VS * EB + 16;    // LDS pitch of a V slab
+  constexpr int KBUF = kKeys * KP;
+  constexpr int BUF = KBUF + (kKeys / VS) * VSP;
+  constexpr int NCK = kKeys * NC / kThreads;       // K chunks per thread and group
+  constexpr int NCV = (kKeys / VS) * D / kThreads;  // V chunks per thread and group
+  static_assert(NCK >= 1 && NCV >= 1, "head_dim too small for the cooperative load");
+  __shared__ __align__(16) char lds[2 * BUF];
 
-  const int lane = threadIdx.x & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, kb = lane >> 4;
   const int G = a.num_q_heads / a.num_kv_heads;
   // XCD-aware order: workgroups are dealt to the 8 XCDs round-robin by id, so
@@ -113,17 +134,18 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
   if (unit >= a.num_seqs * a.num_kv_heads) return;
   const int seq = unit / a.num_kv_heads;
   const int h = (unit % a.num_kv_heads) * G + sub / tpg;
-  const int tile = (sub % tpg) * kWaves + wv;
   const int qs = a.query_start[seq];
   const int ql = a.query_start[seq + 1] - qs;
   int L = a.context_lens[seq];
   L = L < 0 ? 0 : (L > a.len_cap ? a.len_cap : L);
-  const int r0 = tile * kRows;
-  if (ql <= 0 || ql > L || r0 >= ql) return;  // (ql > L is a caller error: rows left alone)
-  const int nrows = ql - r0 < kRows ? ql - r0 : kRows;
-  const int pos0 = L - ql + r0;          // position of the tile's first row
-  const int last = pos0 + nrows - 1;     // position of its last valid row
-  const int mypos = pos0 + (n < nrows ? n : nrows - 1);  // this lane's query position
+  const int rwg = (sub % tpg) * kWaves * kRows;  // the workgroup's first row
+  if (ql <= 0 || ql > L || rwg >= ql) return;   // (ql > L is a caller error: rows left alone)
+  const int last_wg = L - ql + min(ql, rwg + kWaves * kRows) - 1;  // last position any row needs
+  const int r0 = rwg + wv * kRows;                 // this wavefront's first row
+  const int nrows = max(0, min(ql - r0, kRows));   // 0: the wavefront only helps to load
+  const int pos0 = L - ql + r0;                    // position of the tile's first row
+  const int last = pos0 + max(nrows, 1) - 1;       // position of its last valid row
+  const int mypos = pos0 + (n < nrows ? n : max(nrows, 1) - 1);  // this lane's query position
   const int64_t g = h / G;
   const int64_t hkv = a.num_kv_heads;
   // block size: a compile-time constant for groups spanning 2 or 4 blocks
@@ -132,7 +154,6 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
   const int64_t kblock = (int64_t)hkv * NC * bs * 16;  // bytes of one block of the K pool
   const int64_t vblock = (int64_t)hkv * D * bs * EB;   // ... and of the V pool
   const int64_t khead = g * NC * bs * 16, vhead = g * D * bs * EB;
-  const int pstride = 4 * bs * 16;  // bytes from K piece p to p + 4
 
   const char* kbase = reinterpret_cast<const char*>(a.k_cache);
   const char* vbase = reinterpret_cast<const char*>(a.v_cache);
@@ -143,7 +164,7 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
   // rows past the chunk).
   uint4 qr[KN];
   {
-    const int64_t row = (int64_t)qs + r0 + (n < nrows ? n : 0);
+    const int64_t row = (int64_t)qs + (n < nrows ? r0 + n : 0);
     const char* qp = qbase + ((row * a.num_q_heads + h) * D + kb * 8) * EB;
 #pragma unroll
     for (int s = 0; s < KN; ++s) qr[s] = n < nrows ? ld16(qp + 64 * s) : make_uint4(0, 0, 0, 0);
@@ -155,29 +176,23 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
   for (int mt = 0; mt < MT; ++mt) acc[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
 
   TableWindow tw;
-  const int ngroups = last / kKeys + 1;
-  // Keys past `last` are loaded from `last`'s own position instead (valid,
-  // finite data; their scores are masked), so every load is a plain load of
-  // the pool.  Only a V slab that reaches past the context can hold bytes
-  // that were never written (NaN in tests): those elements are zeroed.
-  const bool vtail = (last | (VS - 1)) >= L;
+  const int ngroups = last_wg / kKeys + 1;
+  // Keys past the workgroup's last position are loaded from that position
+  // instead (valid, finite data; their scores are masked).  Only a V slab
+  // that reaches past the context can hold bytes that were never written
+  // (NaN in tests): those elements are zeroed after the operand read.
+  const bool vtail = (last_wg | (VS - 1)) >= L;
 
-  // Loads of group grp into (kr, vr).  K: two 16-key tiles, lane (n, kb)
-  // loads key 16 j + n, pieces kb + 4 i.  V: the 8-token run of k-group kb,
-  // one 16-byte slab row per d tile.  A group past the window (issued to
-  // keep the pipeline's load count fixed) reloads `last`'s keys.
-  // Lane parts of the load addresses (bytes within a block's head run).
-  const uint32_t klane = (uint32_t)kb * bs * 16;  // K piece kb of offset 0
-  const uint32_t vlane = (uint32_t)n * VS * EB;   // V slab row d = n of slab 0
-
-  auto issue = [&](int grp, int gend, uint4 (&kr)[2][KN], uint4 (&vr)[MT]) {
-    // uniform: the group's first key, its block and offset there, and the
-    // last key the tile needs relative to it
-    const int tok = (grp < gend ? grp : gend - 1) * kKeys;
+  // Cooperative loads of group grp into registers: K chunk c = tid + 256 r
+  // is piece c / 32 of key c % 32; V chunk c is row c % D of slab c / D.
+  uint4 pk[NCK], pv[NCV];
+  auto load = [&](int grp) {
+    const int tok = grp * kKeys;
     const int lb0 = BSC ? tok / BSC : tok / bs;
+    if (lb0 < tw.base || lb0 + NBG > tw.base + 64)
+      tw.load(trow, a.max_blocks_per_seq, a.num_blocks, lb0, lane);
     const uint32_t o0 = (uint32_t)(tok - lb0 * bs);  // 0 unless NBG == 1
-    const uint32_t lim = (uint32_t)(last - tok);
-    // the head's run in each block the group spans (uniform pointers)
+    const uint32_t lim = (uint32_t)(last_wg - tok);
     const char* kblk[NBG];
     const char* vblk[NBG];
 #pragma unroll
@@ -195,29 +210,47 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
       return p;
     };
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const uint32_t rel = min((uint32_t)(16 * j + n), lim);
+    for (int r = 0; r < NCK; ++r) {
+      const int c = tid + kThreads * r;
+      const uint32_t rel = min((uint32_t)(c % kKeys), lim);
       const uint32_t off = NBG == 1 ? o0 + rel : rel & (uint32_t)(BSC - 1);
-      const char* kp = pick(kblk, rel) + (klane + off * 16);
-#pragma unroll
-      for (int i = 0; i < KN; ++i) kr[j][i] = ld16(kp + i * pstride);
+      pk[r] = ld16(pick(kblk, rel) + ((uint32_t)(c / kKeys) * bs + off) * 16);
     }
-    const uint32_t relv = min((uint32_t)(VS * kb), lim & ~(uint32_t)(VS - 1));
-    const uint32_t offv = NBG == 1 ? o0 + relv : relv & (uint32_t)(BSC - 1);
-    const char* vp = pick(vblk, relv) + (vlane + offv / VS * (D * VS * EB));
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) vr[mt] = ld16(vp + mt * 16 * VS * EB);
+    for (int r = 0; r < NCV; ++r) {
+      const int c = tid + kThreads * r;
+      const uint32_t relv = min((uint32_t)(c / D) * VS, lim & ~(uint32_t)(VS - 1));
+      const uint32_t offv = NBG == 1 ? o0 + relv : relv & (uint32_t)(BSC - 1);
+      pv[r] = ld16(pick(vblk, relv) + ((offv / VS) * D + (uint32_t)(c % D)) * (VS * EB));
+    }
+  };
+  auto store = [&](char* buf) {
+#pragma unroll
+    for (int r = 0; r < NCK; ++r) {
+      const int c = tid + kThreads * r;
+      *reinterpret_cast<uint4*>(buf + (c % kKeys) * KP + (c / kKeys) * 16) = pk[r];
+    }
+#pragma unroll
+    for (int r = 0; r < NCV; ++r) {
+      const int c = tid + kThreads * r;
+      *reinterpret_cast<uint4*>(buf + KBUF + (c / D) * VSP + (c % D) * 16) = pv[r];
+    }
   };
 
-  auto compute = [&](int grp, const uint4 (&kr)[2][KN], uint4 (&vr)[MT]) {
+  auto compute = [&](int grp, const char* buf) {
     const int tok = grp * kKeys;
+    // Operands are read from LDS next to the matrix op that takes them (fewer
+    // registers, four wavefronts per SIMD to cover the reads).
     float4_t st[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       st[j] = float4_t{0.f, 0.f, 0.f, 0.f};
+      const char* kr = buf + (16 * j + n) * KP + kb * 16;
 #pragma unroll
-      for (int i = 0; i < KN; ++i) st[j] = mfma(TT{}, kr[j][i], qr[i], st[j]);
+      for (int i = 0; i < KN; ++i)
+        st[j] = mfma(TT{}, *reinterpret_cast<const uint4*>(kr + 64 * i), qr[i], st[j]);
     }
+    const char* vr = buf + KBUF + kb * VSP + n * 16;  // V^T operand: slab kb, row d = n + 16 mt
     float sc[8];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -272,35 +305,29 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
         m4[i] = ((2 * i < keep) ? 0xffffu : 0u) | ((2 * i + 1 < keep) ? 0xffff0000u : 0u);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        vr[mt].x &= m4[0];
-        vr[mt].y &= m4[1];
-        vr[mt].z &= m4[2];
-        vr[mt].w &= m4[3];
+        uint4 v = *reinterpret_cast<const uint4*>(vr + mt * 16 * 16);
+        v.x &= m4[0];
+        v.y &= m4[1];
+        v.z &= m4[2];
+        v.w &= m4[3];
+        acc[mt] = mfma(TT{}, v, pb, acc[mt]);
       }
-    }
+    } else {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma(TT{}, vr[mt], pb, acc[mt]);
+      for (int mt = 0; mt < MT; ++mt)
+        acc[mt] = mfma(TT{}, *reinterpret_cast<const uint4*>(vr + mt * 16 * 16), pb, acc[mt]);
+    }
   };
 
-  // The keys are walked in windows of the 64 blocks one table load covers;
-  // inside a window, two register sets alternate so that the loads of the
-  // next group are in flight while the current one is computed.  Every
-  // window issues its groups' loads in the same fixed pattern (a group past
-  // the window reloads the last one and is never computed), which keeps the
-  // compiler's wait counts exact.
-  constexpr int kGpw = 64 / NBG;  // groups per window (64 blocks, less one group's spill)
-  const int gpw = NBG == 1 ? 64 * bs / kKeys : kGpw;
-  uint4 kr0[2][KN], vr0[MT], kr1[2][KN], vr1[MT];
-  for (int w0 = 0; w0 < ngroups; w0 += gpw) {
-    const int w1 = ngroups < w0 + gpw ? ngroups : w0 + gpw;
-    tw.load(trow, a.max_blocks_per_seq, a.num_blocks, w0 * kKeys / bs, lane);
-    issue(w0, w1, kr0, vr0);
-    for (int grp = w0; grp < w1; grp += 2) {
-      issue(grp + 1, w1, kr1, vr1);
-      compute(grp, kr0, vr0);
-      issue(grp + 2, w1, kr0, vr0);
-      if (grp + 1 < w1) compute(grp + 1, kr1, vr1);
-    }
+  load(0);
+  for (int grp = 0; grp < ngroups; ++grp) {
+    char* buf = lds + (grp & 1) * BUF;
+    store(buf);
+    if (grp + 1 < ngroups) load(grp + 1);
+    __syncthreads();
+    // wavefronts without rows, or whose rows all end before this group,
+    // only help with the loads
+    if (nrows > 0 && grp * kKeys <= last) compute(grp, buf);
   }
 
   float l_tot = l_lane + __shfl_xor(l_lane, 16);
