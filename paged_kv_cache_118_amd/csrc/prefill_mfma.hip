@@ -17,12 +17,12 @@
 // kv head's K/V run on one XCD at about the same time, so the cache lines of
 // a key group come from HBM about once and are served to the others from L2
 // (plain, temporal loads).  With lane = 16*kb + n and v_mfma_f32_16x16x32:
-//   S^T = K Q^T  : A = 16 keys x 32 dims (16-byte K pieces, as in decode),
-//                  B = Q^T (query row n), two 16-key tiles per 32-key group;
-//                  lane (n, kb) gets query n's scores of keys 4kb .. 4kb+3
-//                  and 16+4kb .. 16+4kb+3.
+//   S^T = K Q^T  : A = 16 keys x 32 dims (16-byte K pieces), B = Q^T (query
+//                  row n), two 16-key tiles per 32-key group whose rows are
+//                  ordered so that lane (n, kb) gets query n's scores of keys
+//                  8kb .. 8kb+7;
 //   O^T += V^T P^T : A = 16 dims x 32 keys (one 16-byte row of an 8-token V
-//                  slab per k-group), B = P^T gathered with four lane permutes.
+//                  slab per k-group), B = P^T, those eight scores packed.
 // The mask compares each key's position with the lane's query position, so
 // only the groups that reach past the tile's first row pay for it.
 #include <math.h>
@@ -241,11 +241,15 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
     const int tok = grp * kKeys;
     // Operands are read from LDS next to the matrix op that takes them (fewer
     // registers, four wavefronts per SIMD to cover the reads).
+    // Row r of tile j's A operand is key 8 (r / 4) + 4 j + r % 4, so the
+    // output lane (n, kb) holds query n's scores of keys 8 kb .. 8 kb + 3
+    // (tile 0) and 8 kb + 4 .. 8 kb + 7 (tile 1): exactly the eight keys its
+    // slice of the P^T operand needs, with no lane exchange.
     float4_t st[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       st[j] = float4_t{0.f, 0.f, 0.f, 0.f};
-      const char* kr = buf + (16 * j + n) * KP + kb * 16;
+      const char* kr = buf + (8 * (n >> 2) + 4 * j + (n & 3)) * KP + kb * 16;
 #pragma unroll
       for (int i = 0; i < KN; ++i)
         st[j] = mfma(TT{}, *reinterpret_cast<const uint4*>(kr + 64 * i), qr[i], st[j]);
@@ -259,10 +263,8 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
     }
     if (tok + kKeys - 1 > pos0) {  // the group reaches past the tile's first row
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {  // key of sc[e]: 4 kb + e, then 16 + 4 kb + e - 4
-        const int u = tok + (e < 4 ? 4 * kb + e : 12 + 4 * kb + e);
-        if (u > mypos) sc[e] = -INFINITY;  // select: masked scores may be NaN
-      }
+      for (int e = 0; e < 8; ++e)  // key of sc[e]: 8 kb + e
+        if (tok + 8 * kb + e > mypos) sc[e] = -INFINITY;  // select: masked scores may be NaN
     }
     float mx = sc[0];
 #pragma unroll
@@ -285,18 +287,9 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
       pw[e] = __builtin_amdgcn_exp2f(sc[e] - m_run);
       l_lane += pw[e];
     }
-    // P^T operand: lane kb needs keys 8 kb .. 8 kb + 7 of query n, the 4-key
-    // runs of tile kb / 2 held by k-groups 2 (kb % 2) and 2 (kb % 2) + 1.
-    const uint32_t t0a = pack2(TT{}, pw[0], pw[1]), t0b = pack2(TT{}, pw[2], pw[3]);
-    const uint32_t t1a = pack2(TT{}, pw[4], pw[5]), t1b = pack2(TT{}, pw[6], pw[7]);
-    const bool ev = (kb & 1) == 0;
-    const int p1 = ((kb & 1) << 1) | (kb >> 1);
-    const int src1 = (n + 16 * p1) * 4, src2 = (n + 16 * (p1 ^ 1)) * 4;
-    const uint32_t a0 = __builtin_amdgcn_ds_bpermute(src1, ev ? t0a : t1a);
-    const uint32_t a1 = __builtin_amdgcn_ds_bpermute(src1, ev ? t0b : t1b);
-    const uint32_t b0 = __builtin_amdgcn_ds_bpermute(src2, ev ? t1a : t0a);
-    const uint32_t b1 = __builtin_amdgcn_ds_bpermute(src2, ev ? t1b : t0b);
-    const uint4 pb = kb < 2 ? make_uint4(a0, a1, b0, b1) : make_uint4(b0, b1, a0, a1);
+    // P^T operand: keys 8 kb .. 8 kb + 7 of query n, all held by this lane
+    const uint4 pb = make_uint4(pack2(TT{}, pw[0], pw[1]), pack2(TT{}, pw[2], pw[3]),
+                                pack2(TT{}, pw[4], pw[5]), pack2(TT{}, pw[6], pw[7]));
     if (vtail && tok + kKeys > last) {  // zero V of positions past `last` in this group
       const int keep = min(max(last + 1 - tok - kb * VS, 0), VS);
       uint32_t m4[4];
