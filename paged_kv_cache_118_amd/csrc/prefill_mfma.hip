@@ -11,12 +11,13 @@
 // of gitcode.csdn.net "vLLM 推理引擎：PagedAttention 与 KVCache 管理", section 3.
 //
 // Unlike decode, each K/V element now meets many queries, so the work is a
-// real dense contraction.  A wavefront owns 16 query rows of one q head; a
-// workgroup holds four consecutive 16-row tiles of the same head and stages
-// each key group's K/V once in LDS for all four; all workgroups reading one
-// kv head's K/V run on one XCD at about the same time, so the cache lines of
-// a key group come from HBM about once and are served to the others from L2
-// (plain, temporal loads).  With lane = 16*kb + n and v_mfma_f32_16x16x32:
+// real dense contraction.  A wavefront owns 16 or 32 query rows of one q
+// head; a workgroup holds 2 or 4 consecutive row tiles of the same head and
+// stages each key group's K/V once in LDS for all of them; all workgroups
+// reading one kv head's K/V run on one XCD at about the same time, so the
+// cache lines of a key group come from HBM about once and are served to the
+// others from L2 (plain, temporal loads).  16-row tiles, with lane =
+// 16*kb + n and v_mfma_f32_16x16x32 (32-row tiles: see compute32):
 //   S^T = K Q^T  : A = 16 keys x 32 dims (16-byte K pieces), B = Q^T (query
 //                  row n), two 16-key tiles per 32-key group whose rows are
 //                  ordered so that lane (n, kb) gets query n's scores of keys
@@ -26,6 +27,7 @@
 // The mask compares each key's position with the lane's query position, so
 // only the groups that reach past the tile's first row pay for it.
 #include <math.h>
+#include <stdlib.h>
 
 #include "pa_internal.h"
 
@@ -33,9 +35,6 @@ namespace pa {
 
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kRows = 16;  // query rows per wavefront
 constexpr int kKeys = 32;  // keys per step
 
 __device__ __forceinline__ uint4 ld16(const char* p) {
@@ -48,6 +47,18 @@ __device__ __forceinline__ float4_t mfma(F16, const uint4& a, const uint4& b, fl
 }
 __device__ __forceinline__ float4_t mfma(BF16, const uint4& a, const uint4& b, float4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf168_t, a),
+                                                 __builtin_bit_cast(bf168_t, b), c, 0, 0, 0);
+}
+// v_mfma_f32_32x32x16: lane l holds A[row l % 32][k 8 (l / 32) .. +7],
+// B[k 8 (l / 32) .. +7][column l % 32], and C register r is
+// C[8 (r / 4) + 4 (l / 32) + r % 4][l % 32].
+typedef float float16_t __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ float16_t mfma32(F16, const uint4& a, const uint4& b, float16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, a),
+                                                __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ float16_t mfma32(BF16, const uint4& a, const uint4& b, float16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf168_t, a),
                                                  __builtin_bit_cast(bf168_t, b), c, 0, 0, 0);
 }
 template <typename TT>
@@ -88,6 +99,10 @@ struct TableWindow {
 // skip the rescale altogether.
 constexpr float kSlack = 8.f;
 
+// Longest query chunk from which the 32-rows-per-wavefront kernel is used.
+constexpr int kPrefill32MinRows = 64;
+
+
 // NBG = physical blocks one 32-key group spans: 4 (block size 8), 2 (16),
 // 1 (a multiple of 32).
 //
@@ -101,8 +116,13 @@ constexpr float kSlack = 8.f;
 //   K in LDS: 32 rows [key][D], pitch D*2 + 16 bytes (the 16 keys one
 //             operand read touches fall in distinct banks);
 //   V in LDS: 4 slabs of 8 keys, [slab][D][8], as in the pool.
-template <typename TT, int D, int NBG>
-__global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
+// WR = query rows per wavefront: 16 (16x16x32 MFMAs) or 32 (32x32x16 MFMAs,
+// each K/V operand read from LDS then serves twice as many rows); WV =
+// wavefronts per workgroup.
+template <typename TT, int D, int NBG, int WR, int WV>
+__global__ __launch_bounds__(64 * WV) void prefill_mfma_kernel(PrefillArgs a) {
+  constexpr int kWaves = WV;
+  constexpr int kThreads = 64 * WV;
   constexpr int VS = 8;       // V slab width (tokens)
   constexpr int EB = 2;
   constexpr int KN = D / 32;  // k-steps of S^T
@@ -120,13 +140,15 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n = lane & 15, kb = lane >> 4;
+  const int n = lane & 15, kb = lane >> 4;  // 16-row lane roles
+  const int c32 = lane & 31, hh = lane >> 5;  // 32-row lane roles
+  const int qrow = WR == 16 ? n : c32;        // the lane's query row in the tile
   const int G = a.num_q_heads / a.num_kv_heads;
   // XCD-aware order: workgroups are dealt to the 8 XCDs round-robin by id, so
   // every workgroup of one (sequence, kv head) unit -- its q heads and query
   // tiles, which read the same K/V -- gets ids of one residue mod 8 (the same
   // XCD and L2) and consecutive in time.
-  const int tpg = (a.max_query_len + kWaves * kRows - 1) / (kWaves * kRows);
+  const int tpg = (a.max_query_len + kWaves * WR - 1) / (kWaves * WR);
   const int sub_n = G * tpg;  // workgroups per unit
   const int id = blockIdx.x;
   const int unit = (id / 8 / sub_n) * 8 + id % 8;
@@ -138,14 +160,14 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
   const int ql = a.query_start[seq + 1] - qs;
   int L = a.context_lens[seq];
   L = L < 0 ? 0 : (L > a.len_cap ? a.len_cap : L);
-  const int rwg = (sub % tpg) * kWaves * kRows;  // the workgroup's first row
+  const int rwg = (sub % tpg) * kWaves * WR;  // the workgroup's first row
   if (ql <= 0 || ql > L || rwg >= ql) return;   // (ql > L is a caller error: rows left alone)
-  const int last_wg = L - ql + min(ql, rwg + kWaves * kRows) - 1;  // last position any row needs
-  const int r0 = rwg + wv * kRows;                 // this wavefront's first row
-  const int nrows = max(0, min(ql - r0, kRows));   // 0: the wavefront only helps to load
+  const int last_wg = L - ql + min(ql, rwg + kWaves * WR) - 1;  // last position any row needs
+  const int r0 = rwg + wv * WR;                    // this wavefront's first row
+  const int nrows = max(0, min(ql - r0, WR));      // 0: the wavefront only helps to load
   const int pos0 = L - ql + r0;                    // position of the tile's first row
   const int last = pos0 + max(nrows, 1) - 1;       // position of its last valid row
-  const int mypos = pos0 + (n < nrows ? n : max(nrows, 1) - 1);  // this lane's query position
+  const int mypos = pos0 + (qrow < nrows ? qrow : max(nrows, 1) - 1);  // the lane's query position
   const int64_t g = h / G;
   const int64_t hkv = a.num_kv_heads;
   // block size: a compile-time constant for groups spanning 2 or 4 blocks
@@ -160,20 +182,28 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
   const char* qbase = reinterpret_cast<const char*>(a.q);
   const int32_t* trow = a.block_tables + (int64_t)seq * a.max_blocks_per_seq;
 
-  // Q^T operand: query row n of the tile, dims 32 s + 8 kb .. +7 (zero for
-  // rows past the chunk).
-  uint4 qr[KN];
+  // Q^T operand: query row qrow of the tile, the lane's k-slices -- dims
+  // 32 s + 8 kb .. +7 (16 rows) or 16 s + 8 hh .. +7 (32 rows) -- zero for
+  // rows past the chunk.
+  constexpr int QN = WR == 16 ? D / 32 : D / 16;
+  uint4 qr[QN];
   {
-    const int64_t row = (int64_t)qs + (n < nrows ? r0 + n : 0);
-    const char* qp = qbase + ((row * a.num_q_heads + h) * D + kb * 8) * EB;
+    const int64_t row = (int64_t)qs + (qrow < nrows ? r0 + qrow : 0);
+    const char* qp = qbase + ((row * a.num_q_heads + h) * D + (WR == 16 ? kb : hh) * 8) * EB;
 #pragma unroll
-    for (int s = 0; s < KN; ++s) qr[s] = n < nrows ? ld16(qp + 64 * s) : make_uint4(0, 0, 0, 0);
+    for (int s = 0; s < QN; ++s)
+      qr[s] = qrow < nrows ? ld16(qp + (WR == 16 ? 64 : 32) * s) : make_uint4(0, 0, 0, 0);
   }
 
   float m_run = -INFINITY, l_lane = 0.f;
-  float4_t acc[MT];
+  float4_t acc[MT];        // 16 rows: O^T tile mt (dims 16 mt ..)
+  float16_t acc32[D / 32];  // 32 rows: O^T tile mt (dims 32 mt ..)
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc32[mt][r] = 0.f;
 
   TableWindow tw;
   const int ngroups = last_wg / kKeys + 1;
@@ -312,6 +342,83 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
     }
   };
 
+  // 32 rows per wavefront.  Row rho of the S^T A operand is key
+  // 16 (rho / 16) + 8 ((rho / 4) % 2) + 4 ((rho / 8) % 2) + rho % 4, so C
+  // register r of lane (c32, hh) holds query c32's score of key
+  // 8 hh + r + 8 [r >= 8]: registers 0-7 are the P^T slice of keys 0-15,
+  // 8-15 that of keys 16-31, with no lane exchange.
+  auto compute32 = [&](int grp, const char* buf) {
+    const int tok = grp * kKeys;
+    const int krow = 16 * (c32 >> 4) + 8 * ((c32 >> 2) & 1) + 4 * ((c32 >> 3) & 1) + (c32 & 3);
+    float16_t st;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) st[r] = 0.f;
+    const char* kr = buf + krow * KP + hh * 16;
+#pragma unroll
+    for (int s2 = 0; s2 < D / 16; ++s2)
+      st = mfma32(TT{}, *reinterpret_cast<const uint4*>(kr + 32 * s2), qr[s2], st);
+    float sc[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sc[r] = st[r] * a.scale_log2e;
+    if (tok + kKeys - 1 > pos0) {  // the group reaches past the tile's first row
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (tok + 8 * hh + r + (r >= 8 ? 8 : 0) > mypos) sc[r] = -INFINITY;
+    }
+    float mx = sc[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + kSlack) != 0) {
+      const float m_new = mx > m_run + kSlack ? mx : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_lane *= alpha;
+#pragma unroll
+      for (int mt = 0; mt < D / 32; ++mt) acc32[mt] *= alpha;
+      m_run = m_new;
+    }
+    float pw[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      pw[r] = __builtin_amdgcn_exp2f(sc[r] - m_run);
+      l_lane += pw[r];
+    }
+    uint4 pb[2];
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+      pb[kh] = make_uint4(pack2(TT{}, pw[8 * kh], pw[8 * kh + 1]),
+                          pack2(TT{}, pw[8 * kh + 2], pw[8 * kh + 3]),
+                          pack2(TT{}, pw[8 * kh + 4], pw[8 * kh + 5]),
+                          pack2(TT{}, pw[8 * kh + 6], pw[8 * kh + 7]));
+    // V^T operand of key half kh: slab 2 kh + hh, row d = 32 mt + c32
+    const bool vmask = vtail && tok + kKeys > last;
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      const char* vr = buf + KBUF + (2 * kh + hh) * VSP + c32 * 16;
+      if (vmask) {  // zero V of positions past `last` in this group
+        const int keep = min(max(last + 1 - tok - VS * (2 * kh + hh), 0), VS);
+        uint32_t m4[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          m4[i] = ((2 * i < keep) ? 0xffffu : 0u) | ((2 * i + 1 < keep) ? 0xffff0000u : 0u);
+#pragma unroll
+        for (int mt = 0; mt < D / 32; ++mt) {
+          uint4 v = *reinterpret_cast<const uint4*>(vr + mt * 32 * 16);
+          v.x &= m4[0];
+          v.y &= m4[1];
+          v.z &= m4[2];
+          v.w &= m4[3];
+          acc32[mt] = mfma32(TT{}, v, pb[kh], acc32[mt]);
+        }
+      } else {
+#pragma unroll
+        for (int mt = 0; mt < D / 32; ++mt)
+          acc32[mt] = mfma32(TT{}, *reinterpret_cast<const uint4*>(vr + mt * 32 * 16), pb[kh],
+                             acc32[mt]);
+      }
+    }
+  };
+
   load(0);
   for (int grp = 0; grp < ngroups; ++grp) {
     char* buf = lds + (grp & 1) * BUF;
@@ -320,31 +427,68 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
     __syncthreads();
     // wavefronts without rows, or whose rows all end before this group,
     // only help with the loads
-    if (nrows > 0 && grp * kKeys <= last) compute(grp, buf);
+    if (nrows > 0 && grp * kKeys <= last) {
+      if constexpr (WR == 16) compute(grp, buf); else compute32(grp, buf);
+    }
   }
 
-  float l_tot = l_lane + __shfl_xor(l_lane, 16);
-  l_tot += __shfl_xor(l_tot, 32);
-  if (n < nrows) {
-    const float inv = 1.f / l_tot;
-    uint16_t* out = reinterpret_cast<uint16_t*>(a.out) +
-                    (((int64_t)qs + r0 + n) * a.num_q_heads + h) * D + 4 * kb;
+  if constexpr (WR == 16) {
+    float l_tot = l_lane + __shfl_xor(l_lane, 16);
+    l_tot += __shfl_xor(l_tot, 32);
+    if (n < nrows) {
+      const float inv = 1.f / l_tot;
+      uint16_t* out = reinterpret_cast<uint16_t*>(a.out) +
+                      (((int64_t)qs + r0 + n) * a.num_q_heads + h) * D + 4 * kb;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) out[mt * 16 + e] = to_bits(TT{}, acc[mt][e] * inv);
+        for (int e = 0; e < 4; ++e) out[mt * 16 + e] = to_bits(TT{}, acc[mt][e] * inv);
+    }
+  } else {
+    const float l_tot = l_lane + __shfl_xor(l_lane, 32);
+    if (c32 < nrows) {
+      const float inv = 1.f / l_tot;
+      uint16_t* out = reinterpret_cast<uint16_t*>(a.out) +
+                      (((int64_t)qs + r0 + c32) * a.num_q_heads + h) * D + 4 * hh;
+      // register r holds dim 32 mt + 8 (r / 4) + 4 hh + r % 4
+#pragma unroll
+      for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint2 w;
+          w.x = pack2(TT{}, acc32[mt][4 * q] * inv, acc32[mt][4 * q + 1] * inv);
+          w.y = pack2(TT{}, acc32[mt][4 * q + 2] * inv, acc32[mt][4 * q + 3] * inv);
+          *reinterpret_cast<uint2*>(out + 32 * mt + 8 * q) = w;
+        }
+    }
   }
 }
 
-template <typename TT, int D, int NBG>
-hipError_t launch_g(const PrefillArgs& a, hipStream_t s) {
-  const int64_t tpg = (a.max_query_len + kWaves * kRows - 1) / (kWaves * kRows);
+template <typename TT, int D, int NBG, int WR, int WV>
+hipError_t launch_w(const PrefillArgs& a, hipStream_t s) {
+  const int64_t tpg = (a.max_query_len + WV * WR - 1) / (WV * WR);
   const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads;
   const int64_t wgs = (units + 7) / 8 * 8 * (a.num_q_heads / a.num_kv_heads) * tpg;
   if (wgs > 0x7fffffff) return hipErrorInvalidValue;
   dim3 grid((unsigned)wgs);
-  hipLaunchKernelGGL((prefill_mfma_kernel<TT, D, NBG>), grid, dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((prefill_mfma_kernel<TT, D, NBG, WR, WV>), grid, dim3(64 * WV), 0, s, a);
   return hipGetLastError();
+}
+
+// Shape of the workgroup: 32 rows per wavefront and two wavefronts once
+// chunks reach kPrefill32MinRows rows, else 16 rows and four wavefronts.
+// Measured on ragged chunks (prompt tails of 1-512 rows after reused
+// prefixes) two 32-row wavefronts beat four, which leave more of a short
+// chunk's workgroup idle; on uniform 256-row chunks four were 9% faster.
+// Tuning overrides: PA_PREFILL_ROWS (16, 32), PA_PREFILL_WAVES (2, 4).
+template <typename TT, int D, int NBG>
+hipError_t launch_g(const PrefillArgs& a, hipStream_t s) {
+  int wr = a.max_query_len >= kPrefill32MinRows ? 32 : 16, wv = wr == 32 ? 2 : 4;
+  if (const char* e = std::getenv("PA_PREFILL_ROWS")) wr = atoi(e) == 32 ? 32 : atoi(e) == 16 ? 16 : wr;
+  if (const char* e = std::getenv("PA_PREFILL_WAVES")) wv = atoi(e) == 2 ? 2 : 4;
+  if (wr == 32)
+    return wv == 2 ? launch_w<TT, D, NBG, 32, 2>(a, s) : launch_w<TT, D, NBG, 32, 4>(a, s);
+  return wv == 2 ? launch_w<TT, D, NBG, 16, 2>(a, s) : launch_w<TT, D, NBG, 16, 4>(a, s);
 }
 
 template <typename TT, int D>

@@ -106,3 +106,20 @@ def test_prefill_rejects_unsupported():
     with pytest.raises(pa.PAError) as e:
         run_prefill(case, q, qs)
     assert e.value.status == -2
+
+
+@pytest.mark.parametrize("rows,waves", [(16, 2), (16, 4), (32, 2), (32, 4)])
+def test_prefill_every_workgroup_shape(rows, waves, monkeypatch):
+    """Each workgroup shape the library can launch (rows per wavefront x
+    wavefronts, forced through the tuning overrides) on ragged chunks, MHA and
+    grouped heads, against the oracle."""
+    monkeypatch.setenv("PA_PREFILL_ROWS", str(rows))
+    monkeypatch.setenv("PA_PREFILL_WAVES", str(waves))
+    for name in ("mha_f16_bs16", "gqa_bf16_g8_bs32"):
+        spec = SPECS[name]
+        log(f"[prefill shape] {rows}x{waves} {name}")
+        case, q, qs = make_prefill_case(spec, [c for c, _ in CASES], [q for _, q in CASES],
+                                        seed=rows + waves)
+        err = max_err(run_prefill(case, q, qs), oracle_prefill(case, q, qs))
+        log(f"  max abs err {err:.3e}")
+        assert err <= TOL[spec.dtype]
