@@ -14,9 +14,9 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// One workgroup = TT consecutive tokens of one kv head, 8*TT threads (TT = 32
-// for large writes, 8 for decode-sized ones so more CUs share the stores).
-// The K and V rows of the TT tokens are first staged in LDS by 16-byte loads
+// Large writes (prompt chunks): one workgroup = TT = 32 consecutive tokens of
+// one kv head, 8*TT threads.  The K and V rows of the TT tokens are first
+// staged in LDS by 16-byte loads
 // running along each row (so a wavefront reads whole cache lines), then:
 //  K: the pool stores 16-byte pieces [D/X][BS][X]; piece c of a token row is
 //     one 16-byte store, threads taking tokens fastest, so consecutive slots
@@ -126,6 +126,60 @@ __global__ __launch_bounds__(8 * TT) void reshape_and_cache_kernel(
   for (int d = dgrp; d < D; d += NT / TT) vdst[(int64_t)d * vs] = src[d];
 }
 
+// Decode-sized writes (a token or a few per sequence, scattered slots, no
+// slab ever filled whole): 8 tokens of one kv head per workgroup, K pieces
+// straight from the token rows to the pool (tokens fastest), V through LDS so
+// that lanes with consecutive slots write consecutive slab elements; one
+// barrier instead of the staged kernel's three.
+template <int ES>
+__global__ __launch_bounds__(64) void reshape_and_cache_small_kernel(
+    const char* __restrict__ k, const char* __restrict__ v, char* __restrict__ k_cache,
+    char* __restrict__ v_cache, const int64_t* __restrict__ slots, int32_t num_tokens,
+    int64_t k_stride, int64_t v_stride, int32_t hkv, int32_t D, int32_t bs, int64_t num_blocks) {
+  using E = typename std::conditional<ES == 4, uint32_t, uint16_t>::type;
+  constexpr int TT = 8, NT = 64;
+  extern __shared__ __align__(16) char smem[];
+  const int row_bytes = D * ES;
+  const int lds_stride = row_bytes + 4;  // pad: consecutive tokens hit different banks
+  const int h = blockIdx.y;
+  const int t0 = blockIdx.x * TT;
+  const int nt = min(TT, num_tokens - t0);
+  const int64_t max_slot = num_blocks * (int64_t)bs;
+  const int vs = v_slab(bs);
+  const int chunks = row_bytes / 16;
+  for (int i = threadIdx.x; i < nt * chunks; i += NT) {
+    const int c = i / nt, tt = i - c * nt;
+    const int64_t t = t0 + tt;
+    const int64_t slot = slots[t];
+    const uint4 kv = *reinterpret_cast<const uint4*>(k + (t * k_stride + (int64_t)h * D) * ES +
+                                                      c * 16);
+    const uint4 vv = *reinterpret_cast<const uint4*>(v + (t * v_stride + (int64_t)h * D) * ES +
+                                                      c * 16);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(smem + tt * lds_stride + c * 16);
+    dst[0] = vv.x;
+    dst[1] = vv.y;
+    dst[2] = vv.z;
+    dst[3] = vv.w;
+    if (slot >= 0 && slot < max_slot) {
+      const int64_t blk = slot / bs;
+      const int off = (int)(slot - blk * bs);
+      *reinterpret_cast<uint4*>(k_cache + (((blk * hkv + h) * chunks + c) * bs + off) * 16) = kv;
+    }
+  }
+  __syncthreads();
+  const int tt = threadIdx.x % TT;
+  const int dgrp = threadIdx.x / TT;
+  if (tt >= nt) return;
+  const int64_t slot = slots[t0 + tt];
+  if (slot < 0 || slot >= max_slot) return;
+  const int64_t blk = slot / bs;
+  const int off = (int)(slot - blk * bs);
+  E* vdst = reinterpret_cast<E*>(v_cache) + ((blk * hkv + h) * (bs / vs) + off / vs) * (int64_t)D * vs +
+            off % vs;
+  const E* src = reinterpret_cast<const E*>(smem + tt * lds_stride);
+  for (int d = dgrp; d < D; d += NT / TT) vdst[(int64_t)d * vs] = src[d];
+}
+
 // Whole-block copies: block b of either pool is one contiguous run of
 // block_bytes bytes (all heads, all slots), so each pair is two memcpys.
 __global__ __launch_bounds__(kThreads) void copy_blocks_kernel(char* __restrict__ k_cache,
@@ -198,12 +252,23 @@ hipError_t launch_reshape_and_cache(const void* k, const void* v, void* k_cache,
                                     int32_t block_size, int64_t num_blocks, int elem_bytes,
                                     hipStream_t s) {
   if (num_tokens == 0) return hipSuccess;
-  if (num_tokens >= 1024)
+  if (num_tokens >= 1024) {
     launch_rc<32>(k, v, k_cache, v_cache, slots, num_tokens, k_stride, v_stride, num_kv_heads,
                   head_dim, block_size, num_blocks, elem_bytes, s);
-  else
-    launch_rc<8>(k, v, k_cache, v_cache, slots, num_tokens, k_stride, v_stride, num_kv_heads,
-                 head_dim, block_size, num_blocks, elem_bytes, s);
+  } else {
+    dim3 grid((num_tokens + 7) / 8, num_kv_heads);
+    const size_t lds = (size_t)8 * (head_dim * elem_bytes + 4);
+    if (elem_bytes == 4)
+      hipLaunchKernelGGL(reshape_and_cache_small_kernel<4>, grid, dim3(64), lds, s,
+                         (const char*)k, (const char*)v, (char*)k_cache, (char*)v_cache, slots,
+                         num_tokens, k_stride, v_stride, num_kv_heads, head_dim, block_size,
+                         num_blocks);
+    else
+      hipLaunchKernelGGL(reshape_and_cache_small_kernel<2>, grid, dim3(64), lds, s,
+                         (const char*)k, (const char*)v, (char*)k_cache, (char*)v_cache, slots,
+                         num_tokens, k_stride, v_stride, num_kv_heads, head_dim, block_size,
+                         num_blocks);
+  }
   return hipGetLastError();
 }
 
