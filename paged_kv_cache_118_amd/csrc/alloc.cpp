@@ -187,16 +187,22 @@ uint64_t splitmix64(uint64_t& s) {
 
 Digest block_digest(const Digest* parent, uint64_t salt, const int32_t* tokens, int64_t n) {
   pa::Sha256 h;
-  static const Digest zero{};
-  h.update((parent ? *parent : zero).data(), 32);
-  uint8_t b[8];
-  for (int i = 0; i < 8; ++i) b[i] = (uint8_t)(salt >> (8 * i));
-  h.update(b, 8);
+  // the message: parent | salt (little-endian) | tokens (little-endian),
+  // serialised a chunk at a time
+  uint8_t b[1024];
+  if (parent) std::memcpy(b, parent->data(), 32); else std::memset(b, 0, 32);
+  for (int i = 0; i < 8; ++i) b[32 + i] = (uint8_t)(salt >> (8 * i));
+  size_t len = 40;
   for (int64_t t = 0; t < n; ++t) {
     const uint32_t v = (uint32_t)tokens[t];
-    for (int i = 0; i < 4; ++i) b[i] = (uint8_t)(v >> (8 * i));
-    h.update(b, 4);
+    for (int i = 0; i < 4; ++i) b[len + i] = (uint8_t)(v >> (8 * i));
+    len += 4;
+    if (len == sizeof b) {
+      h.update(b, len);
+      len = 0;
+    }
   }
+  h.update(b, len);
   return h.finish();
 }
 

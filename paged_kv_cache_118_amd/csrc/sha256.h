@@ -10,7 +10,13 @@
 #include <array>
 #include <cstddef>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
+
+#if defined(__x86_64__)
+#include <cpuid.h>
+#include <immintrin.h>
+#endif
 
 namespace pa {
 
@@ -53,6 +59,58 @@ struct Sha256Consts {
   }
 };
 
+#if defined(__x86_64__)
+// One compression with the x86 SHA extensions (SHA256RNDS2 performs two rounds
+// on the state split as ABEF / CDGH; SHA256MSG1 / MSG2 compute the sigma0 /
+// sigma1 parts of the message schedule).  Same result as the portable
+// compression below.
+__attribute__((target("sha,sse4.1,ssse3"))) inline void compress_shani(uint32_t h[8],
+                                                                     const uint8_t* blk) {
+  const uint32_t* K = Sha256Consts::get().k;
+  const __m128i bswap = _mm_set_epi64x(0x0c0d0e0f08090a0bULL, 0x0405060700010203ULL);
+  __m128i tmp = _mm_shuffle_epi32(_mm_loadu_si128(reinterpret_cast<const __m128i*>(h)), 0xB1);
+  __m128i s1 = _mm_shuffle_epi32(_mm_loadu_si128(reinterpret_cast<const __m128i*>(h + 4)), 0x1B);
+  __m128i s0 = _mm_alignr_epi8(tmp, s1, 8);  // A B E F
+  s1 = _mm_blend_epi16(s1, tmp, 0xF0);       // C D G H
+  const __m128i abef = s0, cdgh = s1;
+  __m128i w[16];  // w[g] = message words 4g .. 4g+3
+  for (int g = 0; g < 4; ++g)
+    w[g] = _mm_shuffle_epi8(_mm_loadu_si128(reinterpret_cast<const __m128i*>(blk + 16 * g)), bswap);
+  for (int g = 4; g < 16; ++g)
+    w[g] = _mm_sha256msg2_epu32(
+        _mm_add_epi32(_mm_sha256msg1_epu32(w[g - 4], w[g - 3]), _mm_alignr_epi8(w[g - 1], w[g - 2], 4)),
+        w[g - 1]);
+  for (int g = 0; g < 16; ++g) {
+    __m128i m = _mm_add_epi32(w[g], _mm_loadu_si128(reinterpret_cast<const __m128i*>(K + 4 * g)));
+    s1 = _mm_sha256rnds2_epu32(s1, s0, m);
+    m = _mm_shuffle_epi32(m, 0x0E);
+    s0 = _mm_sha256rnds2_epu32(s0, s1, m);
+  }
+  s0 = _mm_add_epi32(s0, abef);
+  s1 = _mm_add_epi32(s1, cdgh);
+  tmp = _mm_shuffle_epi32(s0, 0x1B);                  // F E B A
+  s1 = _mm_shuffle_epi32(s1, 0xB1);                   // D C H G
+  s0 = _mm_blend_epi16(tmp, s1, 0xF0);                // D C B A
+  s1 = _mm_alignr_epi8(s1, tmp, 8);                   // H G F E
+  _mm_storeu_si128(reinterpret_cast<__m128i*>(h), s0);
+  _mm_storeu_si128(reinterpret_cast<__m128i*>(h + 4), s1);
+}
+
+// The extensions are used when the CPU has them, unless PA_NO_SHA_EXT is set
+// (which keeps the portable compression in use, e.g. to test it).
+inline bool cpu_has_sha() {
+  static const bool ok = [] {
+    const char* off = std::getenv("PA_NO_SHA_EXT");
+    if (off && off[0] && off[0] != '0') return false;
+    unsigned a, b, c, d;
+    if (!__get_cpuid(1, &a, &b, &c, &d) || !(c & bit_SSE4_1) || !(c & bit_SSSE3)) return false;
+    if (!__get_cpuid_count(7, 0, &a, &b, &c, &d)) return false;
+    return (b & (1u << 29)) != 0;  // CPUID.(EAX=7,ECX=0):EBX.SHA
+  }();
+  return ok;
+}
+#endif
+
 class Sha256 {
  public:
   Sha256() : n_(0), total_(0) {
@@ -77,12 +135,15 @@ class Sha256 {
 
   std::array<uint8_t, 32> finish() {
     const uint64_t bits = total_ * 8;
-    const uint8_t one = 0x80, zero = 0;
-    update(&one, 1);
-    while (n_ != 56) update(&zero, 1);
-    uint8_t len_be[8];
-    for (int i = 0; i < 8; ++i) len_be[i] = (uint8_t)(bits >> (56 - 8 * i));
-    update(len_be, 8);
+    buf_[n_++] = 0x80;  // padding: 1 bit, zeros, the bit length (FIPS 180-4 5.1.1)
+    if (n_ > 56) {
+      std::memset(buf_ + n_, 0, 64 - n_);
+      compress(buf_);
+      n_ = 0;
+    }
+    std::memset(buf_ + n_, 0, 56 - n_);
+    for (int i = 0; i < 8; ++i) buf_[56 + i] = (uint8_t)(bits >> (56 - 8 * i));
+    compress(buf_);
     std::array<uint8_t, 32> out;
     for (int i = 0; i < 8; ++i)
       for (int j = 0; j < 4; ++j) out[4 * i + j] = (uint8_t)(h_[i] >> (24 - 8 * j));
@@ -93,6 +154,12 @@ class Sha256 {
   static uint32_t rotr(uint32_t x, int r) { return (x >> r) | (x << (32 - r)); }
 
   void compress(const uint8_t* blk) {
+#if defined(__x86_64__)
+    if (cpu_has_sha()) {
+      compress_shani(h_, blk);
+      return;
+    }
+#endif
     const uint32_t* K = Sha256Consts::get().k;
     uint32_t w[64];
     for (int t = 0; t < 16; ++t)

@@ -80,6 +80,27 @@ def test_block_hash_is_sha256_of_the_stated_bytes():
         assert pa.prefix_block_hash(parent, salt, toks) == hashlib.sha256(msg).digest(), n
 
 
+def test_block_hash_portable_compression():
+    """The same check with the CPU's SHA instructions switched off, so the
+    portable compression is the one under test (in a child process: the
+    choice is made once per process)."""
+    import os
+    import subprocess
+    import sys
+    code = ("import hashlib, numpy as np, paged_kv_cache_118_amd as pa\n"
+            "rng = np.random.default_rng(1)\n"
+            "for n in list(range(0, 40)) + [64, 100, 300]:\n"
+            "    t = rng.integers(-2**31, 2**31, size=n, dtype=np.int64).astype(np.int32)\n"
+            "    p = rng.integers(0, 256, size=32).astype(np.uint8).tobytes()\n"
+            "    m = p + (12345).to_bytes(8, 'little') + t.astype('<i4').tobytes()\n"
+            "    assert pa.prefix_block_hash(p, 12345, t) == hashlib.sha256(m).digest(), n\n"
+            "print('ok')\n")
+    env = dict(os.environ, PA_NO_SHA_EXT="1")
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
+                       cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    assert r.returncode == 0 and r.stdout.strip() == "ok", r.stderr[-2000:]
+
+
 def test_every_pin_holds():
     assert P.failures(cpp_factory) == []
 
