@@ -100,12 +100,14 @@ const char* pa_strerror(pa_status s);
  *                    tokens, whatever the lengths; an
  *                    item shared by several wavefronts yields one fp32
  *                    (max, sum, unnormalised output) partial per wavefront;
- *               >0 = the same balanced shares, and each sequence's
- *                    context is cut into partitions of this many tokens (a
- *                    multiple of 256) from its start: an item longer than
- *                    one partition yields one partial per partition, or per
- *                    (partition, wavefront) piece where a partition
- *                    straddles two shares;
+ *               >0 = split-context partitions: each sequence's context is
+ *                    cut into partitions of this many tokens (a multiple of
+ *                    256) from its start, and the wavefronts take balanced
+ *                    shares of whole partitions (no partition is divided
+ *                    between two); a wavefront folds the consecutive
+ *                    partitions it holds of an item into one fp32 partial,
+ *                    so an item spread over several wavefronts yields one
+ *                    partial per wavefront, as above;
  *               -1 = one wavefront per (sequence, head) item, nothing split.
  *               The partials of an item are reduced by a second kernel
  *               (rescaled to their common maximum: one denominator, as in the
@@ -133,8 +135,8 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
                                  int32_t partition_size, pa_dtype dtype);
 
 /* The split pa_decode uses for these arguments: -1 = one wavefront per
- * item, 0 = token-balanced, > 0 = token-balanced with partials cut at
- * partitions of that many tokens. */
+ * item, 0 = token-balanced, > 0 = balanced shares of whole partitions of that
+ * many tokens. */
 int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t block_size, int32_t max_context_len,
                                  int32_t partition_size, pa_dtype dtype);

@@ -86,7 +86,7 @@ struct Plan {
   int step;         // tokens per worker step
   int items_per_seq;
   int rows_per_item;
-  int part_steps;   // split 1: steps per partition, 0 = partials per worker segment only
+  int part_steps;   // split 1: steps per partition (shares are whole partitions), 0 = none
   int num_workers;
   size_t ws_bytes;
   size_t pre_off, ppre_off;
@@ -114,9 +114,7 @@ Plan make_plan(int num_seqs, int hq, int hkv, int head_dim, int block_size, int 
   }
   p.part_steps = partition_size > 0 ? std::max(1, partition_size / p.step) : 0;
   p.num_workers = device_cus() * waves_per_cu(p.path == Path::kMfma, dt, head_dim);
-  const int64_t partitions =
-      p.part_steps ? items * ((item_steps + p.part_steps - 1) / p.part_steps) : items;
-  const size_t slots = (size_t)(partitions + p.num_workers);
+  const size_t slots = (size_t)(items + p.num_workers);  // partial of item i by worker w: i + w
   p.pre_off = round_up(slots * part_record(p.rows_per_item, head_dim) * 4, 256);
   p.ppre_off = p.pre_off + round_up(((size_t)num_seqs + 1) * 4, 256);
   p.ws_bytes = p.ppre_off + round_up(((size_t)num_seqs + 1) * 4, 256);
@@ -267,7 +265,7 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
     case Path::kGeneric: e = launch_decode_generic(a, dtype, s); break;
   }
   if (e != hipSuccess) return PA_EHIP;
-  if (p.split) e = launch_decode_merge(a, dtype, p.items_per_seq, p.step, s);
+  if (p.split) e = launch_decode_merge(a, dtype, p.items_per_seq, s);
   return hip_status(e);
 }
 

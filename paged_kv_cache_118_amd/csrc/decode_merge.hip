@@ -1,15 +1,15 @@
 // Merge of the partials of items that the decode kernels split (decode_split.h).
 //
-// Each (partition, worker) piece of a split item left fp32 (m, l, o) per q row
+// Each worker's piece of a split item left fp32 (m, l, o) per q row
 // of the item: its running max (base-2 domain), the sum of exp2(s - m) and the
 // unnormalised output.  Because every block shares one softmax denominator
 // (wq-win.github.io "079 | vLLM 与 PagedAttention", section 二, the Z / o
 // equations), the exact row is recovered by rescaling to the global max M:
 //   out = sum_i 2^(m_i - M) o_i  /  sum_i 2^(m_i - M) l_i.
 // The pieces an item has follow from the split arithmetic alone (the step
-// prefixes the decode kernel exported, the worker count, the partition size),
-// so nothing but the partials themselves has to be communicated.  This kernel
-// also writes the zero rows of empty sequences.
+// and partition prefixes the decode kernel exported, the worker count, the
+// partition size), so nothing but the partials themselves has to be
+// communicated.  This kernel also writes the zero rows of empty sequences.
 #include <math.h>
 
 #include "decode_split.h"
@@ -67,13 +67,9 @@ __device__ __forceinline__ float merge_output(const DecodeArgs& a, SlotOf slot_o
 }
 
 // One workgroup per item (b, h), one thread per output (q row r, dim d).
-// LDS: st[0..nw] = first stream step of each of the item's workers (clipped to
-// the item), then the item's slot list.
 template <typename TT>
 __global__ __launch_bounds__(1024) void decode_merge_kernel(DecodeArgs a, int H, int R) {
-  extern __shared__ int smem[];
-  __shared__ int s_count;
-  const int D = a.head_dim, B = a.num_seqs, C = a.part_steps;
+  const int D = a.head_dim, B = a.num_seqs;
   const int item = blockIdx.x;
   const int b = item / H, h = item - b * H;
   const int* pre = a.ws_pre;
@@ -84,78 +80,39 @@ __global__ __launch_bounds__(1024) void decode_merge_kernel(DecodeArgs a, int H,
     for (int t = threadIdx.x; t < total; t += blockDim.x) store_out<TT>(a.out, orow0 + t, 0.f);
     return;
   }
-  const Split sp = make_split(a.num_workers, pre[B]);
+  const Split sp = make_split(a.num_workers, pre[B], a.part_steps, H, B, pre, a.ws_ppre);
   const int64_t S = pre[b] + (int64_t)h * n, E = S + n;
   const int F = sp.worker_of(S), Lw = sp.worker_of(E - 1);
-  const int np = C > 0 ? (n + C - 1) / C : 1;
-  if (F == Lw && np == 1) return;  // one piece: the decode kernel wrote the row
-  if (C == 0) {  // one piece per worker: slots item + F .. item + Lw
-    const int base = item + F;
-    for (int t = threadIdx.x; t < total; t += blockDim.x) {
-      const int r = t / D, d = t - r * D;
-      store_out<TT>(a.out, orow0 + t,
-                    merge_output(a, [base](int k) { return base + k; }, Lw - F + 1, R, r, d));
-    }
-    return;
-  }
-  const int pg0 = a.ws_ppre[b] + h * np;
-  const int nw = Lw - F + 1;
-  int* st = smem;
-  int* slots = smem + nw + 1;
-  for (int i = threadIdx.x; i <= nw; i += blockDim.x)
-    st[i] = (int)(i == 0 ? S : (i == nw ? E : sp.start(F + i)));
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    // Walk the pieces in stream order: piece (p, i) ends at the earlier of
-    // partition p's end and worker F+i's end; slot pg0 + p + F + i.
-    int p = 0, i = 0, k = 0;
-    for (;;) {
-      slots[k++] = pg0 + p + F + i;
-      const int64_t pend = C > 0 ? (S + (int64_t)(p + 1) * C < E ? S + (int64_t)(p + 1) * C : E)
-                                 : E;
-      const int64_t wend = st[i + 1];
-      if (pend >= E && wend >= E) break;
-      if (pend <= wend) ++p;
-      if (wend <= pend) ++i;
-    }
-    s_count = k;
-  }
-  __syncthreads();
-  const int K = s_count;
+  if (F == Lw) return;  // one piece: the decode kernel wrote the row
+  // one piece per worker F .. Lw, in slots item + F .. item + Lw
+  const int base = item + F;
   for (int t = threadIdx.x; t < total; t += blockDim.x) {
     const int r = t / D, d = t - r * D;
     store_out<TT>(a.out, orow0 + t,
-                  merge_output(a, [slots](int k) { return slots[k]; }, K, R, r, d));
+                  merge_output(a, [base](int k) { return base + k; }, Lw - F + 1, R, r, d));
   }
 }
 
 }  // namespace
 
-hipError_t launch_decode_merge(const DecodeArgs& a, pa_dtype dt, int items_per_seq, int step,
+hipError_t launch_decode_merge(const DecodeArgs& a, pa_dtype dt, int items_per_seq,
                                hipStream_t s) {
   if (a.num_seqs == 0 || !a.split) return hipSuccess;
   const int R = a.num_q_heads / items_per_seq;
   const int outputs = R * a.head_dim;
   const int threads = outputs >= 1024 ? 1024 : (outputs + 63) / 64 * 64;
-  // workers of one item: at most item_steps / kMinChunk + 2; pieces: that
-  // plus the item's partitions
-  const int item_steps = (a.len_cap + step - 1) / step;
-  int nw_max = item_steps / kMinChunk + 2;
-  if (nw_max > a.num_workers + 1) nw_max = a.num_workers + 1;
-  const int np_max = a.part_steps > 0 ? (item_steps + a.part_steps - 1) / a.part_steps : 1;
-  const size_t lds = sizeof(int) * (size_t)(2 * nw_max + np_max + 2);
   dim3 grid(a.num_seqs * items_per_seq);
   switch (dt) {
     case PA_F32:
-      hipLaunchKernelGGL(decode_merge_kernel<F32>, grid, dim3(threads), lds, s, a, items_per_seq,
+      hipLaunchKernelGGL(decode_merge_kernel<F32>, grid, dim3(threads), 0, s, a, items_per_seq,
                          R);
       break;
     case PA_F16:
-      hipLaunchKernelGGL(decode_merge_kernel<F16>, grid, dim3(threads), lds, s, a, items_per_seq,
+      hipLaunchKernelGGL(decode_merge_kernel<F16>, grid, dim3(threads), 0, s, a, items_per_seq,
                          R);
       break;
     case PA_BF16:
-      hipLaunchKernelGGL(decode_merge_kernel<BF16>, grid, dim3(threads), lds, s, a, items_per_seq,
+      hipLaunchKernelGGL(decode_merge_kernel<BF16>, grid, dim3(threads), 0, s, a, items_per_seq,
                          R);
       break;
   }

@@ -124,7 +124,7 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_mfma_kernel(DecodeArgs a
     if (blockIdx.x == 0 && wv == 0) export_prefixes(s_pre, s_ppre, B, C, a.ws_pre, a.ws_ppre);
     const int N = s_pre[B];  // empty sequences get their zero rows from the merge
     if (N == 0) return;
-    sp = make_split(a.num_workers, N);
+    sp = make_split(a.num_workers, N, C, H, B, s_pre, s_ppre);
     if (worker >= sp.W) return;
     x0 = sp.start(worker);
     count = (int)(sp.start(worker + 1) - x0);
@@ -239,7 +239,7 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_mfma_kernel(DecodeArgs a
   // Phase 1 of a group: S^T = K Q^T, online-softmax update, P^T operand.
   auto qk = [&](const Cursor& cu, const uint4 (&kr)[2][KN], const uint4 (&qr)[KN], int j,
                 uint4& pb, int& nvalid) {
-    if (segment_starts(cu, j, C)) {
+    if (segment_starts(cu, j)) {
       m_run = -INFINITY;
       l_lane = 0.f;
 #pragma unroll
@@ -321,7 +321,7 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_mfma_kernel(DecodeArgs a
     }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma(TT{}, vr[mt], pb, acc[mt]);
-    if (segment_ends(cu, j, count - 1, C)) {
+    if (segment_ends(cu, j, count - 1)) {
       float l_tot = l_lane + __shfl_xor(l_lane, 16);
       l_tot += __shfl_xor(l_tot, 32);
       const int64_t orow0 = (int64_t)cu.b * a.num_q_heads + (int64_t)cu.h * G;
@@ -339,7 +339,7 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_mfma_kernel(DecodeArgs a
         // Partial record (pa_internal.h): for each d tile the group's lanes
         // write one contiguous run of 64 G bytes; then the 128-byte m / l
         // line, written whole (lanes kb = 2, 3 write its zero half).
-        const int64_t slot = (int64_t)partition_index(cu, H, C, s_ppre) + worker;
+        const int64_t slot = (int64_t)cu.item(H) + worker;
         float* rec = a.ws_part + slot * part_record(G, D);
         if (n < G) {
           float* o = rec + (kb * G + n) * 4;

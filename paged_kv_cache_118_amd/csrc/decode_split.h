@@ -8,19 +8,24 @@
 // worker streams the same number of K/V bytes whatever the lengths.  A worker
 // prefetches straight across item boundaries.
 //
-// Segments.  A worker's steps of one item form a segment, which is further
-// cut at partition boundaries when a partition size P = C * STEP is given
-// (item steps [p*C, (p+1)*C) form partition p).  A segment that is a whole
-// item is written as the final output row.  Otherwise it becomes an fp32
-// partial (m, l, o) of the item: running max in the base-2 domain, sum of
-// 2^(s - m), unnormalised output; the merge kernel (decode_merge.hip)
-// combines an item's partials.
+// Partitions.  When a partition size P = C * STEP is given, item steps
+// [p*C, (p+1)*C) form partition p of the item, and the shares are made of
+// whole partitions: worker w takes partitions [w*Pn/W, (w+1)*Pn/W) of the Pn
+// partitions laid end to end, so no partition is divided between wavefronts.
+// Shares then differ by at most one partition.
 //
-// Slots.  The partial of segment (partition p, worker w) goes to slot
-// pg + w, with pg the stream-order index of the partition over all items
-// (the item index itself when no partition size is given).  Along the stream
-// every new segment increases pg, w or both, so slots are unique; the merge
-// recomputes from the same arithmetic which (p, w) pairs an item has.
+// Segments.  A worker's steps of one item form a segment.  A segment that is
+// a whole item is written as the final output row.  Otherwise it becomes an
+// fp32 partial (m, l, o) of the item: running max in the base-2 domain, sum
+// of 2^(s - m), unnormalised output; the merge kernel (decode_merge.hip)
+// combines an item's partials.  A worker owning several consecutive
+// partitions of an item folds them into one partial in registers (the online
+// softmax is exact over any number of keys).
+//
+// Slots.  The partial of the segment of item i by worker w goes to slot i + w.
+// Along the stream every new segment increases the item, the worker or both,
+// so slots are unique; the merge recomputes from the same arithmetic which
+// workers an item has.
 #pragma once
 
 #include "pa_internal.h"
@@ -83,21 +88,67 @@ __device__ inline int wave_scan_steps(const int32_t* lens, int B, int H, int cap
 // is amortised.
 constexpr int kMinChunk = 8;
 
+// Largest b in [0, B-1] with a[b] <= v, for non-decreasing a[0..B].
+__device__ __forceinline__ int last_le(const int* a, int B, int64_t v) {
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a[mid] <= v) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
 struct Split {
   int64_t N;  // steps in the stream (> 0)
   int W;      // workers that take steps
+  // partition-granular shares (C > 0): Pn partitions; pre / ppre are the step
+  // and partition prefixes per sequence, B sequences, H items per sequence
+  int C, Pn, H, B;
+  const int* pre;
+  const int* ppre;
+
+  // first stream step of partition g (g < Pn)
+  __device__ __forceinline__ int64_t partition_start(int64_t g) const {
+    const int b = last_le(ppre, B, g);
+    const int n = (pre[b + 1] - pre[b]) / H, np = (n + C - 1) / C;
+    const int r = (int)(g - ppre[b]);
+    return pre[b] + (int64_t)(r / np) * n + (int64_t)(r % np) * C;
+  }
+  // partition holding stream step x
+  __device__ __forceinline__ int64_t partition_of(int64_t x) const {
+    const int b = last_le(pre, B, x);
+    const int n = (pre[b + 1] - pre[b]) / H, np = (n + C - 1) / C;
+    const int r = (int)(x - pre[b]);
+    return ppre[b] + (int64_t)(r / n) * np + (r % n) / C;
+  }
   // First step of worker w's share (start(W) == N).
-  __device__ __forceinline__ int64_t start(int w) const { return (int64_t)w * N / W; }
+  __device__ __forceinline__ int64_t start(int w) const {
+    if (C == 0) return (int64_t)w * N / W;
+    const int64_t g = (int64_t)w * Pn / W;
+    return g >= Pn ? N : partition_start(g);
+  }
   // The worker whose share holds stream step x: the largest w with start(w) <= x.
   __device__ __forceinline__ int worker_of(int64_t x) const {
-    return (int)(((x + 1) * W - 1) / N);
+    if (C == 0) return (int)(((x + 1) * W - 1) / N);
+    return (int)(((partition_of(x) + 1) * W - 1) / Pn);
   }
 };
 
-__device__ __forceinline__ Split make_split(int num_workers, int N) {
+// The split of N stream steps over at most num_workers workers; with C > 0,
+// in whole partitions (pre / ppre as exported by the decode kernels).
+__device__ __forceinline__ Split make_split(int num_workers, int N, int C = 0, int H = 1,
+                                            int B = 0, const int* pre = nullptr,
+                                            const int* ppre = nullptr) {
   Split s;
   s.N = N;
-  const int cap = N / kMinChunk;
+  s.C = C;
+  s.H = H;
+  s.B = B;
+  s.pre = pre;
+  s.ppre = ppre;
+  s.Pn = C > 0 ? ppre[B] : 0;
+  int cap = N / kMinChunk;
+  if (C > 0 && s.Pn < cap) cap = s.Pn;  // every worker gets at least one partition
   s.W = num_workers < cap ? num_workers : (cap > 0 ? cap : 1);
   return s;
 }
@@ -140,21 +191,13 @@ __device__ __forceinline__ void advance(Cursor& c, const int* s_pre, const int* 
   c.n = (c.L + step - 1) / step;
 }
 
-// Stream-order index of the partition holding the cursor's step (the item
-// index when C == 0).
-__device__ __forceinline__ int partition_index(const Cursor& c, int H, int C, const int* s_ppre) {
-  if (C == 0) return c.item(H);
-  const int np = (c.n + C - 1) / C;
-  return s_ppre[c.b] + c.h * np + c.k / C;
-}
-
 // The step ends a segment of a worker whose last stream step has index
 // `last_j` within its share (j = index of this step within the share).
-__device__ __forceinline__ bool segment_ends(const Cursor& c, int j, int last_j, int C) {
-  return j == last_j || c.k == c.n - 1 || (C > 0 && (c.k + 1) % C == 0);
+__device__ __forceinline__ bool segment_ends(const Cursor& c, int j, int last_j) {
+  return j == last_j || c.k == c.n - 1;
 }
-__device__ __forceinline__ bool segment_starts(const Cursor& c, int j, int C) {
-  return j == 0 || c.k == 0 || (C > 0 && c.k % C == 0);
+__device__ __forceinline__ bool segment_starts(const Cursor& c, int j) {
+  return j == 0 || c.k == 0;
 }
 
 // Copies the scan's prefixes to global memory for the merge kernel:

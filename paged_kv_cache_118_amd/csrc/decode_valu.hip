@@ -213,7 +213,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
     if (blockIdx.x == 0 && wv == 0) export_prefixes(s_pre, s_ppre, B, C, a.ws_pre, a.ws_ppre);
     const int N = s_pre[B];  // empty sequences get their zero rows from the merge
     if (N == 0) return;
-    sp = make_split(a.num_workers, N);
+    sp = make_split(a.num_workers, N, C, H, B, s_pre, s_ppre);
     if (worker >= sp.W) return;
     x0 = sp.start(worker);
     count = (int)(sp.start(worker + 1) - x0);
@@ -321,7 +321,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
 
   auto compute = [&](const Cursor& cu, const uint4 (&kr)[NK], uint4 (&vr)[NK],
                      const uint4 (&qr)[NK], int j) {
-    if (segment_starts(cu, j, C)) {
+    if (segment_starts(cu, j)) {
       m_run = -INFINITY;
       l_lane = 0.f;
 #pragma unroll
@@ -351,7 +351,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
     for (int r = 0; r < R; ++r) acc[r] *= alpha;
     lane_pv<TT, R, NK>(acc, pt, vr);
 
-    if (segment_ends(cu, j, count - 1, C)) {
+    if (segment_ends(cu, j, count - 1)) {
       const float l_tot = wave_sum(l_lane);
       const int item = cu.item(H);
       if (seg_k0 == 0 && cu.k == cu.n - 1) {  // the whole item: final row
@@ -359,7 +359,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
 #pragma unroll
         for (int r = 0; r < R; ++r) store_out<TT>(a.out, orow + lane + 64 * r, acc[r] / l_tot);
       } else {
-        const int64_t slot = (int64_t)partition_index(cu, H, C, s_ppre) + worker;
+        const int64_t slot = (int64_t)cu.item(H) + worker;
         // partial record (pa_internal.h): o, then the 128-byte m / l line
         float* rec = a.ws_part + slot * part_record(1, D);
 #pragma unroll

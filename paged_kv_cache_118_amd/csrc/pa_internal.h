@@ -122,7 +122,7 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, pa_dtype dt, hipStream_t s);
 hipError_t launch_decode_generic(const DecodeArgs& a, pa_dtype dt, hipStream_t s);
 // Merge of the split items' partials (decode_merge.hip); step = tokens per
 // worker step of the decode kernel that ran.
-hipError_t launch_decode_merge(const DecodeArgs& a, pa_dtype dt, int items_per_seq, int step,
+hipError_t launch_decode_merge(const DecodeArgs& a, pa_dtype dt, int items_per_seq,
                                hipStream_t s);
 bool decode_valu_supported(pa_dtype dt, int head_dim, int block_size);
 // Resident wavefronts per CU of the kernel a call with these arguments runs.
