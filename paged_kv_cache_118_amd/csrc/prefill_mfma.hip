@@ -61,9 +61,34 @@ __device__ __forceinline__ float16_t mfma32(BF16, const uint4& a, const uint4& b
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf168_t, a),
                                                  __builtin_bit_cast(bf168_t, b), c, 0, 0, 0);
 }
-template <typename TT>
-__device__ __forceinline__ uint32_t pack2(TT t, float lo, float hi) {
-  return (uint32_t)to_bits(t, lo) | ((uint32_t)to_bits(t, hi) << 16);
+// Two fp32 values to one packed pair, round to nearest even (one
+// v_cvt_pk_{f16,bf16}_f32).
+__device__ __forceinline__ uint32_t pack2(F16, float lo, float hi) {
+  const half2_t h = {(_Float16)lo, (_Float16)hi};
+  return __builtin_bit_cast(uint32_t, h);
+}
+__device__ __forceinline__ uint32_t pack2(BF16, float lo, float hi) {
+  const bf162_t h = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, h);
+}
+// c + the two elements of a packed pair, in fp32 (a dot product with 1, 1).
+__device__ __forceinline__ float psum2(F16, uint32_t w, float c) {
+  return dot2(F16{}, w, 0x3C003C00u, c);
+}
+__device__ __forceinline__ float psum2(BF16, uint32_t w, float c) {
+  return dot2(BF16{}, w, 0x3F803F80u, c);
+}
+// max / sum of x and x in the lane 32 apart (one v_permlane32_swap: lanes
+// 0-31 of the copy trade places with lanes 32-63 of x).
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_add(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // Lane i holds the physical id of logical block base + i (0 for entries past
@@ -194,6 +219,20 @@ __global__ __launch_bounds__(64 * WV) void prefill_mfma_kernel(PrefillArgs a) {
     for (int s = 0; s < QN; ++s)
       qr[s] = qrow < nrows ? ld16(qp + (WR == 16 ? 64 : 32) * s) : make_uint4(0, 0, 0, 0);
   }
+  // Scores are used as s * scl with scl = |scale * log2 e| > 0 (so the
+  // maximum of the raw dot products gives the maximum score, and the scale
+  // folds into the exponent's fma); a negative scale flips q's sign bits
+  // instead, which is exact.
+  const float scl = fabsf(a.scale_log2e);
+  if (a.scale_log2e < 0.f) {
+#pragma unroll
+    for (int s = 0; s < QN; ++s) {
+      qr[s].x ^= 0x80008000u;
+      qr[s].y ^= 0x80008000u;
+      qr[s].z ^= 0x80008000u;
+      qr[s].w ^= 0x80008000u;
+    }
+  }
 
   float m_run = -INFINITY, l_lane = 0.f;
   float4_t acc[MT];        // 16 rows: O^T tile mt (dims 16 mt ..)
@@ -215,8 +254,7 @@ __global__ __launch_bounds__(64 * WV) void prefill_mfma_kernel(PrefillArgs a) {
 
   // Cooperative loads of group grp into registers: K chunk c = tid + 256 r
   // is piece c / 32 of key c % 32; V chunk c is row c % D of slab c / D.
-  uint4 pk[NCK], pv[NCV];
-  auto load = [&](int grp) {
+  auto load = [&](int grp, uint4 (&pk)[NCK], uint4 (&pv)[NCV]) {
     const int tok = grp * kKeys;
     const int lb0 = BSC ? tok / BSC : tok / bs;
     if (lb0 < tw.base || lb0 + NBG > tw.base + 64)
@@ -254,7 +292,7 @@ __global__ __launch_bounds__(64 * WV) void prefill_mfma_kernel(PrefillArgs a) {
       pv[r] = ld16(pick(vblk, relv) + ((offv / VS) * D + (uint32_t)(c % D)) * (VS * EB));
     }
   };
-  auto store = [&](char* buf) {
+  auto store = [&](char* buf, const uint4 (&pk)[NCK], const uint4 (&pv)[NCV]) {
 #pragma unroll
     for (int r = 0; r < NCK; ++r) {
       const int c = tid + kThreads * r;
@@ -285,11 +323,11 @@ __global__ __launch_bounds__(64 * WV) void prefill_mfma_kernel(PrefillArgs a) {
         st[j] = mfma(TT{}, *reinterpret_cast<const uint4*>(kr + 64 * i), qr[i], st[j]);
     }
     const char* vr = buf + KBUF + kb * VSP + n * 16;  // V^T operand: slab kb, row d = n + 16 mt
-    float sc[8];
+    float sc[8];  // raw dot products; the score is sc * scl
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      sc[e] = st[0][e] * a.scale_log2e;
-      sc[4 + e] = st[1][e] * a.scale_log2e;
+      sc[e] = st[0][e];
+      sc[4 + e] = st[1][e];
     }
     if (tok + kKeys - 1 > pos0) {  // the group reaches past the tile's first row
 #pragma unroll
@@ -300,7 +338,7 @@ __global__ __launch_bounds__(64 * WV) void prefill_mfma_kernel(PrefillArgs a) {
 #pragma unroll
     for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sc[e]);
     mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = xor32_max(mx) * scl;
     // mx is finite: key 0 is in every row's range, and the first group of
     // every row reaches here with m_run = -inf
     if (__builtin_amdgcn_ballot_w64(mx > m_run + kSlack) != 0) {
@@ -313,13 +351,15 @@ __global__ __launch_bounds__(64 * WV) void prefill_mfma_kernel(PrefillArgs a) {
     }
     float pw[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      pw[e] = __builtin_amdgcn_exp2f(sc[e] - m_run);
-      l_lane += pw[e];
-    }
-    // P^T operand: keys 8 kb .. 8 kb + 7 of query n, all held by this lane
+    for (int e = 0; e < 8; ++e) pw[e] = __builtin_amdgcn_exp2f(fmaf(sc[e], scl, -m_run));
+    // P^T operand: keys 8 kb .. 8 kb + 7 of query n, all held by this lane;
+    // the row sum takes the same rounded weights the matrix op does
     const uint4 pb = make_uint4(pack2(TT{}, pw[0], pw[1]), pack2(TT{}, pw[2], pw[3]),
                                 pack2(TT{}, pw[4], pw[5]), pack2(TT{}, pw[6], pw[7]));
+    l_lane = psum2(TT{}, pb.w, psum2(TT{}, pb.z, psum2(TT{}, pb.y, psum2(TT{}, pb.x, l_lane))));
+    uint4 v[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) v[mt] = *reinterpret_cast<const uint4*>(vr + mt * 16 * 16);
     if (vtail && tok + kKeys > last) {  // zero V of positions past `last` in this group
       const int keep = min(max(last + 1 - tok - kb * VS, 0), VS);
       uint32_t m4[4];
@@ -328,18 +368,14 @@ __global__ __launch_bounds__(64 * WV) void prefill_mfma_kernel(PrefillArgs a) {
         m4[i] = ((2 * i < keep) ? 0xffffu : 0u) | ((2 * i + 1 < keep) ? 0xffff0000u : 0u);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        uint4 v = *reinterpret_cast<const uint4*>(vr + mt * 16 * 16);
-        v.x &= m4[0];
-        v.y &= m4[1];
-        v.z &= m4[2];
-        v.w &= m4[3];
-        acc[mt] = mfma(TT{}, v, pb, acc[mt]);
+        v[mt].x &= m4[0];
+        v[mt].y &= m4[1];
+        v[mt].z &= m4[2];
+        v[mt].w &= m4[3];
       }
-    } else {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        acc[mt] = mfma(TT{}, *reinterpret_cast<const uint4*>(vr + mt * 16 * 16), pb, acc[mt]);
     }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma(TT{}, v[mt], pb, acc[mt]);
   };
 
   // 32 rows per wavefront.  Row rho of the S^T A operand is key
@@ -357,9 +393,9 @@ __global__ __launch_bounds__(64 * WV) void prefill_mfma_kernel(PrefillArgs a) {
 #pragma unroll
     for (int s2 = 0; s2 < D / 16; ++s2)
       st = mfma32(TT{}, *reinterpret_cast<const uint4*>(kr + 32 * s2), qr[s2], st);
-    float sc[16];
+    float sc[16];  // raw dot products; the score is sc * scl
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sc[r] = st[r] * a.scale_log2e;
+    for (int r = 0; r < 16; ++r) sc[r] = st[r];
     if (tok + kKeys - 1 > pos0) {  // the group reaches past the tile's first row
 #pragma unroll
       for (int r = 0; r < 16; ++r)
@@ -368,7 +404,7 @@ __global__ __launch_bounds__(64 * WV) void prefill_mfma_kernel(PrefillArgs a) {
     float mx = sc[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = xor32_max(mx) * scl;
     if (__builtin_amdgcn_ballot_w64(mx > m_run + kSlack) != 0) {
       const float m_new = mx > m_run + kSlack ? mx : m_run;
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -379,10 +415,7 @@ __global__ __launch_bounds__(64 * WV) void prefill_mfma_kernel(PrefillArgs a) {
     }
     float pw[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      pw[r] = __builtin_amdgcn_exp2f(sc[r] - m_run);
-      l_lane += pw[r];
-    }
+    for (int r = 0; r < 16; ++r) pw[r] = __builtin_amdgcn_exp2f(fmaf(sc[r], scl, -m_run));
     uint4 pb[2];
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh)
@@ -390,11 +423,22 @@ __global__ __launch_bounds__(64 * WV) void prefill_mfma_kernel(PrefillArgs a) {
                           pack2(TT{}, pw[8 * kh + 2], pw[8 * kh + 3]),
                           pack2(TT{}, pw[8 * kh + 4], pw[8 * kh + 5]),
                           pack2(TT{}, pw[8 * kh + 6], pw[8 * kh + 7]));
+    // the row sum takes the same rounded weights the matrix op does
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+      l_lane = psum2(TT{}, pb[kh].w,
+                     psum2(TT{}, pb[kh].z, psum2(TT{}, pb[kh].y, psum2(TT{}, pb[kh].x, l_lane))));
     // V^T operand of key half kh: slab 2 kh + hh, row d = 32 mt + c32
     const bool vmask = vtail && tok + kKeys > last;
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
       const char* vr = buf + KBUF + (2 * kh + hh) * VSP + c32 * 16;
+      uint4 v[D / 32];
+#pragma unroll
+      for (int mt = 0; mt < D / 32; ++mt) v[mt] = *reinterpret_cast<const uint4*>(vr + mt * 32 * 16);
+      // Only the operands depend on the branch, so the accumulators stay in
+      // place (MFMAs on both sides of a branch made the compiler copy all of
+      // them at the join).
       if (vmask) {  // zero V of positions past `last` in this group
         const int keep = min(max(last + 1 - tok - VS * (2 * kh + hh), 0), VS);
         uint32_t m4[4];
@@ -403,33 +447,39 @@ __global__ __launch_bounds__(64 * WV) void prefill_mfma_kernel(PrefillArgs a) {
           m4[i] = ((2 * i < keep) ? 0xffffu : 0u) | ((2 * i + 1 < keep) ? 0xffff0000u : 0u);
 #pragma unroll
         for (int mt = 0; mt < D / 32; ++mt) {
-          uint4 v = *reinterpret_cast<const uint4*>(vr + mt * 32 * 16);
-          v.x &= m4[0];
-          v.y &= m4[1];
-          v.z &= m4[2];
-          v.w &= m4[3];
-          acc32[mt] = mfma32(TT{}, v, pb[kh], acc32[mt]);
+          v[mt].x &= m4[0];
+          v[mt].y &= m4[1];
+          v[mt].z &= m4[2];
+          v[mt].w &= m4[3];
         }
-      } else {
-#pragma unroll
-        for (int mt = 0; mt < D / 32; ++mt)
-          acc32[mt] = mfma32(TT{}, *reinterpret_cast<const uint4*>(vr + mt * 32 * 16), pb[kh],
-                             acc32[mt]);
       }
+#pragma unroll
+      for (int mt = 0; mt < D / 32; ++mt) acc32[mt] = mfma32(TT{}, v[mt], pb[kh], acc32[mt]);
     }
   };
 
-  load(0);
-  for (int grp = 0; grp < ngroups; ++grp) {
+  // Group g's K/V travel HBM -> registers two groups ahead of their use
+  // (register sets A and B alternate), then registers -> LDS buffer g % 2
+  // just before the group's barrier.  Buffer g % 2 was last read by group
+  // g - 2, which every wavefront finished before the barrier of group g - 1.
+  auto step = [&](int grp, uint4 (&pk)[NCK], uint4 (&pv)[NCV]) {
     char* buf = lds + (grp & 1) * BUF;
-    store(buf);
-    if (grp + 1 < ngroups) load(grp + 1);
+    store(buf, pk, pv);
+    if (grp + 2 < ngroups) load(grp + 2, pk, pv);
     __syncthreads();
     // wavefronts without rows, or whose rows all end before this group,
     // only help with the loads
     if (nrows > 0 && grp * kKeys <= last) {
       if constexpr (WR == 16) compute(grp, buf); else compute32(grp, buf);
     }
+  };
+  uint4 pkA[NCK], pvA[NCV], pkB[NCK], pvB[NCV];
+  load(0, pkA, pvA);
+  if (ngroups > 1) load(1, pkB, pvB);
+  for (int grp = 0; grp < ngroups; grp += 2) {
+    step(grp, pkA, pvA);
+    if (grp + 1 >= ngroups) break;
+    step(grp + 1, pkB, pvB);
   }
 
   if constexpr (WR == 16) {
@@ -445,7 +495,7 @@ __global__ __launch_bounds__(64 * WV) void prefill_mfma_kernel(PrefillArgs a) {
         for (int e = 0; e < 4; ++e) out[mt * 16 + e] = to_bits(TT{}, acc[mt][e] * inv);
     }
   } else {
-    const float l_tot = l_lane + __shfl_xor(l_lane, 32);
+    const float l_tot = xor32_add(l_lane);
     if (c32 < nrows) {
       const float inv = 1.f / l_tot;
       uint16_t* out = reinterpret_cast<uint16_t*>(a.out) +
@@ -483,7 +533,14 @@ hipError_t launch_w(const PrefillArgs& a, hipStream_t s) {
 // Tuning overrides: PA_PREFILL_ROWS (16, 32), PA_PREFILL_WAVES (2, 4).
 template <typename TT, int D, int NBG>
 hipError_t launch_g(const PrefillArgs& a, hipStream_t s) {
-  int wr = a.max_query_len >= kPrefill32MinRows ? 32 : 16, wv = wr == 32 ? 2 : 4;
+  // 32-row wavefronts from 64-row chunks on.  Four of them per workgroup
+  // when chunks reach 128 rows and contexts 2048 tokens: each key group's
+  // LDS fill then serves twice the rows, which pays on long contexts (0.66
+  // against 0.59 PFLOP/s on 256-row chunks of 600-8300-token contexts), while
+  // on short contexts with ragged chunks two do better (the partly idle
+  // wavefronts of a 128-row workgroup cost more than the shared fills save).
+  int wr = a.max_query_len >= kPrefill32MinRows ? 32 : 16;
+  int wv = wr == 16 || (a.max_query_len >= 4 * 32 && a.len_cap >= 2048) ? 4 : 2;
   if (const char* e = std::getenv("PA_PREFILL_ROWS")) wr = atoi(e) == 32 ? 32 : atoi(e) == 16 ? 16 : wr;
   if (const char* e = std::getenv("PA_PREFILL_WAVES")) wv = atoi(e) == 2 ? 2 : 4;
   if (wr == 32)
