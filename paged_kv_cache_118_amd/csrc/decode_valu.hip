@@ -50,7 +50,6 @@ __device__ __forceinline__ float dpp(float x) {
 __device__ __forceinline__ float bcast_lane(float x, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
 }
-__device__ __forceinline__ float xor_max(float x, int m) { return fmaxf(x, __shfl_xor(x, m)); }
 __device__ __forceinline__ float wave_sum(float x) {
   for (int m = 1; m < 64; m <<= 1) x += __shfl_xor(x, m);
   return x;
@@ -336,8 +335,8 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
     if (tq >= nvalid) sc = -INFINITY;  // select, never multiply: masked K may be NaN
     float mx = fmaxf(sc, dpp<0x124>(sc));  // row_ror:4
     mx = fmaxf(mx, dpp<0x128>(mx));        // row_ror:8
-    mx = xor_max(mx, 16);
-    mx = xor_max(mx, 32);
+    mx = xor16_max(mx);
+    mx = xor32_max(mx);
     const float m_new = fmaxf(m_run, mx);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     const float pv = __builtin_amdgcn_exp2f(sc - m_new);

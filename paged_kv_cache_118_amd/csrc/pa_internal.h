@@ -60,6 +60,26 @@ __device__ __forceinline__ float dot2(BF16, uint32_t a, uint32_t b, float c) {
                                          __builtin_bit_cast(bf162_t, b), c, false);
 }
 
+// ------------------------------------------------------- lane exchanges --
+// max / sum of x and x in the lane 32 (16) apart, without LDS: one
+// v_permlane32_swap (v_permlane16_swap) of x with a copy of itself leaves,
+// in every lane, x and its partner's x in the two registers.
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_add(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor16_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // ------------------------------------------------------------ decode args --
 struct DecodeArgs {
   void* out;

@@ -78,18 +78,6 @@ __device__ __forceinline__ float psum2(F16, uint32_t w, float c) {
 __device__ __forceinline__ float psum2(BF16, uint32_t w, float c) {
   return dot2(BF16{}, w, 0x3F803F80u, c);
 }
-// max / sum of x and x in the lane 32 apart (one v_permlane32_swap: lanes
-// 0-31 of the copy trade places with lanes 32-63 of x).
-__device__ __forceinline__ float xor32_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                  false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float xor32_add(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                  false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
 
 // Lane i holds the physical id of logical block base + i (0 for entries past
 // the row or outside the pool: such blocks only feed masked keys).
@@ -337,7 +325,7 @@ __global__ __launch_bounds__(64 * WV) void prefill_mfma_kernel(PrefillArgs a) {
     float mx = sc[0];
 #pragma unroll
     for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sc[e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = xor16_max(mx);
     mx = xor32_max(mx) * scl;
     // mx is finite: key 0 is in every row's range, and the first group of
     // every row reaches here with m_run = -inf
