@@ -257,13 +257,25 @@ __global__ __launch_bounds__(64 * WV) void prefill_mfma_kernel(PrefillArgs a) {
       kblk[q] = kbase + ph * kblock + khead;
       vblk[q] = vbase + ph * vblock + vhead;
     }
-    auto pick = [&](const char* const (&b)[NBG], uint32_t rel) {  // block of key tok + rel
-      const char* p = b[0];
-      if constexpr (NBG > 1) {
-#pragma unroll
-        for (int u = 1; u < NBG; ++u) p = rel >= (uint32_t)(u * BSC) ? b[u] : p;
+    // base of the block holding key tok + rel
+    auto pick = [&](const char* const (&b)[NBG], uint32_t rel) {
+      if constexpr (NBG == 4) {
+        // bit tests on copies of the four bases: with a chain of compares
+        // the compiler formed an indexed load from the array, which put the
+        // array in scratch memory
+        const char* b0 = b[0];
+        const char* b1 = b[1];
+        const char* b2 = b[2];
+        const char* b3 = b[3];
+        const uint32_t q = rel / (uint32_t)(BSC > 0 ? BSC : 1);  // 0 .. 3
+        const char* lo = (q & 1) ? b1 : b0;
+        const char* hi = (q & 1) ? b3 : b2;
+        return (q & 2) ? hi : lo;
+      } else {
+        const char* p = b[0];
+        if constexpr (NBG > 1) p = rel >= (uint32_t)BSC ? b[1] : p;
+        return p;
       }
-      return p;
     };
 #pragma unroll
     for (int r = 0; r < NCK; ++r) {
