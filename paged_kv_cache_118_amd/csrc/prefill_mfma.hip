@@ -37,6 +37,11 @@ namespace {
 
 constexpr int kKeys = 32;  // keys per step
 
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glb_void;
+// s_waitcnt operand: vmcnt 0, expcnt and lgkmcnt at their maxima (gfx9).
+constexpr int kVmcntZero = 0x0F70;
+
 __device__ __forceinline__ uint4 ld16(const char* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
@@ -132,7 +137,7 @@ constexpr int kPrefill32MinRows = 64;
 // WR = query rows per wavefront: 16 (16x16x32 MFMAs) or 32 (32x32x16 MFMAs,
 // each K/V operand read from LDS then serves twice as many rows); WV =
 // wavefronts per workgroup.
-template <typename TT, int D, int NBG, int WR, int WV>
+template <typename TT, int D, int NBG, int WR, int WV, bool DMA>
 __global__ __launch_bounds__(64 * WV) void prefill_mfma_kernel(PrefillArgs a) {
   constexpr int kWaves = WV;
   constexpr int kThreads = 64 * WV;
@@ -148,7 +153,25 @@ __global__ __launch_bounds__(64 * WV) void prefill_mfma_kernel(PrefillArgs a) {
   constexpr int NCK = kKeys * NC / kThreads;       // K chunks per thread and group
   constexpr int NCV = (kKeys / VS) * D / kThreads;  // V chunks per thread and group
   static_assert(NCK >= 1 && NCV >= 1, "head_dim too small for the cooperative load");
-  __shared__ __align__(16) char lds[2 * BUF];
+  // Direct global -> LDS loads (32-row wavefronts): each 16-byte load of a
+  // wavefront lands at LDS base + 16 * lane, so a load instruction fills 1
+  // KiB contiguously and the layout is chosen by what each lane fetches:
+  //   K: [piece][32 keys][16 B], key slot s of a piece row holding key
+  //      krow(s) -- the key the S^T operand's lane s reads -- so a half
+  //      wavefront's operand read is one contiguous 512-byte run;
+  //   V: [slab][D][16 B], as in the pool, unpadded.
+  // No staging registers: the loads of group g + 1 fly while group g is
+  // computed and the wavefront waits for them before the next barrier.
+  static_assert(!DMA || WR == 32, "direct LDS loads only with 32-row wavefronts");
+  constexpr int KBUFD = NC * kKeys * 16;
+  constexpr int BUFD = KBUFD + (kKeys / VS) * D * 16;
+  constexpr int NID = 2 * D / 16;  // 1-KiB load instructions per group (K, then V)
+  static_assert(!DMA || NID % WV == 0, "direct loads must split evenly over the wavefronts");
+  __shared__ __align__(16) char lds[DMA ? BUFD : 2 * BUF];
+  // second buffer of the direct-load path, a separate object: with both
+  // buffers in one array the compiler could not tell the operand reads of
+  // one from the loads in flight into the other, and waited for the loads
+  __shared__ __align__(16) char lds_b[DMA ? BUFD : 16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -292,6 +315,62 @@ __global__ __launch_bounds__(64 * WV) void prefill_mfma_kernel(PrefillArgs a) {
       pv[r] = ld16(pick(vblk, relv) + ((offv / VS) * D + (uint32_t)(c % D)) * (VS * EB));
     }
   };
+  // Direct loads of group grp into LDS buffer buf: wavefront wv issues load
+  // instructions wv * NID / WV ..; instruction i < D / 16 fills K pieces 2 i
+  // and 2 i + 1 (lane: piece 2 i + lane / 32, key krow(lane % 32)), the
+  // others 64 rows of a V slab.
+  auto dma = [&](int grp, char* buf) {
+    const int tok = grp * kKeys;
+    const int lb0 = BSC ? tok / BSC : tok / bs;
+    if (lb0 < tw.base || lb0 + NBG > tw.base + 64)
+      tw.load(trow, a.max_blocks_per_seq, a.num_blocks, lb0, lane);
+    const uint32_t o0 = (uint32_t)(tok - lb0 * bs);
+    const uint32_t lim = (uint32_t)(last_wg - tok);
+    const char* kblk[NBG];
+    const char* vblk[NBG];
+#pragma unroll
+    for (int q = 0; q < NBG; ++q) {
+      const int64_t ph = tw.get(lb0 + q);
+      kblk[q] = kbase + ph * kblock + khead;
+      vblk[q] = vbase + ph * vblock + vhead;
+    }
+    auto pick = [&](const char* const (&b)[NBG], uint32_t rel) {
+      if constexpr (NBG == 4) {
+        const char* b0 = b[0];
+        const char* b1 = b[1];
+        const char* b2 = b[2];
+        const char* b3 = b[3];
+        const uint32_t q = rel / (uint32_t)(BSC > 0 ? BSC : 1);
+        const char* lo = (q & 1) ? b1 : b0;
+        const char* hi = (q & 1) ? b3 : b2;
+        return (q & 2) ? hi : lo;
+      } else {
+        const char* p = b[0];
+        if constexpr (NBG > 1) p = rel >= (uint32_t)BSC ? b[1] : p;
+        return p;
+      }
+    };
+    const int key = 16 * (c32 >> 4) + 8 * ((c32 >> 2) & 1) + 4 * ((c32 >> 3) & 1) + (c32 & 3);
+    const uint32_t rel = min((uint32_t)key, lim);
+    const uint32_t off = NBG == 1 ? o0 + rel : rel & (uint32_t)(BSC - 1);
+    const char* kp = pick(kblk, rel) + ((uint32_t)hh * bs + off) * 16;  // piece hh of the key
+#pragma unroll
+    for (int t = 0; t < NID / WV; ++t) {
+      const int i = wv * (NID / WV) + t;  // wave-uniform
+      if (i < D / 16) {
+        __builtin_amdgcn_global_load_lds((glb_void*)(kp + (int64_t)2 * i * bs * 16),
+                                         (lds_void*)(buf + i * 1024), 16, 0, 0);
+      } else {
+        const int iv = i - D / 16, slab = iv / (D / 64);
+        const uint32_t relv = min((uint32_t)slab * VS, lim & ~(uint32_t)(VS - 1));
+        const uint32_t offv = NBG == 1 ? o0 + relv : relv & (uint32_t)(BSC - 1);
+        const char* vp = pick(vblk, relv) +
+                         ((offv / VS) * D + (uint32_t)((iv % (D / 64)) * 64 + lane)) * (VS * EB);
+        __builtin_amdgcn_global_load_lds((glb_void*)vp, (lds_void*)(buf + KBUFD + iv * 1024), 16,
+                                         0, 0);
+      }
+    }
+  };
   auto store = [&](char* buf, const uint4 (&pk)[NCK], const uint4 (&pv)[NCV]) {
 #pragma unroll
     for (int r = 0; r < NCK; ++r) {
@@ -389,10 +468,12 @@ __global__ __launch_bounds__(64 * WV) void prefill_mfma_kernel(PrefillArgs a) {
     float16_t st;
 #pragma unroll
     for (int r = 0; r < 16; ++r) st[r] = 0.f;
-    const char* kr = buf + krow * KP + hh * 16;
+    // K operand of k-step s2: piece 2 s2 + hh of key krow
+    const char* kr = DMA ? buf + (hh * kKeys + c32) * 16 : buf + krow * KP + hh * 16;
+    constexpr int KSTEP = DMA ? 2 * kKeys * 16 : 32;
 #pragma unroll
     for (int s2 = 0; s2 < D / 16; ++s2)
-      st = mfma32(TT{}, *reinterpret_cast<const uint4*>(kr + 32 * s2), qr[s2], st);
+      st = mfma32(TT{}, *reinterpret_cast<const uint4*>(kr + KSTEP * s2), qr[s2], st);
     float sc[16];  // raw dot products; the score is sc * scl
 #pragma unroll
     for (int r = 0; r < 16; ++r) sc[r] = st[r];
@@ -432,7 +513,8 @@ __global__ __launch_bounds__(64 * WV) void prefill_mfma_kernel(PrefillArgs a) {
     const bool vmask = vtail && tok + kKeys > last;
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
-      const char* vr = buf + KBUF + (2 * kh + hh) * VSP + c32 * 16;
+      const char* vr = DMA ? buf + KBUFD + (2 * kh + hh) * (D * 16) + c32 * 16
+                           : buf + KBUF + (2 * kh + hh) * VSP + c32 * 16;
       uint4 v[D / 32];
 #pragma unroll
       for (int mt = 0; mt < D / 32; ++mt) v[mt] = *reinterpret_cast<const uint4*>(vr + mt * 32 * 16);
@@ -458,6 +540,24 @@ __global__ __launch_bounds__(64 * WV) void prefill_mfma_kernel(PrefillArgs a) {
     }
   };
 
+  if constexpr (DMA) {
+    // group g in LDS buffer g % 2: its loads were issued during group g - 1;
+    // this wavefront waits for its own, the barrier for everyone's (and for
+    // every wavefront to be done with group g - 1, whose buffer the loads of
+    // group g + 1 then overwrite)
+    auto step = [&](int grp, char* cur, char* nxt) {
+      __builtin_amdgcn_s_waitcnt(kVmcntZero);
+      __syncthreads();
+      if (grp + 1 < ngroups) dma(grp + 1, nxt);
+      if (nrows > 0 && grp * kKeys <= last) compute32(grp, cur);
+    };
+    dma(0, lds);
+    for (int grp = 0; grp < ngroups; grp += 2) {
+      step(grp, lds, lds_b);
+      if (grp + 1 >= ngroups) break;
+      step(grp + 1, lds_b, lds);
+    }
+  } else {
   // Group g's K/V travel HBM -> registers two groups ahead of their use
   // (register sets A and B alternate), then registers -> LDS buffer g % 2
   // just before the group's barrier.  Buffer g % 2 was last read by group
@@ -480,6 +580,7 @@ __global__ __launch_bounds__(64 * WV) void prefill_mfma_kernel(PrefillArgs a) {
     step(grp, pkA, pvA);
     if (grp + 1 >= ngroups) break;
     step(grp + 1, pkB, pvB);
+  }
   }
 
   if constexpr (WR == 16) {
@@ -514,23 +615,20 @@ __global__ __launch_bounds__(64 * WV) void prefill_mfma_kernel(PrefillArgs a) {
   }
 }
 
-template <typename TT, int D, int NBG, int WR, int WV>
+template <typename TT, int D, int NBG, int WR, int WV, bool DMA = false>
 hipError_t launch_w(const PrefillArgs& a, hipStream_t s) {
   const int64_t tpg = (a.max_query_len + WV * WR - 1) / (WV * WR);
   const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads;
   const int64_t wgs = (units + 7) / 8 * 8 * (a.num_q_heads / a.num_kv_heads) * tpg;
   if (wgs > 0x7fffffff) return hipErrorInvalidValue;
   dim3 grid((unsigned)wgs);
-  hipLaunchKernelGGL((prefill_mfma_kernel<TT, D, NBG, WR, WV>), grid, dim3(64 * WV), 0, s, a);
+  hipLaunchKernelGGL((prefill_mfma_kernel<TT, D, NBG, WR, WV, DMA>), grid, dim3(64 * WV), 0, s, a);
   return hipGetLastError();
 }
 
-// Shape of the workgroup: 32 rows per wavefront and two wavefronts once
-// chunks reach kPrefill32MinRows rows, else 16 rows and four wavefronts.
-// Measured on ragged chunks (prompt tails of 1-512 rows after reused
-// prefixes) two 32-row wavefronts beat four, which leave more of a short
-// chunk's workgroup idle; on uniform 256-row chunks four were 9% faster.
-// Tuning overrides: PA_PREFILL_ROWS (16, 32), PA_PREFILL_WAVES (2, 4).
+// Shape of the workgroup (launch_g): rows per wavefront, wavefronts per
+// workgroup and how K/V reach LDS, from the longest chunk and the context
+// bound; PA_PREFILL_ROWS / _WAVES / _DMA override them (tests, tuning).
 template <typename TT, int D, int NBG>
 hipError_t launch_g(const PrefillArgs& a, hipStream_t s) {
   // 32-row wavefronts from 64-row chunks on.  Four of them per workgroup
@@ -543,8 +641,18 @@ hipError_t launch_g(const PrefillArgs& a, hipStream_t s) {
   int wv = wr == 16 || (a.max_query_len >= 4 * 32 && a.len_cap >= 2048) ? 4 : 2;
   if (const char* e = std::getenv("PA_PREFILL_ROWS")) wr = atoi(e) == 32 ? 32 : atoi(e) == 16 ? 16 : wr;
   if (const char* e = std::getenv("PA_PREFILL_WAVES")) wv = atoi(e) == 2 ? 2 : 4;
-  if (wr == 32)
+  if (wr == 32) {
+    // Direct global -> LDS loads with four wavefronts (long contexts: 0.68
+    // against 0.65 PFLOP/s on the 66B chunk writers, +6% at block size 8);
+    // with two, on short contexts, the register-staged loads were 4% faster.
+    // PA_PREFILL_DMA = 0 / 1 forces either.
+    bool dma = wv == 4;
+    if (const char* e = std::getenv("PA_PREFILL_DMA")) dma = atoi(e) != 0;
+    if (dma)
+      return wv == 2 ? launch_w<TT, D, NBG, 32, 2, true>(a, s)
+                     : launch_w<TT, D, NBG, 32, 4, true>(a, s);
     return wv == 2 ? launch_w<TT, D, NBG, 32, 2>(a, s) : launch_w<TT, D, NBG, 32, 4>(a, s);
+  }
   return wv == 2 ? launch_w<TT, D, NBG, 16, 2>(a, s) : launch_w<TT, D, NBG, 16, 4>(a, s);
 }
 

@@ -108,16 +108,19 @@ def test_prefill_rejects_unsupported():
     assert e.value.status == -2
 
 
-@pytest.mark.parametrize("rows,waves", [(16, 2), (16, 4), (32, 2), (32, 4)])
-def test_prefill_every_workgroup_shape(rows, waves, monkeypatch):
+@pytest.mark.parametrize("rows,waves,dma", [(16, 2, 0), (16, 4, 0), (32, 2, 0), (32, 4, 0),
+                                             (32, 2, 1), (32, 4, 1)])
+def test_prefill_every_workgroup_shape(rows, waves, dma, monkeypatch):
     """Each workgroup shape the library can launch (rows per wavefront x
-    wavefronts, forced through the tuning overrides) on ragged chunks, MHA and
-    grouped heads, against the oracle."""
+    wavefronts x register-staged or direct LDS loads, forced through the
+    tuning overrides) on ragged chunks, MHA and grouped heads, against the
+    oracle."""
     monkeypatch.setenv("PA_PREFILL_ROWS", str(rows))
     monkeypatch.setenv("PA_PREFILL_WAVES", str(waves))
-    for name in ("mha_f16_bs16", "gqa_bf16_g8_bs32"):
+    monkeypatch.setenv("PA_PREFILL_DMA", str(dma))
+    for name in ("mha_f16_bs16", "gqa_bf16_g8_bs32", "mha_f16_bs8", "gqa_f16_g4_bs16_d64"):
         spec = SPECS[name]
-        log(f"[prefill shape] {rows}x{waves} {name}")
+        log(f"[prefill shape] {rows}x{waves} dma={dma} {name}")
         case, q, qs = make_prefill_case(spec, [c for c, _ in CASES], [q for _, q in CASES],
                                         seed=rows + waves)
         err = max_err(run_prefill(case, q, qs), oracle_prefill(case, q, qs))
