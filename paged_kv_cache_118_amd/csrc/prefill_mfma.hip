@@ -166,7 +166,7 @@ __global__ __launch_bounds__(64 * WV) void prefill_mfma_kernel(PrefillArgs a) {
   constexpr int KBUFD = NC * kKeys * 16;
   constexpr int BUFD = KBUFD + (kKeys / VS) * D * 16;
   constexpr int NID = 2 * D / 16;  // 1-KiB load instructions per group (K, then V)
-  static_assert(!DMA || NID % WV == 0, "direct loads must split evenly over the wavefronts");
+  static_assert(!DMA || NID % (2 * WV) == 0, "direct loads must split evenly over the wavefronts");
   __shared__ __align__(16) char lds[DMA ? BUFD : 2 * BUF];
   // second buffer of the direct-load path, a separate object: with both
   // buffers in one array the compiler could not tell the operand reads of
@@ -315,10 +315,10 @@ __global__ __launch_bounds__(64 * WV) void prefill_mfma_kernel(PrefillArgs a) {
       pv[r] = ld16(pick(vblk, relv) + ((offv / VS) * D + (uint32_t)(c % D)) * (VS * EB));
     }
   };
-  // Direct loads of group grp into LDS buffer buf: wavefront wv issues load
-  // instructions wv * NID / WV ..; instruction i < D / 16 fills K pieces 2 i
-  // and 2 i + 1 (lane: piece 2 i + lane / 32, key krow(lane % 32)), the
-  // others 64 rows of a V slab.
+  // Direct loads of group grp into LDS buffer buf: a K load instruction i
+  // (i < D / 16) fills pieces 2 i and 2 i + 1 (lane: piece 2 i + lane / 32,
+  // key krow(lane % 32)), a V load instruction iv 64 rows of slab
+  // iv / (D / 64).
   auto dma = [&](int grp, char* buf) {
     const int tok = grp * kKeys;
     const int lb0 = BSC ? tok / BSC : tok / bs;
@@ -354,21 +354,23 @@ __global__ __launch_bounds__(64 * WV) void prefill_mfma_kernel(PrefillArgs a) {
     const uint32_t rel = min((uint32_t)key, lim);
     const uint32_t off = NBG == 1 ? o0 + rel : rel & (uint32_t)(BSC - 1);
     const char* kp = pick(kblk, rel) + ((uint32_t)hh * bs + off) * 16;  // piece hh of the key
+    // every wavefront issues NID / (2 WV) K loads, then as many V loads
+    constexpr int NIH = NID / 2 / WV;
 #pragma unroll
-    for (int t = 0; t < NID / WV; ++t) {
-      const int i = wv * (NID / WV) + t;  // wave-uniform
-      if (i < D / 16) {
-        __builtin_amdgcn_global_load_lds((glb_void*)(kp + (int64_t)2 * i * bs * 16),
-                                         (lds_void*)(buf + i * 1024), 16, 0, 0);
-      } else {
-        const int iv = i - D / 16, slab = iv / (D / 64);
-        const uint32_t relv = min((uint32_t)slab * VS, lim & ~(uint32_t)(VS - 1));
-        const uint32_t offv = NBG == 1 ? o0 + relv : relv & (uint32_t)(BSC - 1);
-        const char* vp = pick(vblk, relv) +
-                         ((offv / VS) * D + (uint32_t)((iv % (D / 64)) * 64 + lane)) * (VS * EB);
-        __builtin_amdgcn_global_load_lds((glb_void*)vp, (lds_void*)(buf + KBUFD + iv * 1024), 16,
-                                         0, 0);
-      }
+    for (int t = 0; t < NIH; ++t) {
+      const int i = wv * NIH + t;  // K pieces 2 i, 2 i + 1
+      __builtin_amdgcn_global_load_lds((glb_void*)(kp + (int64_t)2 * i * bs * 16),
+                                       (lds_void*)(buf + i * 1024), 16, 0, 0);
+    }
+#pragma unroll
+    for (int t = 0; t < NIH; ++t) {
+      const int iv = wv * NIH + t, slab = iv / (D / 64);  // rows (iv % (D / 64)) * 64 + lane
+      const uint32_t relv = min((uint32_t)slab * VS, lim & ~(uint32_t)(VS - 1));
+      const uint32_t offv = NBG == 1 ? o0 + relv : relv & (uint32_t)(BSC - 1);
+      const char* vp = pick(vblk, relv) +
+                       ((offv / VS) * D + (uint32_t)((iv % (D / 64)) * 64 + lane)) * (VS * EB);
+      __builtin_amdgcn_global_load_lds((glb_void*)vp, (lds_void*)(buf + KBUFD + iv * 1024), 16, 0,
+                                       0);
     }
   };
   auto store = [&](char* buf, const uint4 (&pk)[NCK], const uint4 (&pv)[NCV]) {
