@@ -644,11 +644,11 @@ hipError_t launch_g(const PrefillArgs& a, hipStream_t s) {
   if (const char* e = std::getenv("PA_PREFILL_ROWS")) wr = atoi(e) == 32 ? 32 : atoi(e) == 16 ? 16 : wr;
   if (const char* e = std::getenv("PA_PREFILL_WAVES")) wv = atoi(e) == 2 ? 2 : 4;
   if (wr == 32) {
-    // Direct global -> LDS loads with four wavefronts (long contexts: 0.68
-    // against 0.65 PFLOP/s on the 66B chunk writers, +6% at block size 8);
-    // with two, on short contexts, the register-staged loads were 4% faster.
-    // PA_PREFILL_DMA = 0 / 1 forces either.
-    bool dma = wv == 4;
+    // Direct global -> LDS loads (0.71-0.73 against 0.65-0.67 PFLOP/s on
+    // the 66B chunk writers; 3-4% faster on the short contexts of the
+    // prefix-sharing prompts, two wavefronts).  PA_PREFILL_DMA = 0 selects
+    // the register-staged loads.
+    bool dma = true;
     if (const char* e = std::getenv("PA_PREFILL_DMA")) dma = atoi(e) != 0;
     if (dma)
       return wv == 2 ? launch_w<TT, D, NBG, 32, 2, true>(a, s)
