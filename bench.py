@@ -251,7 +251,7 @@ class Workload:
             return a
 
         def step(a):
-            slots = np.concatenate([a.append(b, 1)[0] for b in range(B)])
+            slots, _ = a.append_batch(np.arange(B), np.ones(B, dtype=np.int32))
             tables, lens_now = a.block_tables(np.arange(B), maxb)
             return slots, tables, lens_now
 
@@ -287,15 +287,9 @@ class Workload:
             return a
 
         def step(a):
-            slots, pairs = [], []
-            for c in range(B):
-                s, pair = a.append(c, 1)
-                slots.append(s)
-                if pair:
-                    pairs.append(pair)
+            slots, pairs = a.append_batch(np.arange(B), np.ones(B, dtype=np.int32))
             tables, lens_now = a.block_tables(np.arange(B), maxb)
-            return np.concatenate(slots), np.array(pairs, dtype=np.int64).reshape(-1, 2), \
-                tables, lens_now
+            return slots, pairs.reshape(-1, 2), tables, lens_now
 
         _, (slots, pairs, tables, lens_now) = self._alloc_step(build, step)
         self.lens, self.tables, self.slots, self.nb = lens_now, tables, slots, nb
@@ -329,9 +323,11 @@ class Workload:
             return a
 
         def step(a):
-            slots = [a.append(b, chunk)[0] for b in writers] + [a.append(b, 1)[0] for b in dec]
+            ids = np.concatenate([writers, dec])
+            nt = np.concatenate([np.full(len(writers), chunk), np.ones(len(dec))]).astype(np.int32)
+            slots, _ = a.append_batch(ids, nt)
             tables, lens_now = a.block_tables(dec, maxb)
-            return np.concatenate(slots), tables, lens_now
+            return slots, tables, lens_now
 
         a, (slots, tables, lens_now) = self._alloc_step(build, step)
         self.lens, self.tables, self.slots, self.nb = lens_now, tables, slots, nb

@@ -260,6 +260,19 @@ pa_status pa_alloc_fork(pa_alloc* a, int64_t parent_id, int64_t child_id);
 pa_status pa_alloc_append(pa_alloc* a, int64_t seq_id, int32_t n_tokens, int64_t* slots_out,
                           int64_t* cow_pairs_out, int32_t* n_cow_out);
 
+/* One step for n sequences in a single call: pa_alloc_append(seq_ids[i],
+ * n_tokens[i]) for i = 0 .. n-1 in that order.  slots_out receives the slots
+ * of all sequences back to back (sum of n_tokens entries); cow_pairs_out
+ * receives the copy-on-write pairs, [*n_cow_out][2] in sequence order, room
+ * for n pairs (may be NULL only if no sequence writes into a shared tail
+ * block, else PA_EINVAL for that sequence).  Stops at the first sequence
+ * that fails and returns its status: the *n_done_out sequences before it were
+ * appended (their slots and pairs are written), it and those after it are
+ * untouched.  Host memory only. */
+pa_status pa_alloc_append_batch(pa_alloc* a, const int64_t* seq_ids, const int32_t* n_tokens,
+                                int32_t n, int64_t* slots_out, int64_t* cow_pairs_out,
+                                int32_t* n_cow_out, int32_t* n_done_out);
+
 /* Drop the sequence, from its last block to its first: each block loses one
  * reference; a block at 0 is reclaimed (a prefix-cache entry stays cached,
  * evictable, see below). */

@@ -51,6 +51,7 @@ def _load():
         "pa_alloc_add_seq": (i32, [vp, i64, i32]),
         "pa_alloc_fork": (i32, [vp, i64, i64]),
         "pa_alloc_append": (i32, [vp, i64, i32, vp, vp, vp]),
+        "pa_alloc_append_batch": (i32, [vp, vp, vp, i32, vp, vp, vp, vp]),
         "pa_alloc_free_seq": (i32, [vp, i64]),
         "pa_alloc_block_tables": (i32, [vp, vp, i32, i32, vp, vp]),
         "pa_alloc_num_free": (i64, [vp]),
@@ -77,7 +78,8 @@ _lib = _load()
 EXPORTED = ("pa_strerror", "pa_decode", "pa_decode_workspace_bytes", "pa_decode_partition_size",
             "pa_prefill", "pa_swap_blocks",
             "pa_reshape_and_cache", "pa_copy_blocks", "pa_alloc_create", "pa_alloc_destroy",
-            "pa_alloc_add_seq", "pa_alloc_fork", "pa_alloc_append", "pa_alloc_free_seq",
+            "pa_alloc_add_seq", "pa_alloc_fork", "pa_alloc_append", "pa_alloc_append_batch",
+            "pa_alloc_free_seq",
             "pa_alloc_block_tables", "pa_alloc_num_free", "pa_alloc_refcount",
             "pa_alloc_seq_len", "pa_alloc_seq_num_blocks", "pa_alloc_add_seq_tokens",
             "pa_alloc_append_tokens", "pa_alloc_num_cached", "pa_alloc_num_evictable",
@@ -329,6 +331,29 @@ class BlockAllocator:
                                     slots.ctypes.data_as(ctypes.c_void_p),
                                     pair.ctypes.data_as(ctypes.c_void_p), ctypes.byref(n)))
         return slots[:n_tokens], ((int(pair[0]), int(pair[1])) if n.value else None)
+
+    def append_batch(self, seq_ids, n_tokens):
+        """One step for many sequences in one call.  Returns (slots int64[sum
+        n_tokens], cow pairs int64[k][2]); on failure raises PAError (OutOfBlocks
+        for PA_ENOMEM) with .done = the number of sequences appended before
+        the failing one."""
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        nt = np.ascontiguousarray(n_tokens, dtype=np.int32)
+        if ids.shape != nt.shape or ids.ndim != 1:
+            raise ValueError("seq_ids and n_tokens must be 1-D and of one length")
+        slots = np.empty(max(int(nt.sum()), 1), dtype=np.int64)
+        pairs = np.empty((max(len(ids), 1), 2), dtype=np.int64)
+        ncow, done = ctypes.c_int32(0), ctypes.c_int32(0)
+        st = _lib.pa_alloc_append_batch(self._h, ids.ctypes.data_as(ctypes.c_void_p),
+                                        nt.ctypes.data_as(ctypes.c_void_p), len(ids),
+                                        slots.ctypes.data_as(ctypes.c_void_p),
+                                        pairs.ctypes.data_as(ctypes.c_void_p),
+                                        ctypes.byref(ncow), ctypes.byref(done))
+        if st != 0:
+            err = OutOfBlocks(st) if st == -3 else PAError(st)
+            err.done = done.value
+            raise err
+        return slots[:int(nt.sum())], pairs[:ncow.value]
 
     def free_seq(self, seq_id: int) -> None:
         _check(_lib.pa_alloc_free_seq(self._h, seq_id))

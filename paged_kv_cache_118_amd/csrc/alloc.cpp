@@ -317,6 +317,33 @@ pa_status pa_alloc_append(pa_alloc* a, int64_t seq_id, int32_t n_tokens, int64_t
   return st;
 }
 
+pa_status pa_alloc_append_batch(pa_alloc* a, const int64_t* seq_ids, const int32_t* n_tokens,
+                                int32_t n, int64_t* slots_out, int64_t* cow_pairs_out,
+                                int32_t* n_cow_out, int32_t* n_done_out) {
+  if (!a || n < 0 || (n > 0 && (!seq_ids || !n_tokens)) || !n_cow_out || !n_done_out)
+    return PA_EINVAL;
+  *n_cow_out = 0;
+  *n_done_out = 0;
+  int64_t total = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    if (n_tokens[i] < 0) return PA_EINVAL;
+    total += n_tokens[i];
+  }
+  if (total > 0 && !slots_out) return PA_EINVAL;
+  int64_t at = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    int32_t ncow = 0;
+    const pa_status st =
+        pa_alloc_append(a, seq_ids[i], n_tokens[i], n_tokens[i] > 0 ? slots_out + at : nullptr,
+                        cow_pairs_out ? cow_pairs_out + 2 * (int64_t)*n_cow_out : nullptr, &ncow);
+    if (st != PA_OK) return st;  // this sequence untouched (pa_alloc_append is all or nothing)
+    *n_cow_out += ncow;
+    at += n_tokens[i];
+    *n_done_out = i + 1;
+  }
+  return PA_OK;
+}
+
 pa_status pa_alloc_add_seq_tokens(pa_alloc* a, int64_t seq_id, const int32_t* tokens,
                                   int32_t num_tokens, uint64_t salt, int32_t* num_cached_out) {
   if (!a || num_tokens < 0 || (num_tokens > 0 && !tokens) || !num_cached_out) return PA_EINVAL;

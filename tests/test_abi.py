@@ -254,3 +254,73 @@ def test_alloc_matches_reference_on_random_ops():
             for b in row[row >= 0]:
                 holders[b] += 1
     assert all(a.refcount(b) == holders[b] for b in range(nb))
+
+
+def _batch_script(seed, nb=4000, bs=4):
+    """Two allocators with one seed driven by one random script of adds,
+    forks and frees; each step's appends go per sequence to one, as one
+    batch to the other."""
+    rng = np.random.default_rng(seed)
+    one, many = pa.BlockAllocator(nb, bs, shuffle_seed=5), pa.BlockAllocator(nb, bs, shuffle_seed=5)
+    live, nxt = [], 0
+    for step in range(60):
+        op = rng.integers(0, 4)
+        if op == 0 or not live:
+            n = int(rng.integers(1, 14))
+            for a in (one, many):
+                a.add_seq(nxt, n)
+            live.append(nxt)
+            nxt += 1
+        elif op == 1 and len(live) < 30:
+            src = live[int(rng.integers(0, len(live)))]
+            for a in (one, many):
+                a.fork(src, nxt)
+            live.append(nxt)
+            nxt += 1
+        elif op == 2 and len(live) > 3:
+            sid = live.pop(int(rng.integers(0, len(live))))
+            for a in (one, many):
+                a.free_seq(sid)
+        ids = [s for s in live if rng.random() < 0.7]
+        nt = [int(rng.integers(0, 6)) for _ in ids]
+        slots1, pairs1 = [], []
+        for s, n in zip(ids, nt):
+            sl, pr = one.append(s, n)
+            slots1.extend(int(x) for x in sl)
+            if pr:
+                pairs1.append(pr)
+        slots2, pairs2 = many.append_batch(ids, nt)
+        assert [int(x) for x in slots2] == slots1
+        assert [tuple(int(x) for x in p) for p in pairs2] == pairs1
+        t1, l1 = one.block_tables(live, 40)
+        t2, l2 = many.block_tables(live, 40)
+        assert np.array_equal(t1, t2) and np.array_equal(l1, l2)
+        assert one.num_free() == many.num_free()
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_alloc_append_batch_equals_per_sequence_appends(seed):
+    """pa_alloc_append_batch is the per-sequence appends in order: the same
+    slots, copy-on-write pairs (forked sequences writing into shared tails),
+    tables, lengths and free count."""
+    _batch_script(seed)
+
+
+def test_alloc_append_batch_stops_at_first_failure():
+    """Out of blocks at the third sequence: the first two are appended, the
+    third and fourth untouched, the error says how many were done."""
+    a = pa.BlockAllocator(6, 4)
+    for s in range(4):
+        a.add_seq(s, 4)  # one full block each; 2 blocks left
+    with pytest.raises(pa.OutOfBlocks) as e:
+        a.append_batch([0, 1, 2, 3], [1, 1, 1, 1])
+    assert e.value.done == 2
+    _, lens = a.block_tables([0, 1, 2, 3], 4)
+    assert list(lens) == [5, 5, 4, 4] and a.num_free() == 0
+    with pytest.raises(pa.PAError) as e:  # unknown sequence at index 1
+        a.append_batch([2, 99, 3], [0, 1, 0])
+    assert e.value.done == 1 and e.value.status == -6
+    with pytest.raises(pa.PAError):
+        a.append_batch([2], [-1])
+    s, p = a.append_batch([], [])
+    assert len(s) == 0 and len(p) == 0
