@@ -117,6 +117,9 @@ struct TableWindow {
 // skip the rescale altogether.
 constexpr float kSlack = 8.f;
 
+// Sequences up to which the workgroups take them longest context first.
+constexpr int kOrderSeqs = 64;
+
 // Longest query chunk from which the 32-rows-per-wavefront kernel is used.
 constexpr int kPrefill32MinRows = 64;
 
@@ -187,10 +190,36 @@ __global__ __launch_bounds__(64 * WV) void prefill_mfma_kernel(PrefillArgs a) {
   const int tpg = (a.max_query_len + kWaves * WR - 1) / (kWaves * WR);
   const int sub_n = G * tpg;  // workgroups per unit
   const int id = blockIdx.x;
-  const int unit = (id / 8 / sub_n) * 8 + id % 8;
+  const int unit = (id / 8 / sub_n) * 8 + id % 8;  // rank of the unit in dispatch order
   const int sub = (id / 8) % sub_n;
   if (unit >= a.num_seqs * a.num_kv_heads) return;
-  const int seq = unit / a.num_kv_heads;
+  int seq = unit / a.num_kv_heads;
+  // Longest contexts first (up to kOrderSeqs sequences): the workgroups are
+  // dispatched in id order as slots free up, so starting the long units
+  // first keeps one of them from setting the end of the kernel.  The rank of
+  // a sequence counts the longer ones (ties by index); every workgroup
+  // ranks the clamped lengths itself.
+  if (a.num_seqs <= kOrderSeqs) {
+    __shared__ int s_clen[kOrderSeqs];
+    __shared__ int s_order[kOrderSeqs];
+    const int B = a.num_seqs;
+    if (tid < B) {
+      const int Lt = a.context_lens[tid];
+      s_clen[tid] = Lt < 0 ? 0 : (Lt > a.len_cap ? a.len_cap : Lt);
+    }
+    __syncthreads();
+    if (tid < B) {
+      const int mine = s_clen[tid];
+      int rank = 0;
+      for (int j = 0; j < B; ++j) {
+        const int o = s_clen[j];
+        rank += o > mine || (o == mine && j < tid);
+      }
+      s_order[rank] = tid;
+    }
+    __syncthreads();
+    seq = s_order[seq];
+  }
   const int h = (unit % a.num_kv_heads) * G + sub / tpg;
   const int qs = a.query_start[seq];
   const int ql = a.query_start[seq + 1] - qs;
