@@ -127,19 +127,21 @@ constexpr int kPrefill32MinRows = 64;
 // NBG = physical blocks one 32-key group spans: 4 (block size 8), 2 (16),
 // 1 (a multiple of 32).
 //
-// The four wavefronts of a workgroup hold 64 consecutive query rows of one q
-// head and need the same keys, so each 32-key group's K and V are loaded from
-// the pool once per workgroup, by all 256 threads (16-byte loads, whole cache
-// lines), into LDS, and every wavefront reads its MFMA operands from there.
-// Two LDS buffers alternate: while the wavefronts compute group g from one,
-// the loads of group g + 1 are in flight in registers and are written to the
-// other buffer at the top of the next step; one barrier per group.
-//   K in LDS: 32 rows [key][D], pitch D*2 + 16 bytes (the 16 keys one
-//             operand read touches fall in distinct banks);
-//   V in LDS: 4 slabs of 8 keys, [slab][D][8], as in the pool.
+// The WV wavefronts of a workgroup hold WV * WR consecutive query rows of one
+// q head and need the same keys, so each 32-key group's K and V are loaded
+// from the pool once per workgroup, by all its threads, into LDS, and every
+// wavefront reads its MFMA operands from there; two LDS buffers alternate,
+// one barrier per group.  The loads take one of two routes:
+//  - DMA (32-row wavefronts): global_load_lds straight into LDS, one group
+//    ahead (layout at the kernel's LDS declarations);
+//  - registers (16-row wavefronts, or PA_PREFILL_DMA=0): 16-byte loads two
+//    groups ahead into registers, written to LDS at the top of the group's
+//    step.  K in LDS: 32 rows [key][D], pitch D*2 + 16 bytes (the 16 keys
+//    one operand read touches fall in distinct banks); V: 4 slabs of 8 keys,
+//    [slab][D][8], as in the pool, pitch D*16 + 16.
 // WR = query rows per wavefront: 16 (16x16x32 MFMAs) or 32 (32x32x16 MFMAs,
 // each K/V operand read from LDS then serves twice as many rows); WV =
-// wavefronts per workgroup.
+// wavefronts per workgroup; DMA = the load route.
 template <typename TT, int D, int NBG, int WR, int WV, bool DMA>
 __global__ __launch_bounds__(64 * WV) void prefill_mfma_kernel(PrefillArgs a) {
   constexpr int kWaves = WV;
