@@ -664,14 +664,13 @@ hipError_t launch_w(const PrefillArgs& a, hipStream_t s) {
 // bound; PA_PREFILL_ROWS / _WAVES / _DMA override them (tests, tuning).
 template <typename TT, int D, int NBG>
 hipError_t launch_g(const PrefillArgs& a, hipStream_t s) {
-  // 32-row wavefronts from 64-row chunks on.  Four of them per workgroup
-  // when chunks reach 128 rows and contexts 2048 tokens: each key group's
-  // LDS fill then serves twice the rows, which pays on long contexts (0.66
-  // against 0.59 PFLOP/s on 256-row chunks of 600-8300-token contexts), while
-  // on short contexts with ragged chunks two do better (the partly idle
-  // wavefronts of a 128-row workgroup cost more than the shared fills save).
+  // 32-row wavefronts from 64-row chunks on, four of them per workgroup
+  // from 128 rows on: each key group's LDS fill then serves twice the rows
+  // (with the direct loads this pays on long contexts, 256-row chunks of
+  // 600-8000 tokens, and on the ragged 1-512-row chunks of 513-1024-token
+  // prompts alike: 1.87 against 1.92 ms and 2.87 against 3.12 ms there).
   int wr = a.max_query_len >= kPrefill32MinRows ? 32 : 16;
-  int wv = wr == 16 || (a.max_query_len >= 4 * 32 && a.len_cap >= 2048) ? 4 : 2;
+  int wv = wr == 16 || a.max_query_len >= 4 * 32 ? 4 : 2;
   if (const char* e = std::getenv("PA_PREFILL_ROWS")) wr = atoi(e) == 32 ? 32 : atoi(e) == 16 ? 16 : wr;
   if (const char* e = std::getenv("PA_PREFILL_WAVES")) wv = atoi(e) == 2 ? 2 : 4;
   if (wr == 32) {
