@@ -375,6 +375,10 @@ class Workload:
             self.q.append(W.randn((B, sp.num_q_heads, sp.head_dim), sp.dtype, gen, dev))
         self.k_new, self.v_new = W.new_token_rows(T, sp.num_kv_heads, sp.head_dim, sp.dtype, gen,
                                                   dev)
+        # tokens written by prompt chunks before the decoding sequences' own
+        # (one each, in sequence order: what pa_decode_write takes)
+        self.n_chunk_tokens = T - B
+        assert self.n_chunk_tokens >= 0
         self.out = torch.empty_like(self.q[0])
         self.slots_dev = torch.from_numpy(self.slots).to(dev)
         self.tables_dev = torch.from_numpy(self.tables).to(dev)
@@ -445,6 +449,25 @@ class Workload:
                           partition_size=self.part, workspace=self.ws)
 
     def step(self, r):
+        """Copy-on-write copies (if any), then the decoding sequences' new
+        tokens written and attended in one pa_decode_write launch; a mixed
+        step's prompt-chunk tokens are written by pa_reshape_and_cache first."""
+        pa, sp = self.pa, self.spec
+        if self.pairs_dev is not None:
+            pa.pa_copy_blocks(self.k[r], self.v[r], self.pairs_dev, sp.block_size)
+        if self.n_chunk_tokens:
+            pa.pa_reshape_and_cache(self.k_new[:self.n_chunk_tokens],
+                                    self.v_new[:self.n_chunk_tokens], self.k[r], self.v[r],
+                                    self.slots_dev[:self.n_chunk_tokens], sp.block_size)
+        pa.pa_decode_write(self.out, self.q[r], self.k_new[self.n_chunk_tokens:],
+                           self.v_new[self.n_chunk_tokens:], self.k[r], self.v[r],
+                           self.tables_dev, self.lens_dev, sp.scale, sp.block_size,
+                           sp.num_kv_heads, self.max_ctx, partition_size=self.part,
+                           workspace=self.ws)
+
+    def step_separate(self, r):
+        """The same step with the write as its own launch (pa_reshape_and_cache
+        of every new token, then pa_decode): for comparison."""
         pa, sp = self.pa, self.spec
         if self.pairs_dev is not None:
             pa.pa_copy_blocks(self.k[r], self.v[r], self.pairs_dev, sp.block_size)
@@ -871,6 +894,16 @@ def main():
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
 
+    # the same step with the cache write as a launch of its own (comparison)
+    for i in range(args.warmup):
+        wl.step_separate(i % wl.replicas)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        wl.step_separate(i % wl.replicas)
+    torch.cuda.synchronize()
+    ms_step_sep = (time.perf_counter() - t0) * 1e3 / args.steps
+
     # timed region 2: K pa_decode calls back to back (the step's other calls
     # left out), bracketed by HIP events on the stream they run on: the mean
     # duration of one call (its decode and merge kernels) for the roofline
@@ -895,6 +928,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
+        "ms_per_step_separate_write": round(ms_step_sep, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -88,7 +88,9 @@ const char* pa_strerror(pa_status s);
  *  k_cache      K pool, layout above, num_blocks blocks (device)
  *  v_cache      V pool, layout above (device)
  *  block_tables [num_seqs][max_blocks_per_seq] int32 (device); entries past
- *               ceil(L / BS) are never read (padding is conventionally -1)
+ *               ceil(L / BS) are never used (the kernels may load them, within
+ *               the row's max_blocks_per_seq entries, as part of a 64-entry
+ *               window; padding is conventionally -1)
  *  context_lens [num_seqs] int32 (device).  Must satisfy
  *               L <= max_context_len and L <= max_blocks_per_seq * BS;
  *               positions beyond either bound are ignored.
@@ -126,6 +128,40 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
                     int32_t max_context_len, int64_t num_blocks, pa_dtype dtype,
                     int32_t partition_size, void* workspace, size_t workspace_bytes,
                     void* stream);
+
+/* ------------------------------------------------------------------------
+ * pa_decode_write -- one decode iteration's cache write and attention in a
+ * single launch: the write of each sequence's new token followed by
+ * attention over the context that includes it ([P5] section 三: the new
+ * token's K/V is stored into its slot before the iteration attends).
+ *
+ * For every sequence b with L = context_lens[b] >= 1, the token at position
+ * L - 1 has K row k_new[b*new_token_stride ...] and V row v_new[...] (each
+ * [num_kv_heads][head_dim] contiguous, dtype).  The call stores both rows
+ * into that position's slot, block_tables[b][(L-1)/BS] * BS + (L-1) % BS
+ * (bit for bit, as pa_reshape_and_cache with that slot would), and computes
+ * `out` exactly as pa_decode would over the pools after that store; the
+ * kernels read position L - 1 from the new rows themselves.  Sequences with
+ * L = 0 write nothing.  A table entry outside the pool skips the store (the
+ * row's result is then undefined, as for pa_decode).
+ *  k_new, v_new      device rows, 16-byte aligned; new_token_stride in
+ *                    elements, >= num_kv_heads * head_dim, a multiple of 16
+ *                    bytes.  Host pointers are PA_EINVAL before any launch.
+ *  other arguments   as pa_decode (same workspace size).
+ * Every new token's slot must belong to its sequence alone in this call: no
+ * two sequences write one slot, and no sequence reads another's new slot as
+ * one of its positions (a block about to be written is private, which the
+ * allocator's copy-on-write pairs, copied first, ensure).  PA_VALIDATE=1
+ * checks this too.
+ * ---------------------------------------------------------------------- */
+pa_status pa_decode_write(void* out, const void* q, const void* k_new, const void* v_new,
+                          int64_t new_token_stride, void* k_cache, void* v_cache,
+                          const int32_t* block_tables, const int32_t* context_lens, float scale,
+                          int32_t block_size, int32_t num_kv_heads, int32_t num_seqs,
+                          int32_t num_q_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                          int32_t max_context_len, int64_t num_blocks, pa_dtype dtype,
+                          int32_t partition_size, void* workspace, size_t workspace_bytes,
+                          void* stream);
 
 /* Workspace bytes pa_decode needs for these sizes (0 when nothing splits).
  * Pass the same arguments as to pa_decode, on the device it will run on (the
@@ -182,7 +218,9 @@ pa_status pa_prefill(void* out, const void* q, const void* k_cache, const void* 
  *  k, v          device token rows of dtype; strides in elements, >= Hkv*D
  *  slot_mapping  [num_tokens] int64 (device)
  * Requirements: head_dim * element size a multiple of 16 bytes; k, v and the
- * pools 16-byte aligned; strides a multiple of 16 bytes.
+ * pools 16-byte aligned; strides a multiple of 16 bytes.  k and v must be
+ * device memory (or pinned host memory mapped at the same address): any
+ * other pointer, e.g. pageable host memory, is PA_EINVAL before any launch.
  * ---------------------------------------------------------------------- */
 pa_status pa_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,
                                const int64_t* slot_mapping, int32_t num_tokens,
@@ -277,6 +315,14 @@ pa_status pa_alloc_append_batch(pa_alloc* a, const int64_t* seq_ids, const int32
  * reference; a block at 0 is reclaimed (a prefix-cache entry stays cached,
  * evictable, see below). */
 pa_status pa_alloc_free_seq(pa_alloc* a, int64_t seq_id);
+
+/* pa_alloc_free_seq for a sequence whose reserved slots were never written
+ * (e.g. its iteration was abandoned): every block it entered into the prefix
+ * table leaves the table first, so that no later request can reuse a block
+ * without its K/V, and then its blocks are released as by pa_alloc_free_seq
+ * (those entries' blocks go to the free list).  Entries the sequence reused
+ * from others are untouched. */
+pa_status pa_alloc_discard_seq(pa_alloc* a, int64_t seq_id);
 
 /* Host rows for pa_decode: tables_out [n][max_blocks] (padded with -1) and
  * lens_out [n].  PA_EINVAL if a sequence holds more than max_blocks blocks. */

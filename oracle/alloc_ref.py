@@ -138,6 +138,7 @@ class PrefixCachingPool(BlockPool):
         self.evictable: list[int] = []       # table entries at count 0, oldest first
         self.tokens: dict[int, list | None] = {}  # None: tokens unknown, not cached
         self.salt: dict[int, int] = {}
+        self.entered: dict[int, list] = {}   # seq -> blocks it entered into the table
 
     def key(self, salt: int, tokens, i: int) -> tuple:
         """Key of block i: the salt and every token up to the end of block i."""
@@ -167,10 +168,11 @@ class PrefixCachingPool(BlockPool):
             self.evictable.remove(b)
         self.ref[b] += 1
 
-    def _register(self, key: tuple, b: int) -> None:
+    def _register(self, key: tuple, b: int, seq: int) -> None:
         if key not in self.cached:
             self.cached[key] = b
             self.key_of[b] = key
+            self.entered.setdefault(seq, []).append(b)
 
     def add_seq(self, seq: int, n_tokens: int) -> None:
         super().add_seq(seq, n_tokens)
@@ -200,7 +202,7 @@ class PrefixCachingPool(BlockPool):
             b = self._take()
             table.append(b)
             if (i + 1) * bs <= n:
-                self._register(self.key(salt, tokens, i), b)
+                self._register(self.key(salt, tokens, i), b, seq)
         self.tables[seq] = table
         self.lens[seq] = n
         self.tokens[seq] = tokens
@@ -231,13 +233,23 @@ class PrefixCachingPool(BlockPool):
                 if (p + 1) % bs == 0:
                     i = p // bs
                     self._register(self.key(self.salt[seq], self.tokens[seq], i),
-                                   self.tables[seq][i])
+                                   self.tables[seq][i], seq)
         return slots, pairs
 
     def free_seq(self, seq: int) -> None:
         super().free_seq(seq)
         del self.tokens[seq]
         self.salt.pop(seq, None)
+        self.entered.pop(seq, None)
+
+    def discard_seq(self, seq: int) -> None:
+        """Release a sequence whose reserved slots never received their K / V:
+        the table entries it created are forgotten first (their blocks then
+        go to the free list), so no later request can reuse them."""
+        for b in self.entered.get(seq, []):
+            if b in self.key_of:
+                del self.cached[self.key_of.pop(b)]
+        self.free_seq(seq)
 
     def reset_cache(self) -> None:
         """Forget every table entry; evictable blocks become free (oldest

@@ -38,6 +38,8 @@ def _load():
         "pa_strerror": (ctypes.c_char_p, [i32]),
         "pa_decode": (i32, [vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, i32, i32, i32, i32, i64,
                             i32, i32, vp, sz, vp]),
+        "pa_decode_write": (i32, [vp, vp, vp, vp, i64, vp, vp, vp, vp, f32, i32, i32, i32, i32,
+                                  i32, i32, i32, i64, i32, i32, vp, sz, vp]),
         "pa_decode_workspace_bytes": (sz, [i32, i32, i32, i32, i32, i32, i32, i32]),
         "pa_decode_partition_size": (i32, [i32, i32, i32, i32, i32, i32, i32, i32]),
         "pa_prefill": (i32, [vp, vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, i32, i32, i32, i32,
@@ -53,6 +55,7 @@ def _load():
         "pa_alloc_append": (i32, [vp, i64, i32, vp, vp, vp]),
         "pa_alloc_append_batch": (i32, [vp, vp, vp, i32, vp, vp, vp, vp]),
         "pa_alloc_free_seq": (i32, [vp, i64]),
+        "pa_alloc_discard_seq": (i32, [vp, i64]),
         "pa_alloc_block_tables": (i32, [vp, vp, i32, i32, vp, vp]),
         "pa_alloc_num_free": (i64, [vp]),
         "pa_alloc_refcount": (i32, [vp, i64]),
@@ -75,11 +78,12 @@ def _load():
 _lib = _load()
 
 # every symbol include/pa.h declares (checked by the CPU test suite)
-EXPORTED = ("pa_strerror", "pa_decode", "pa_decode_workspace_bytes", "pa_decode_partition_size",
+EXPORTED = ("pa_strerror", "pa_decode", "pa_decode_write", "pa_decode_workspace_bytes",
+            "pa_decode_partition_size",
             "pa_prefill", "pa_swap_blocks",
             "pa_reshape_and_cache", "pa_copy_blocks", "pa_alloc_create", "pa_alloc_destroy",
             "pa_alloc_add_seq", "pa_alloc_fork", "pa_alloc_append", "pa_alloc_append_batch",
-            "pa_alloc_free_seq",
+            "pa_alloc_free_seq", "pa_alloc_discard_seq",
             "pa_alloc_block_tables", "pa_alloc_num_free", "pa_alloc_refcount",
             "pa_alloc_seq_len", "pa_alloc_seq_num_blocks", "pa_alloc_add_seq_tokens",
             "pa_alloc_append_tokens", "pa_alloc_num_cached", "pa_alloc_num_evictable",
@@ -125,6 +129,19 @@ def _stream(stream) -> ctypes.c_void_p:
     if isinstance(stream, torch.cuda.Stream):
         return ctypes.c_void_p(stream.cuda_stream)
     return ctypes.c_void_p(int(stream))
+
+
+def _scratch(nbytes: int, device, stream) -> torch.Tensor:
+    """A uint8 device buffer for one call's kernels on ``stream``: when that
+    is not the current stream, the caching allocator is told the buffer is in
+    use there until that stream's work is done."""
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if stream is not None:
+        ts = stream if isinstance(stream, torch.cuda.Stream) else \
+            torch.cuda.ExternalStream(int(stream), device=device)
+        if ts != torch.cuda.current_stream(device):
+            buf.record_stream(ts)
+    return buf
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -200,7 +217,7 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, block
     ws_bytes = int(_lib.pa_decode_workspace_bytes(B, hq, num_kv_heads, D, block_size,
                                                   max_context_len, partition_size, dt))
     if ws_bytes and workspace is None:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+        workspace = _scratch(ws_bytes, q.device, stream)
     ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(_lib.pa_decode(_dev_ptr(out, "out"), _dev_ptr(q, "q"), _dev_ptr(k_cache, "k_cache"),
@@ -208,6 +225,51 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, block
                           _dev_ptr(context_lens, "context_lens"), float(scale), block_size,
                           num_kv_heads, B, hq, D, block_tables.shape[1], int(max_context_len),
                           nb, dt, int(partition_size), ws_ptr, ws_len, _stream(stream)))
+    return out
+
+
+def pa_decode_write(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale,
+                    block_size, num_kv_heads, max_context_len, partition_size=0, workspace=None,
+                    stream=None):
+    """One decode iteration in one launch (see pa.h): sequence b's new token,
+    rows k_new[b] / v_new[b] ([num_seqs, Hkv, D]; the sequence dim may be
+    strided), is stored at position context_lens[b] - 1 of its table, and
+    ``out`` is pa_decode's result over the context including it."""
+    B, hq, D = q.shape
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q in shape and dtype")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("pools must have q's dtype")
+    nb = _check_pools(k_cache, v_cache, num_kv_heads, block_size, D)
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("block_tables and context_lens must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_tables must be [num_seqs, max_blocks], context_lens [num_seqs]")
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        if tuple(t.shape) != (B, num_kv_heads, D) or t.dtype != q.dtype:
+            raise ValueError(f"{name} must be [num_seqs, num_kv_heads, head_dim] of q's dtype")
+        if t.stride(2) != 1 or t.stride(1) != D:
+            raise ValueError(f"{name} rows must be [Hkv, D] contiguous per sequence")
+        if not t.is_cuda or t.device != q.device:
+            raise ValueError(f"{name} must be a device tensor on q's device")
+    if k_new.stride(0) != v_new.stride(0):
+        raise ValueError("k_new and v_new must have one sequence stride")
+    dt = _dtype_code(q)
+    ws_bytes = int(_lib.pa_decode_workspace_bytes(B, hq, num_kv_heads, D, block_size,
+                                                  max_context_len, partition_size, dt))
+    if ws_bytes and workspace is None:
+        workspace = _scratch(ws_bytes, q.device, stream)
+    ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_lib.pa_decode_write(_dev_ptr(out, "out"), _dev_ptr(q, "q"),
+                                ctypes.c_void_p(k_new.data_ptr()),
+                                ctypes.c_void_p(v_new.data_ptr()), k_new.stride(0),
+                                _dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"),
+                                _dev_ptr(block_tables, "block_tables"),
+                                _dev_ptr(context_lens, "context_lens"), float(scale), block_size,
+                                num_kv_heads, B, hq, D, block_tables.shape[1],
+                                int(max_context_len), nb, dt, int(partition_size), ws_ptr, ws_len,
+                                _stream(stream)))
     return out
 
 
@@ -251,6 +313,9 @@ def pa_reshape_and_cache(k, v, k_cache, v_cache, slot_mapping, block_size, strea
             raise ValueError(f"{name} rows must be [Hkv, D] contiguous per token")
     if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (T,):
         raise ValueError("slot_mapping must be int64 [num_tokens]")
+    for name, t in (("k", k), ("v", v)):
+        if not t.is_cuda or t.device != k_cache.device:
+            raise ValueError(f"{name} must be a device tensor on the pools' device")
     nb = _check_pools(k_cache, v_cache, hkv, block_size, D)
     _check(_lib.pa_reshape_and_cache(ctypes.c_void_p(k.data_ptr()),
                                      ctypes.c_void_p(v.data_ptr()),
@@ -357,6 +422,11 @@ class BlockAllocator:
 
     def free_seq(self, seq_id: int) -> None:
         _check(_lib.pa_alloc_free_seq(self._h, seq_id))
+
+    def discard_seq(self, seq_id: int) -> None:
+        """free_seq for a sequence whose slots were never written: the prefix
+        table entries it created are dropped first (pa_alloc_discard_seq)."""
+        _check(_lib.pa_alloc_discard_seq(self._h, seq_id))
 
     def block_tables(self, seq_ids, max_blocks: int):
         ids = np.ascontiguousarray(seq_ids, dtype=np.int64)

@@ -51,6 +51,7 @@ struct pa_alloc {
     bool has_last = false;
     Digest last{};               // digest of the last full block
     std::vector<int32_t> tail;   // tokens of the partially filled block
+    std::vector<int32_t> entered;  // blocks this sequence entered into the table
   };
   std::unordered_map<int64_t, Seq> seqs;
 
@@ -167,9 +168,11 @@ struct pa_alloc {
     ++ref[b];
   }
   // the block b has just become full with digest d: it enters the table
-  // unless that prefix already has an entry
-  void offer(int32_t b, const Digest& d) {
-    if (find(d) < 0) insert(b, d);
+  // unless that prefix already has an entry (returns whether it did)
+  bool offer(int32_t b, const Digest& d) {
+    if (find(d) >= 0) return false;
+    insert(b, d);
+    return true;
   }
   int64_t blocks_for(int64_t n) const { return (n + block_size - 1) / block_size; }
 };
@@ -294,6 +297,7 @@ pa_status pa_alloc_fork(pa_alloc* a, int64_t parent_id, int64_t child_id) {
   if (it == a->seqs.end() || a->seqs.count(child_id)) return PA_ENOENT;
   try {
     pa_alloc::Seq child = it->second;
+    child.entered.clear();  // entries belong to the sequence that created them
     if (child.tracked) child.tail.reserve((size_t)a->block_size);
     a->seqs.emplace(child_id, std::move(child));
   } catch (...) {
@@ -356,6 +360,7 @@ pa_status pa_alloc_add_seq_tokens(pa_alloc* a, int64_t seq_id, const int32_t* to
     a->scratch.resize((size_t)nfull);
     s.blocks.reserve((size_t)nblocks);
     s.tail.reserve((size_t)bs);
+    s.entered.reserve((size_t)nfull);
   } catch (...) {
     return PA_ENOMEM;
   }
@@ -387,7 +392,7 @@ pa_status pa_alloc_add_seq_tokens(pa_alloc* a, int64_t seq_id, const int32_t* to
   for (int64_t i = hits; i < nblocks; ++i) {
     const int32_t b = a->take();
     s.blocks.push_back(b);
-    if (i < nfull) a->offer(b, a->scratch[(size_t)i]);
+    if (i < nfull && a->offer(b, a->scratch[(size_t)i])) s.entered.push_back(b);
   }
   s.len = num_tokens;
   s.tracked = true;
@@ -418,7 +423,14 @@ pa_status pa_alloc_append_tokens(pa_alloc* a, int64_t seq_id, const int32_t* tok
       s.last = block_digest(s.has_last ? &s.last : nullptr, s.salt, s.tail.data(), bs);
       s.has_last = true;
       s.tail.clear();
-      a->offer(s.blocks[(size_t)((L + t) / bs)], s.last);
+      const int32_t b = s.blocks[(size_t)((L + t) / bs)];
+      if (a->offer(b, s.last)) {
+        try {
+          s.entered.push_back(b);
+        } catch (...) {  // cannot record it: keep the block out of the table instead
+          a->erase(b);
+        }
+      }
     }
   }
   return PA_OK;
@@ -432,6 +444,17 @@ pa_status pa_alloc_free_seq(pa_alloc* a, int64_t seq_id) {
   for (size_t i = blocks.size(); i-- > 0;) a->drop(blocks[i]);
   a->seqs.erase(it);
   return PA_OK;
+}
+
+pa_status pa_alloc_discard_seq(pa_alloc* a, int64_t seq_id) {
+  if (!a) return PA_EINVAL;
+  auto it = a->seqs.find(seq_id);
+  if (it == a->seqs.end()) return PA_ENOENT;
+  // the sequence still references every block it entered, so none of them
+  // can have been evicted and re-entered by another sequence meanwhile
+  for (int32_t b : it->second.entered)
+    if (a->cache_ready && a->is_entry[b]) a->erase(b);
+  return pa_alloc_free_seq(a, seq_id);
 }
 
 pa_status pa_alloc_block_tables(const pa_alloc* a, const int64_t* seq_ids, int32_t n,

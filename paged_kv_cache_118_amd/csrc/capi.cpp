@@ -21,17 +21,26 @@ constexpr int kPartGranule = 256;  // fixed chunks are a multiple of this many t
 constexpr int kMfmaMinGroup = 4;
 // The token-balanced split keeps per-sequence prefix sums in LDS.
 constexpr int kMaxSplitSeqs = 8192;
-// Workers per CU: the decode kernel's occupancy (one round of workers fills
-// the chip), capped for the VALU kernel at kValuWorkersPerCu, or the tuning
-// override PA_VALU_WAVES_PER_CU / PA_MFMA_WAVES_PER_CU.  Every worker
-// boundary inside an item costs one more fp32 partial written and merged, so
-// fewer, longer shares pay off once the CU is kept busy: 8 VALU workers per
-// CU measured about 1% faster than 16 on the OPT-13B-shaped workload.
+// Workers per CU: the decode kernel's occupancy with the launch's dynamic LDS
+// (one round of workers fills the chip), capped for the VALU kernel at
+// kValuWorkersPerCu.  Every worker boundary inside an item costs one more
+// fp32 partial written and merged, so fewer, longer shares pay off once the
+// CU is kept busy: 8 VALU workers per CU measured about 1% faster than 16 on
+// the OPT-13B-shaped workload.
 constexpr int kValuWorkersPerCu = 8;
+constexpr int kWavesPerWorkgroup = 4;  // both split kernels launch 4-wavefront workgroups
 
-int waves_per_cu(bool mfma, pa_dtype dt, int head_dim) {
-  const char* e = std::getenv(mfma ? "PA_MFMA_WAVES_PER_CU" : "PA_VALU_WAVES_PER_CU");
-  if (e && std::atoi(e) > 0 && std::atoi(e) <= 64) return std::atoi(e);
+int device_lds_per_cu() {
+  int dev = 0, v = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 64 * 1024;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
+          hipSuccess ||
+      v <= 0)
+    return 64 * 1024;
+  return v;
+}
+
+int waves_per_cu(bool mfma, pa_dtype dt, int head_dim, int num_seqs) {
   static int cache[2][3][5] = {};
   int dsel = head_dim == 64 ? 0 : head_dim == 128 ? 1 : head_dim == 256 ? 2 : 3;
   if (dsel > 2) dsel = 3;
@@ -39,7 +48,10 @@ int waves_per_cu(bool mfma, pa_dtype dt, int head_dim) {
   if (x == 0)
     x = mfma ? decode_mfma_waves_per_cu(dt, head_dim)
              : std::min(kValuWorkersPerCu, decode_valu_waves_per_cu(dt, head_dim));
-  return x;
+  // resident workgroups are also bounded by the LDS the split keeps per workgroup
+  static const int lds_cu = device_lds_per_cu();
+  const int by_lds = (int)(lds_cu / split_lds_bytes(num_seqs)) * kWavesPerWorkgroup;
+  return std::max(kWavesPerWorkgroup, std::min(x, by_lds));
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -113,7 +125,7 @@ Plan make_plan(int num_seqs, int hq, int hkv, int head_dim, int block_size, int 
     return p;
   }
   p.part_steps = partition_size > 0 ? std::max(1, partition_size / p.step) : 0;
-  p.num_workers = device_cus() * waves_per_cu(p.path == Path::kMfma, dt, head_dim);
+  p.num_workers = device_cus() * waves_per_cu(p.path == Path::kMfma, dt, head_dim, num_seqs);
   const size_t slots = (size_t)(items + p.num_workers);  // partial of item i by worker w: i + w
   p.pre_off = round_up(slots * part_record(p.rows_per_item, head_dim) * 4, 256);
   p.ppre_off = p.pre_off + round_up(((size_t)num_seqs + 1) * 4, 256);
@@ -143,6 +155,142 @@ bool copy_to_host(std::vector<T>& dst, const T* src, size_t n, hipStream_t s) {
   if (hipMemcpyAsync(dst.data(), src, n * sizeof(T), hipMemcpyDeviceToHost, s) != hipSuccess)
     return false;
   return hipStreamSynchronize(s) == hipSuccess;
+}
+
+}  // namespace
+
+namespace {
+
+// pa_decode and pa_decode_write: k_new / v_new null for a plain decode.
+pa_status decode_impl(void* out, const void* q, const void* k_new, const void* v_new,
+                      int64_t new_stride, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* context_lens, float scale,
+                      int32_t block_size, int32_t num_kv_heads, int32_t num_seqs,
+                      int32_t num_q_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                      int32_t max_context_len, int64_t num_blocks, pa_dtype dtype,
+                      int32_t partition_size, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      block_size <= 0 || max_blocks_per_seq < 0 || max_context_len < 0 || num_blocks <= 0)
+    return PA_EINVAL;
+  if (!dtype_ok(dtype)) return PA_ENOTSUP;
+  if (num_q_heads % num_kv_heads != 0) return PA_EINVAL;
+  if (!std::isfinite(scale)) return PA_EINVAL;
+  if (!(head_dim == 16 || head_dim == 32 || head_dim == 64 || head_dim == 128 || head_dim == 256))
+    return PA_ENOTSUP;
+  if (!block_size_ok(block_size)) return PA_ENOTSUP;
+  if (partition_size > 0 && partition_size % kPartGranule != 0) return PA_EINVAL;
+  const bool write = k_new != nullptr || v_new != nullptr;
+  if (write) {
+    const int es = elem_bytes(dtype);
+    if (!k_new || !v_new || new_stride < (int64_t)num_kv_heads * head_dim ||
+        (new_stride * es) % 16 != 0)
+      return PA_EINVAL;
+  }
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_EINVAL;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    return PA_EINVAL;
+  if (write) {
+    if (!aligned16(k_new) || !aligned16(v_new)) return PA_EINVAL;
+    // the new rows come straight from a caller's tensors: a host pointer
+    // would fault the kernel
+    if (!device_accessible(k_new) || !device_accessible(v_new)) return PA_EINVAL;
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+
+  const int64_t cap64 = std::min<int64_t>((int64_t)max_context_len,
+                                          (int64_t)max_blocks_per_seq * block_size);
+  const int len_cap = (int)cap64;
+  // the workspace size depends on max_context_len only (what the caller sized it with)
+  const Plan sized = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                               max_context_len, partition_size, dtype);
+  Plan p = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, len_cap,
+                     partition_size, dtype);
+
+  DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.scale_log2e = scale * 1.4426950408889634f;
+  a.block_size = block_size;
+  a.num_kv_heads = num_kv_heads;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.head_dim = head_dim;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.len_cap = len_cap;
+  a.num_blocks = num_blocks;
+  a.split = p.split;
+  a.part_steps = p.part_steps;
+  a.num_workers = p.num_workers;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.new_stride = new_stride;
+  a.fold_in_merge = p.path == Path::kMfma ? 1 : 0;
+  if (p.split) {
+    if (p.ws_bytes > sized.ws_bytes) return PA_EINVAL;  // cannot happen: len_cap <= max
+    if (!workspace || workspace_bytes < p.ws_bytes || !aligned16(workspace)) return PA_EINVAL;
+    char* base = static_cast<char*>(workspace);
+    a.ws_part = reinterpret_cast<float*>(base);
+    a.ws_pre = reinterpret_cast<int32_t*>(base + p.pre_off);
+    a.ws_ppre = reinterpret_cast<int32_t*>(base + p.ppre_off);
+  }
+
+  if (validate_enabled()) {
+    std::vector<int32_t> lens, tab;
+    if (!copy_to_host(lens, context_lens, (size_t)num_seqs, s)) return PA_EHIP;
+    if (!copy_to_host(tab, block_tables, (size_t)num_seqs * max_blocks_per_seq, s))
+      return PA_EHIP;
+    for (int b = 0; b < num_seqs; ++b) {
+      if (lens[b] < 0 || lens[b] > len_cap) return PA_EVALIDATE;
+      const int nb = (lens[b] + block_size - 1) / block_size;
+      for (int j = 0; j < nb; ++j) {
+        const int32_t e = tab[(size_t)b * max_blocks_per_seq + j];
+        if (e < 0 || e >= num_blocks) return PA_EVALIDATE;
+      }
+    }
+    if (write) {
+      // every new token's slot is its sequence's alone: no other sequence
+      // writes it or reads it as one of its positions in this call
+      std::unordered_set<int64_t> written;
+      for (int b = 0; b < num_seqs; ++b) {
+        if (lens[b] == 0) continue;
+        const int pos = lens[b] - 1;
+        const int64_t slot =
+            (int64_t)tab[(size_t)b * max_blocks_per_seq + pos / block_size] * block_size +
+            pos % block_size;
+        if (!written.insert(slot).second) return PA_EVALIDATE;
+      }
+      for (int b = 0; b < num_seqs; ++b)
+        for (int u = 0; u + 1 < lens[b]; ++u) {
+          const int64_t slot =
+              (int64_t)tab[(size_t)b * max_blocks_per_seq + u / block_size] * block_size +
+              u % block_size;
+          if (written.count(slot)) return PA_EVALIDATE;
+        }
+    }
+  }
+
+  hipError_t e = hipSuccess;
+  if (write && p.path != Path::kGeneric && !p.split) {
+    // an unsplit decode has no merge to fold the new token in: store the
+    // tokens first and decode the pools plainly
+    e = launch_store_new_tokens(a, dtype, s);
+    if (e != hipSuccess) return PA_EHIP;
+    a.k_new = a.v_new = nullptr;
+  }
+  switch (p.path) {
+    case Path::kMfma: e = launch_decode_mfma(a, dtype, s); break;
+    case Path::kValu: e = launch_decode_valu(a, dtype, s); break;
+    case Path::kGeneric: e = launch_decode_generic(a, dtype, s); break;
+  }
+  if (e != hipSuccess) return PA_EHIP;
+  if (p.split) e = launch_decode_merge(a, dtype, p.items_per_seq, s);
+  return hip_status(e);
 }
 
 }  // namespace
@@ -190,83 +338,25 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
                     int32_t max_context_len, int64_t num_blocks, pa_dtype dtype,
                     int32_t partition_size, void* workspace, size_t workspace_bytes,
                     void* stream) {
-  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
-      block_size <= 0 || max_blocks_per_seq < 0 || max_context_len < 0 || num_blocks <= 0)
-    return PA_EINVAL;
-  if (!dtype_ok(dtype)) return PA_ENOTSUP;
-  if (num_q_heads % num_kv_heads != 0) return PA_EINVAL;
-  if (!std::isfinite(scale)) return PA_EINVAL;
-  if (!(head_dim == 16 || head_dim == 32 || head_dim == 64 || head_dim == 128 || head_dim == 256))
-    return PA_ENOTSUP;
-  if (!block_size_ok(block_size)) return PA_ENOTSUP;
-  if (partition_size > 0 && partition_size % kPartGranule != 0) return PA_EINVAL;
-  if (num_seqs == 0) return PA_OK;
-  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_EINVAL;
-  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
-    return PA_EINVAL;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  return decode_impl(out, q, nullptr, nullptr, 0, k_cache, v_cache, block_tables, context_lens,
+                     scale, block_size, num_kv_heads, num_seqs, num_q_heads, head_dim,
+                     max_blocks_per_seq, max_context_len, num_blocks, dtype, partition_size,
+                     workspace, workspace_bytes, stream);
+}
 
-  const int64_t cap64 = std::min<int64_t>((int64_t)max_context_len,
-                                          (int64_t)max_blocks_per_seq * block_size);
-  const int len_cap = (int)cap64;
-  // the workspace size depends on max_context_len only (what the caller sized it with)
-  const Plan sized = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
-                               max_context_len, partition_size, dtype);
-  Plan p = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, len_cap,
-                     partition_size, dtype);
-
-  DecodeArgs a{};
-  a.out = out;
-  a.q = q;
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
-  a.block_tables = block_tables;
-  a.context_lens = context_lens;
-  a.scale_log2e = scale * 1.4426950408889634f;
-  a.block_size = block_size;
-  a.num_kv_heads = num_kv_heads;
-  a.num_seqs = num_seqs;
-  a.num_q_heads = num_q_heads;
-  a.head_dim = head_dim;
-  a.max_blocks_per_seq = max_blocks_per_seq;
-  a.len_cap = len_cap;
-  a.num_blocks = num_blocks;
-  a.split = p.split;
-  a.part_steps = p.part_steps;
-  a.num_workers = p.num_workers;
-  if (p.split) {
-    if (p.ws_bytes > sized.ws_bytes) return PA_EINVAL;  // cannot happen: len_cap <= max
-    if (!workspace || workspace_bytes < p.ws_bytes || !aligned16(workspace)) return PA_EINVAL;
-    char* base = static_cast<char*>(workspace);
-    a.ws_part = reinterpret_cast<float*>(base);
-    a.ws_pre = reinterpret_cast<int32_t*>(base + p.pre_off);
-    a.ws_ppre = reinterpret_cast<int32_t*>(base + p.ppre_off);
-  }
-
-  if (validate_enabled()) {
-    std::vector<int32_t> lens, tab;
-    if (!copy_to_host(lens, context_lens, (size_t)num_seqs, s)) return PA_EHIP;
-    if (!copy_to_host(tab, block_tables, (size_t)num_seqs * max_blocks_per_seq, s))
-      return PA_EHIP;
-    for (int b = 0; b < num_seqs; ++b) {
-      if (lens[b] < 0 || lens[b] > len_cap) return PA_EVALIDATE;
-      const int nb = (lens[b] + block_size - 1) / block_size;
-      for (int j = 0; j < nb; ++j) {
-        const int32_t e = tab[(size_t)b * max_blocks_per_seq + j];
-        if (e < 0 || e >= num_blocks) return PA_EVALIDATE;
-      }
-    }
-  }
-
-  hipError_t e = hipSuccess;
-  switch (p.path) {
-    case Path::kMfma: e = launch_decode_mfma(a, dtype, s); break;
-    case Path::kValu: e = launch_decode_valu(a, dtype, s); break;
-    case Path::kGeneric: e = launch_decode_generic(a, dtype, s); break;
-  }
-  if (e != hipSuccess) return PA_EHIP;
-  if (p.split) e = launch_decode_merge(a, dtype, p.items_per_seq, s);
-  return hip_status(e);
+pa_status pa_decode_write(void* out, const void* q, const void* k_new, const void* v_new,
+                          int64_t new_token_stride, void* k_cache, void* v_cache,
+                          const int32_t* block_tables, const int32_t* context_lens, float scale,
+                          int32_t block_size, int32_t num_kv_heads, int32_t num_seqs,
+                          int32_t num_q_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                          int32_t max_context_len, int64_t num_blocks, pa_dtype dtype,
+                          int32_t partition_size, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  if (!k_new || !v_new) return PA_EINVAL;
+  return decode_impl(out, q, k_new, v_new, new_token_stride, k_cache, v_cache, block_tables,
+                     context_lens, scale, block_size, num_kv_heads, num_seqs, num_q_heads,
+                     head_dim, max_blocks_per_seq, max_context_len, num_blocks, dtype,
+                     partition_size, workspace, workspace_bytes, stream);
 }
 
 pa_status pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -347,6 +437,9 @@ pa_status pa_reshape_and_cache(const void* k, const void* v, void* k_cache, void
   if ((k_token_stride * es) % 16 != 0 || (v_token_stride * es) % 16 != 0) return PA_EINVAL;
   if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache))
     return PA_EINVAL;
+  // the token rows often come straight from a caller's tensors: a host
+  // pointer here would fault the kernel
+  if (!device_accessible(k) || !device_accessible(v)) return PA_EINVAL;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (validate_enabled()) {
     std::vector<int64_t> slots;

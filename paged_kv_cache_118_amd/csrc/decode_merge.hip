@@ -10,6 +10,12 @@
 // and partition prefixes the decode kernel exported, the worker count, the
 // partition size), so nothing but the partials themselves has to be
 // communicated.  This kernel also writes the zero rows of empty sequences.
+//
+// For pa_decode_write it is also where the step's new token enters: the
+// decode kernel leaves the token out and writes partials only, and the merge
+// adds the token's own term and stores the token into its slot (the write
+// that precedes attention in wq-win.github.io "079 | vLLM 与 PagedAttention",
+// section 三; no kernel reads that slot before the merge runs).
 #include <math.h>
 
 #include "decode_split.h"
@@ -31,14 +37,15 @@ __device__ __forceinline__ void store_out(void* out, int64_t idx, float x) {
 // kBatch pieces back to back, then folds them in with one rescale.
 constexpr int kBatch = 16;
 
-// slot_of(k) = slot of the item's k-th piece, k < K.
+// slot_of(k) = slot of the item's k-th piece, k < K.  (m0, l0, o0) is a piece
+// already in hand (the new token's term, or nothing: -inf, 0, 0).
 template <typename SlotOf>
 __device__ __forceinline__ float merge_output(const DecodeArgs& a, SlotOf slot_of, int K, int R,
-                                              int r, int d) {
+                                              int r, int d, float m0, float l0, float o0) {
   const int D = a.head_dim;
   const int od = ((d >> 4) * 4 + ((d & 15) >> 2)) * R * 4 + r * 4 + (d & 3);  // within a record
   const int RS = part_record(R, D);
-  float M = -INFINITY, Lt = 0.f, acc = 0.f;
+  float M = m0, Lt = l0, acc = o0;
   for (int k0 = 0; k0 < K; k0 += kBatch) {
     float m[kBatch], l[kBatch], o[kBatch];
 #pragma unroll
@@ -66,32 +73,147 @@ __device__ __forceinline__ float merge_output(const DecodeArgs& a, SlotOf slot_o
   return acc / Lt;
 }
 
-// One workgroup per item (b, h), one thread per output (q row r, dim d).
 template <typename TT>
+__device__ __forceinline__ float elem(const void* base, int64_t i) {
+  if constexpr (TT::bytes == 4)
+    return reinterpret_cast<const float*>(base)[i];
+  else
+    return lo_to_float(TT{}, reinterpret_cast<const uint16_t*>(base)[i]);
+}
+
+// pa_decode_write: where sequence b's new token goes -- element d of kv head
+// g at position L - 1 -- as element indices into the K and V pools; -1 when
+// the table entry is not a block of the pool (nothing is stored then).
+struct NewSlot {
+  int64_t k, v;
+};
+__device__ __forceinline__ NewSlot new_slot(const DecodeArgs& a, int32_t blk, int g, int L,
+                                            int d, int elem_bytes) {
+  const int D = a.head_dim, bs = a.block_size, pos = L - 1;
+  if (blk < 0 || (int64_t)blk >= a.num_blocks) return {-1, -1};
+  const int off = pos % bs, vs = v_slab(bs);
+  const int64_t hkv = a.num_kv_heads;
+  return {k_elem_index(blk, g, off, d, hkv, bs, D, elem_bytes),
+          ((((int64_t)blk * hkv + g) * (bs / vs) + off / vs) * D + d) * vs + off % vs};
+}
+
+// One workgroup per item (b, h), one thread per output (q row r, dim d).
+// FOLD (pa_decode_write): the decode kernel covered positions 0 .. L-2 and
+// the new token at L - 1 enters here, one of two ways.  With a.fold_in_merge
+// (the grouped-query kernel) every segment left a partial and the merge adds
+// the token's own term -- score s = scale q . k_new, weight 2^(s - s) = 1,
+// value v_new; otherwise the decode kernel already added it, and only
+// sequences with no earlier position (L = 1: the row is v_new) need a row
+// here.  In both, the item that owns the kv head's first q row stores the
+// token into its slot.
+template <typename TT, bool FOLD>
 __global__ __launch_bounds__(1024) void decode_merge_kernel(DecodeArgs a, int H, int R) {
+  using E = typename TT::raw;
   const int D = a.head_dim, B = a.num_seqs;
   const int item = blockIdx.x;
   const int b = item / H, h = item - b * H;
   const int* pre = a.ws_pre;
-  const int n = (pre[b + 1] - pre[b]) / H;
   const int64_t orow0 = ((int64_t)b * a.num_q_heads + (int64_t)h * R) * D;
   const int total = R * D;
-  if (n == 0) {  // empty sequence: zero rows
+  // items are q heads (R = 1) or the G q heads of a kv head (R = G)
+  const int G = a.num_q_heads / a.num_kv_heads;
+  const int g = R == 1 ? h / G : h;
+  const int64_t nrow = (int64_t)b * a.new_stride + (int64_t)g * D;
+  // first round of loads, all independent: lengths and prefixes, and (FOLD)
+  // the thread's element of the new token's rows
+  const int n = (pre[b + 1] - pre[b]) / H;
+  const int L = FOLD ? clamp_len(a.context_lens[b], a.len_cap) : 0;
+  E kx = 0, vx = 0;
+  const int td = threadIdx.x < D ? threadIdx.x : 0;
+  if constexpr (FOLD) {
+    kx = reinterpret_cast<const E*>(a.k_new)[nrow + td];
+    vx = reinterpret_cast<const E*>(a.v_new)[nrow + td];
+  }
+  if (FOLD ? L == 0 : n == 0) {  // empty sequence: zero rows
     for (int t = threadIdx.x; t < total; t += blockDim.x) store_out<TT>(a.out, orow0 + t, 0.f);
     return;
   }
-  const Split sp = make_split(a.num_workers, pre[B], a.part_steps, H, B, pre, a.ws_ppre);
-  const int64_t S = pre[b] + (int64_t)h * n, E = S + n;
-  const int F = sp.worker_of(S), Lw = sp.worker_of(E - 1);
-  if (F == Lw) return;  // one piece: the decode kernel wrote the row
-  // one piece per worker F .. Lw, in slots item + F .. item + Lw
+  // second round: the new token's block, and the partials (below)
+  const bool stores = FOLD && (R > 1 || h % G == 0) && threadIdx.x < D;
+  const int32_t blk =
+      stores ? a.block_tables[(int64_t)b * a.max_blocks_per_seq + (L - 1) / a.block_size] : -1;
+  auto store_token = [&]() {
+    if (!stores) return;
+    const NewSlot ns = new_slot(a, blk, g, L, threadIdx.x, TT::bytes);
+    if (ns.k < 0) return;
+    // non-temporal: these scattered pieces of lines are not read again here
+    // (measured: the step's token stores 6 us cheaper than plain stores)
+    __builtin_nontemporal_store(kx, reinterpret_cast<E*>(const_cast<void*>(a.k_cache)) + ns.k);
+    __builtin_nontemporal_store(vx, reinterpret_cast<E*>(const_cast<void*>(a.v_cache)) + ns.v);
+  };
+  int F = 0, K = 0;  // the decode kernel's pieces: workers F .. F + K - 1
+  if (n > 0) {
+    const Split sp = make_split(a.num_workers, pre[B], a.part_steps, H, B, pre, a.ws_ppre);
+    const int64_t S = pre[b] + (int64_t)h * n, E2 = S + n;
+    F = sp.worker_of(S);
+    const int Lw = sp.worker_of(E2 - 1);
+    if ((!FOLD || !a.fold_in_merge) && F == Lw) {  // one piece: the decode kernel wrote the row
+      store_token();
+      return;
+    }
+    K = Lw - F + 1;
+  }
+  // one piece per worker F .. F + K - 1, in slots item + F ..
   const int base = item + F;
-  for (int t = threadIdx.x; t < total; t += blockDim.x) {
-    const int r = t / D, d = t - r * D;
-    store_out<TT>(a.out, orow0 + t,
-                  merge_output(a, [base](int k) { return base + k; }, Lw - F + 1, R, r, d));
+  auto slot_of = [base](int k) { return base + k; };
+  if (!FOLD || !a.fold_in_merge) {
+    // the pieces hold every position; a sequence of one (FOLD, n = 0) is
+    // its new token alone: weight 1, row v_new
+    const bool only_new = FOLD && n == 0;
+    for (int t = threadIdx.x; t < total; t += blockDim.x) {
+      const int r = t / D, d = t - r * D;
+      store_out<TT>(a.out, orow0 + t,
+                    merge_output(a, slot_of, K, R, r, d, only_new ? 0.f : -INFINITY,
+                                 only_new ? 1.f : 0.f,
+                                 only_new ? elem<TT>(a.v_new, nrow + d) : 0.f));
+    }
+  } else {
+    __shared__ float s_new[16];  // the new token's score per q row (base-2 domain)
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    for (int r = wv; r < R; r += nw) {
+      float p = 0.f;
+      for (int d = lane; d < D; d += 64)
+        p = fmaf(elem<TT>(a.q, orow0 + (int64_t)r * D + d), elem<TT>(a.k_new, nrow + d), p);
+      for (int m = 1; m < 64; m <<= 1) p += __shfl_xor(p, m);
+      if (lane == 0) s_new[r] = p * a.scale_log2e;
+    }
+    __syncthreads();
+    for (int t = threadIdx.x; t < total; t += blockDim.x) {
+      const int r = t / D, d = t - r * D;
+      store_out<TT>(a.out, orow0 + t,
+                    merge_output(a, slot_of, K, R, r, d, s_new[r], 1.f,
+                                 elem<TT>(a.v_new, nrow + d)));
+    }
+  }
+  store_token();
+}
+
+// The store alone, for a pa_decode_write whose decode runs unsplit (the
+// plain kernel then reads the token from the pool): one workgroup per
+// (sequence, kv head), one thread per element.
+template <typename TT>
+__global__ __launch_bounds__(256) void store_new_tokens_kernel(DecodeArgs a) {
+  using E = typename TT::raw;
+  const int b = blockIdx.y, g = blockIdx.x;
+  const int L = clamp_len(a.context_lens[b], a.len_cap);
+  if (L == 0) return;
+  const int32_t blk = a.block_tables[(int64_t)b * a.max_blocks_per_seq + (L - 1) / a.block_size];
+  const int64_t nrow = (int64_t)b * a.new_stride + (int64_t)g * a.head_dim;
+  for (int d = threadIdx.x; d < a.head_dim; d += blockDim.x) {
+    const NewSlot ns = new_slot(a, blk, g, L, d, TT::bytes);
+    if (ns.k < 0) return;
+    __builtin_nontemporal_store(reinterpret_cast<const E*>(a.k_new)[nrow + d],
+                                reinterpret_cast<E*>(const_cast<void*>(a.k_cache)) + ns.k);
+    __builtin_nontemporal_store(reinterpret_cast<const E*>(a.v_new)[nrow + d],
+                                reinterpret_cast<E*>(const_cast<void*>(a.v_cache)) + ns.v);
   }
 }
+
 
 }  // namespace
 
@@ -102,18 +224,48 @@ hipError_t launch_decode_merge(const DecodeArgs& a, pa_dtype dt, int items_per_s
   const int outputs = R * a.head_dim;
   const int threads = outputs >= 1024 ? 1024 : (outputs + 63) / 64 * 64;
   dim3 grid(a.num_seqs * items_per_seq);
+  const bool fold = a.k_new != nullptr;
   switch (dt) {
     case PA_F32:
-      hipLaunchKernelGGL(decode_merge_kernel<F32>, grid, dim3(threads), 0, s, a, items_per_seq,
-                         R);
+      if (fold)
+        hipLaunchKernelGGL((decode_merge_kernel<F32, true>), grid, dim3(threads), 0, s, a,
+                           items_per_seq, R);
+      else
+        hipLaunchKernelGGL((decode_merge_kernel<F32, false>), grid, dim3(threads), 0, s, a,
+                           items_per_seq, R);
       break;
     case PA_F16:
-      hipLaunchKernelGGL(decode_merge_kernel<F16>, grid, dim3(threads), 0, s, a, items_per_seq,
-                         R);
+      if (fold)
+        hipLaunchKernelGGL((decode_merge_kernel<F16, true>), grid, dim3(threads), 0, s, a,
+                           items_per_seq, R);
+      else
+        hipLaunchKernelGGL((decode_merge_kernel<F16, false>), grid, dim3(threads), 0, s, a,
+                           items_per_seq, R);
       break;
     case PA_BF16:
-      hipLaunchKernelGGL(decode_merge_kernel<BF16>, grid, dim3(threads), 0, s, a, items_per_seq,
-                         R);
+      if (fold)
+        hipLaunchKernelGGL((decode_merge_kernel<BF16, true>), grid, dim3(threads), 0, s, a,
+                           items_per_seq, R);
+      else
+        hipLaunchKernelGGL((decode_merge_kernel<BF16, false>), grid, dim3(threads), 0, s, a,
+                           items_per_seq, R);
+      break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_store_new_tokens(const DecodeArgs& a, pa_dtype dt, hipStream_t s) {
+  if (a.num_seqs == 0 || !a.k_new) return hipSuccess;
+  dim3 grid(a.num_kv_heads, a.num_seqs);
+  switch (dt) {
+    case PA_F32:
+      hipLaunchKernelGGL(store_new_tokens_kernel<F32>, grid, dim3(128), 0, s, a);
+      break;
+    case PA_F16:
+      hipLaunchKernelGGL(store_new_tokens_kernel<F16>, grid, dim3(128), 0, s, a);
+      break;
+    case PA_BF16:
+      hipLaunchKernelGGL(store_new_tokens_kernel<BF16>, grid, dim3(128), 0, s, a);
       break;
   }
   return hipGetLastError();

@@ -28,7 +28,6 @@
 //                  softmax rescale of the accumulators is lane-local.
 // The max / sum over the 4 k-groups of a head cross lanes (xor 16, 32).
 #include <math.h>
-#include <stdlib.h>
 
 #include "decode_split.h"
 #include "pa_internal.h"
@@ -90,10 +89,12 @@ struct TableWindow {
   }
 };
 
-// SCHED 0: two-phase pipeline (K and V of a group issued one phase apart).
-// SCHED 1: single phase (K and V of group j+1 issued before group j computes).
-template <typename TT, int D, int SCHED, int OCC>
-__global__ __launch_bounds__(kThreads, OCC) void decode_mfma_kernel(DecodeArgs a) {
+// FOLD (pa_decode_write): each sequence's last position, the new token, is
+// left out here -- the stream covers positions 0 .. L-2 -- and every segment
+// is written as a partial, which the merge kernel combines with the new
+// token's own term (fold_in_merge).
+template <typename TT, int D, bool FOLD>
+__global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int VS = 8;       // V slab width (tokens)
   constexpr int EB = 2;
   constexpr int KN = D / 32;  // uint4 per lane per K tile (= QK k-steps)
@@ -119,7 +120,8 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_mfma_kernel(DecodeArgs a
   int64_t x0 = 0;  // split 1: first stream step of this worker
   if (a.split) {
     if (wv == 0)
-      wave_scan_steps(a.context_lens, B, H, a.len_cap, kGroup, C, s_pre, s_len, s_ppre);
+      wave_scan_steps(a.context_lens, B, H, a.len_cap, FOLD ? 1 : 0, kGroup, C, s_pre, s_len,
+                      s_ppre);
     __syncthreads();
     if (blockIdx.x == 0 && wv == 0) export_prefixes(s_pre, s_ppre, B, C, a.ws_pre, a.ws_ppre);
     const int N = s_pre[B];  // empty sequences get their zero rows from the merge
@@ -273,13 +275,9 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_mfma_kernel(DecodeArgs a
     mx = xor32_max(mx);
     const float m_new = fmaxf(m_run, mx);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    float pw[8], psum = 0.f;
+    float pw[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      pw[e] = __builtin_amdgcn_exp2f(sc[e] - m_new);
-      psum += pw[e];
-    }
-    l_lane = l_lane * alpha + psum;
+    for (int e = 0; e < 8; ++e) pw[e] = __builtin_amdgcn_exp2f(sc[e] - m_new);
     m_run = m_new;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[mt] *= alpha;
@@ -290,6 +288,9 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_mfma_kernel(DecodeArgs a
     // to a source offering the tile it needs.
     const uint32_t t0a = pack2(TT{}, pw[0], pw[1]), t0b = pack2(TT{}, pw[2], pw[3]);
     const uint32_t t1a = pack2(TT{}, pw[4], pw[5]), t1b = pack2(TT{}, pw[6], pw[7]);
+    // the row sum takes the same rounded weights the P^T operand carries
+    // (every token's pair sits in exactly one lane before the permutes)
+    l_lane = psum2(TT{}, t1b, psum2(TT{}, t1a, psum2(TT{}, t0b, psum2(TT{}, t0a, l_lane * alpha))));
     const bool ev = (kb & 1) == 0;
     const int p1 = ((kb & 1) << 1) | (kb >> 1);
     const int src1 = (n + 16 * p1) * 4, src2 = (n + 16 * (p1 ^ 1)) * 4;
@@ -325,7 +326,7 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_mfma_kernel(DecodeArgs a
       float l_tot = l_lane + __shfl_xor(l_lane, 16);
       l_tot += __shfl_xor(l_tot, 32);
       const int64_t orow0 = (int64_t)cu.b * a.num_q_heads + (int64_t)cu.h * G;
-      if (seg_k0 == 0 && cu.k == cu.n - 1) {  // the whole item: final rows
+      if (!FOLD && seg_k0 == 0 && cu.k == cu.n - 1) {  // the whole item: final rows
         if (n < G) {
           const int64_t orow = (orow0 + n) * D;
           const float inv = 1.f / l_tot;
@@ -357,118 +358,62 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_mfma_kernel(DecodeArgs a
       uniform(c);
     }
   };
-  if constexpr (SCHED == 0) {
-    // Pipeline, per group j: qk(j) | issue V(j+1) | pv(j) | issue K(j+2).
-    // Each load is issued a full group ahead of its use, yet only three of
-    // the four K/V register sets are live at any time.  Issues past the
-    // worker's last group read cached bytes instead, keeping the waits static.
-    uint4 kA[2][KN], kB[2][KN], vA[MT], vB[MT], qA[KN], qB[KN];
-    int qia = -1, qib = -1;
-    Cursor c1 = c0;
-    next(c1, 1);
-    issue_k(c0, kA, qA, qia, true);
-    issue_v(c0, vA, true);
-    issue_k(c1, kB, qB, qib, 1 < count);
-    int j = 0;
-    for (;;) {
-      Cursor c2 = c1;
-      next(c2, j + 2);
-      {
-        uint4 pb;
-        int nv;
-        qk(c0, kA, qA, j, pb, nv);
-        issue_v(c1, vB, j + 1 < count);
-        pv(c0, vA, pb, nv, j);
-        issue_k(c2, kA, qA, qia, j + 2 < count);
-      }
-      if (++j >= count) break;
-      c0 = c1;
-      c1 = c2;
-      c2 = c1;
-      next(c2, j + 2);
-      {
-        uint4 pb;
-        int nv;
-        qk(c0, kB, qB, j, pb, nv);
-        issue_v(c1, vA, j + 1 < count);
-        pv(c0, vB, pb, nv, j);
-        issue_k(c2, kB, qB, qib, j + 2 < count);
-      }
-      if (++j >= count) break;
-      c0 = c1;
-      c1 = c2;
-    }
-  } else {
-    // Single phase: K and V of group j+1 are issued together before group j
-    // computes.
-    uint4 kA[2][KN], kB[2][KN], vA[MT], vB[MT], qA[KN], qB[KN];
-    int qia = -1, qib = -1;
-    Cursor c1 = c0;
-    next(c1, 1);
-    issue_k(c0, kA, qA, qia, true);
-    issue_v(c0, vA, true);
-    int j = 0;
-    for (;;) {
-      issue_k(c1, kB, qB, qib, j + 1 < count);
+  // Pipeline, per group j: qk(j) | issue V(j+1) | pv(j) | issue K(j+2).
+  // Each load is issued a full group ahead of its use, yet only three of
+  // the four K/V register sets are live at any time.  Issues past the
+  // worker's last group read cached bytes instead, keeping the waits static.
+  uint4 kA[2][KN], kB[2][KN], vA[MT], vB[MT], qA[KN], qB[KN];
+  int qia = -1, qib = -1;
+  Cursor c1 = c0;
+  next(c1, 1);
+  issue_k(c0, kA, qA, qia, true);
+  issue_v(c0, vA, true);
+  issue_k(c1, kB, qB, qib, 1 < count);
+  int j = 0;
+  for (;;) {
+    Cursor c2 = c1;
+    next(c2, j + 2);
+    {
+      uint4 pb;
+      int nv;
+      qk(c0, kA, qA, j, pb, nv);
       issue_v(c1, vB, j + 1 < count);
-      {
-        uint4 pb;
-        int nv;
-        qk(c0, kA, qA, j, pb, nv);
-        pv(c0, vA, pb, nv, j);
-      }
-      if (++j >= count) break;
-      c0 = c1;
-      next(c1, j + 1);
-      issue_k(c1, kA, qA, qia, j + 1 < count);
-      issue_v(c1, vA, j + 1 < count);
-      {
-        uint4 pb;
-        int nv;
-        qk(c0, kB, qB, j, pb, nv);
-        pv(c0, vB, pb, nv, j);
-      }
-      if (++j >= count) break;
-      c0 = c1;
-      next(c1, j + 1);
+      pv(c0, vA, pb, nv, j);
+      issue_k(c2, kA, qA, qia, j + 2 < count);
     }
+    if (++j >= count) break;
+    c0 = c1;
+    c1 = c2;
+    c2 = c1;
+    next(c2, j + 2);
+    {
+      uint4 pb;
+      int nv;
+      qk(c0, kB, qB, j, pb, nv);
+      issue_v(c1, vA, j + 1 < count);
+      pv(c0, vB, pb, nv, j);
+      issue_k(c2, kB, qB, qib, j + 2 < count);
+    }
+    if (++j >= count) break;
+    c0 = c1;
+    c1 = c2;
   }
-}
-
-// Schedule variant (tuning): PA_MFMA_SCHED = 0 two-phase (default),
-// 1 single-phase, 2 two-phase built for 3 waves per SIMD.
-int mfma_sched() {
-  static int v = -1;
-  if (v < 0) {
-    const char* e = std::getenv("PA_MFMA_SCHED");
-    v = (e && e[0] >= '0' && e[0] <= '2') ? e[0] - '0' : 0;
-  }
-  return v;
 }
 
 template <typename TT, int D>
 const void* mfma_fn() {
-  switch (mfma_sched()) {
-    case 1: return reinterpret_cast<const void*>(&decode_mfma_kernel<TT, D, 1, 2>);
-    case 2: return reinterpret_cast<const void*>(&decode_mfma_kernel<TT, D, 0, 3>);
-  }
-  return reinterpret_cast<const void*>(&decode_mfma_kernel<TT, D, 0, 2>);
+  return reinterpret_cast<const void*>(&decode_mfma_kernel<TT, D, false>);
 }
 
 template <typename TT, int D>
 hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
   dim3 grid((a.num_workers + kWaves - 1) / kWaves);
-  const size_t lds = a.split ? sizeof(int) * (3 * (size_t)a.num_seqs + 2) : 0;
-  switch (mfma_sched()) {
-    case 1:
-      hipLaunchKernelGGL((decode_mfma_kernel<TT, D, 1, 2>), grid, dim3(kThreads), lds, s, a);
-      break;
-    case 2:
-      hipLaunchKernelGGL((decode_mfma_kernel<TT, D, 0, 3>), grid, dim3(kThreads), lds, s, a);
-      break;
-    default:
-      hipLaunchKernelGGL((decode_mfma_kernel<TT, D, 0, 2>), grid, dim3(kThreads), lds, s, a);
-  }
+  if (a.k_new)
+    hipLaunchKernelGGL((decode_mfma_kernel<TT, D, true>), grid, dim3(kThreads),
+                       decode_split_lds(a), s, a);
+  else
+    hipLaunchKernelGGL((decode_mfma_kernel<TT, D, false>), grid, dim3(kThreads),
+                       decode_split_lds(a), s, a);
   return hipGetLastError();
 }
 

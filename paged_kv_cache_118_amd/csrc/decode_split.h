@@ -38,20 +38,26 @@ __device__ __forceinline__ int clamp_len(int L, int cap) { return L < 0 ? 0 : (L
 // encoding).
 constexpr int kVmcntZero = 0x0F70;
 
+// Dynamic LDS a decode launch with these arguments needs.
+inline size_t decode_split_lds(const DecodeArgs& a) {
+  return a.split ? split_lds_bytes(a.num_seqs) : 0;
+}
+
 // Exclusive prefixes over sequences of H * n_b (LDS s_pre[0..B]) and, when
-// C > 0, of H * ceil(n_b / C) (s_ppre[0..B]), plus the clamped lengths
-// (s_len[0..B-1]), computed by ONE wavefront: lane i handles a contiguous run
-// of sequences, then a shuffle scan across lanes.  The caller publishes the
-// arrays to the other wavefronts with a barrier.  Returns N = s_pre[B] (in
-// every lane).
-__device__ inline int wave_scan_steps(const int32_t* lens, int B, int H, int cap, int step, int C,
-                                      int* s_pre, int* s_len, int* s_ppre) {
+// C > 0, of H * ceil(n_b / C) (s_ppre[0..B]), plus the clamped lengths less
+// `drop` trailing positions (s_len[0..B-1]; drop = 1 leaves out the new token
+// that the merge folds in), computed by ONE wavefront: lane i handles a
+// contiguous run of sequences, then a shuffle scan across lanes.  The caller
+// publishes the arrays to the other wavefronts with a barrier.  Returns
+// N = s_pre[B] (in every lane).
+__device__ inline int wave_scan_steps(const int32_t* lens, int B, int H, int cap, int drop,
+                                      int step, int C, int* s_pre, int* s_len, int* s_ppre) {
   const int lane = threadIdx.x & 63;
   const int per = (B + 63) / 64;
   const int j0 = min(lane * per, B), j1 = min(j0 + per, B);
   int local = 0, plocal = 0;
   for (int j = j0; j < j1; ++j) {
-    const int L = clamp_len(lens[j], cap);
+    const int L = max(clamp_len(lens[j], cap) - drop, 0);
     s_len[j] = L;
     const int n = (L + step - 1) / step;
     local += H * n;

@@ -156,6 +156,15 @@ __device__ __forceinline__ void store_out(void* out, int64_t idx, float x) {
     reinterpret_cast<uint16_t*>(out)[idx] = to_bits(TT{}, x);
 }
 
+// One element of a token row, widened.
+template <typename TT>
+__device__ __forceinline__ float new_elem(const char* p) {
+  if constexpr (TT::bytes == 4)
+    return *reinterpret_cast<const float*>(p);
+  else
+    return lo_to_float(TT{}, *reinterpret_cast<const uint16_t*>(p));
+}
+
 // Block-table window: lane i holds the physical id of logical block base + i
 // (0 past the table row, and for ids outside the pool -- padding included --
 // so that no entry ever produces an out-of-range address; such blocks only
@@ -180,7 +189,13 @@ struct TableWindow {
   }
 };
 
-template <typename TT, int D, int NB>
+// FOLD (pa_decode_write): each sequence's last position, the new token, is
+// left out of the stream -- it covers positions 0 .. L-2 -- and the worker
+// that finishes an item adds the token's term from its K / V rows at that
+// segment's end (one more online-softmax step of a single key), so a whole
+// item still ends as its final row and a split one as partials that already
+// hold the token.  The merge kernel stores the token into its slot.
+template <typename TT, int D, int NB, bool FOLD>
 __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
   constexpr int EB = TT::bytes;
   constexpr int NK = D * EB / 64;  // uint4 per lane per step, K and V alike
@@ -207,7 +222,9 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
   Split sp{};
   int64_t x0 = 0;  // split 1: first stream step of this worker
   if (a.split) {
-    if (wv == 0) wave_scan_steps(a.context_lens, B, H, a.len_cap, kStep, C, s_pre, s_len, s_ppre);
+    if (wv == 0)
+      wave_scan_steps(a.context_lens, B, H, a.len_cap, FOLD ? 1 : 0, kStep, C, s_pre, s_len,
+                      s_ppre);
     __syncthreads();
     if (blockIdx.x == 0 && wv == 0) export_prefixes(s_pre, s_ppre, B, C, a.ws_pre, a.ws_ppre);
     const int N = s_pre[B];  // empty sequences get their zero rows from the merge
@@ -262,9 +279,25 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
   // in cache (token 0 of the same instruction, or the item's q row), so they
   // cost no HBM traffic while the number of loads, and so every wait count,
   // stays fixed.
+  // FOLD: an item's last step also prefetches the new token's K pieces
+  // c + 4i (kn) and V elements of rows lane + 64 r (vn), for the fold at the
+  // end of that step; other steps load the same count from the item's q row
+  // (in cache), so that the wait counts stay static.
   auto issue = [&](const Cursor& cu, uint4 (&kr)[NK], uint4 (&vr)[NK], uint4 (&qr)[NK],
-                   int& qitem, bool live) {
+                   int& qitem, bool live, uint4 (&kn)[NK], float (&vn)[R]) {
     const int item = cu.item(H);
+    if constexpr (FOLD) {
+      const bool want = live && cu.k == cu.n - 1;
+      const int64_t row = (int64_t)cu.b * a.new_stride + (int64_t)(cu.h / group) * D;
+      const char* kp = want ? reinterpret_cast<const char*>(a.k_new) + row * EB + c * 16
+                            : qbase + (int64_t)item * D * EB + c * 16;
+      const char* vp = want ? reinterpret_cast<const char*>(a.v_new) + row * EB
+                            : qbase + (int64_t)item * D * EB;
+#pragma unroll
+      for (int i = 0; i < NK; ++i) kn[i] = ld16(kp + 64 * i);
+#pragma unroll
+      for (int r = 0; r < R; ++r) vn[r] = new_elem<TT>(vp + (lane + 64 * r) * EB);
+    }
     if (qitem != item) {
       qitem = item;
       const char* qp = qbase + (int64_t)item * D * EB + c * 16;
@@ -319,7 +352,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
   int seg_k0 = c0.k;  // first step of the current segment within its item
 
   auto compute = [&](const Cursor& cu, const uint4 (&kr)[NK], uint4 (&vr)[NK],
-                     const uint4 (&qr)[NK], int j) {
+                     const uint4 (&qr)[NK], int j, const uint4 (&kn)[NK], const float (&vn)[R]) {
     if (segment_starts(cu, j)) {
       m_run = -INFINITY;
       l_lane = 0.f;
@@ -351,6 +384,21 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
     lane_pv<TT, R, NK>(acc, pt, vr);
 
     if (segment_ends(cu, j, count - 1)) {
+      if (FOLD && cu.k == cu.n - 1) {
+        // the new token: score q . k_new (the quad's lanes hold q's pieces
+        // c + 4i; so do their loads of k_new), weight, V row elements
+        float sn = lane_dot(TT{}, qr, kn);
+        sn += dpp<0xB1>(sn);
+        sn += dpp<0x4E>(sn);
+        sn *= a.scale_log2e;
+        const float mn = fmaxf(m_run, sn);
+        const float al = __builtin_amdgcn_exp2f(m_run - mn);
+        const float pn = __builtin_amdgcn_exp2f(sn - mn);
+        l_lane = l_lane * al + (lane == 0 ? pn : 0.f);
+        m_run = mn;
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r] = fmaf(pn, vn[r], acc[r] * al);
+      }
       const float l_tot = wave_sum(l_lane);
       const int item = cu.item(H);
       if (seg_k0 == 0 && cu.k == cu.n - 1) {  // the whole item: final row
@@ -375,6 +423,8 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
   // the compiler's wait counts never hold a load of the next batch.  Issues
   // past the worker's last step read cached bytes (see `issue`).
   uint4 kr[NB][NK], vr[NB][NK], qr[NB][NK];
+  uint4 kn[NB][NK];  // FOLD: the new token's rows, prefetched with its item's last step
+  float vn[NB][R];
   int qi[NB];
 #pragma unroll
   for (int u = 0; u < NB; ++u) qi[u] = -1;
@@ -391,10 +441,11 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
       }
     }
 #pragma unroll
-    for (int u = 0; u < NB; ++u) issue(cs[u], kr[u], vr[u], qr[u], qi[u], j + u < count);
+    for (int u = 0; u < NB; ++u)
+      issue(cs[u], kr[u], vr[u], qr[u], qi[u], j + u < count, kn[u], vn[u]);
 #pragma unroll
     for (int u = 0; u < NB; ++u)
-      if (j + u < count) compute(cs[u], kr[u], vr[u], qr[u], j + u);
+      if (j + u < count) compute(cs[u], kr[u], vr[u], qr[u], j + u, kn[u], vn[u]);
     // All of the batch's loads have landed here on every path (the ones past
     // the last step are never consumed); saying so keeps the compiler from
     // waiting on them inside the next batch's issue.
@@ -438,17 +489,22 @@ __global__ __launch_bounds__(64) void decode_generic_kernel(DecodeArgs a) {
   }
   float m = -INFINITY, l = 0.f;
   const int32_t* trow = a.block_tables + (int64_t)b * a.max_blocks_per_seq;
+  // fused write (pa_decode_write): position L - 1 comes from the new rows
+  const bool wr = a.k_new != nullptr && L > 0;
+  const int64_t nrow = (int64_t)b * a.new_stride + (int64_t)g * D;
   for (int u = 0; u < L; ++u) {
     int blk = trow[u / bs];
     if (blk < 0 || (int64_t)blk >= a.num_blocks) blk = 0;
     const int off = u % bs;
+    const bool nu = wr && u == L - 1;
     float part = 0.f;
 #pragma unroll
     for (int r = 0; r < MAXR; ++r) {
       const int d = lane + 64 * r;
       if (d < D)
-        part += qd[r] * load_elem<TT>(a.k_cache,
-                                      k_elem_index(blk, g, off, d, hkv, bs, D, TT::bytes));
+        part += qd[r] * (nu ? load_elem<TT>(a.k_new, nrow + d)
+                            : load_elem<TT>(a.k_cache,
+                                            k_elem_index(blk, g, off, d, hkv, bs, D, TT::bytes)));
     }
     const float sc = wave_sum(part) * a.scale_log2e;
     const float m_new = fmaxf(m, sc);
@@ -462,7 +518,29 @@ __global__ __launch_bounds__(64) void decode_generic_kernel(DecodeArgs a) {
       if (d < D) {
         const int64_t vi =
             ((((int64_t)blk * hkv + g) * (bs / vs) + off / vs) * D + d) * vs + off % vs;
-        acc[r] = acc[r] * alpha + pw * load_elem<TT>(a.v_cache, vi);
+        acc[r] = acc[r] * alpha +
+                 pw * (nu ? load_elem<TT>(a.v_new, nrow + d) : load_elem<TT>(a.v_cache, vi));
+      }
+    }
+  }
+  if (wr && h % (a.num_q_heads / hkv) == 0) {  // one q head per kv head stores the token
+    const int pos = L - 1;
+    const int blk = trow[pos / bs];
+    const int off = pos % bs;
+    if (blk >= 0 && (int64_t)blk < a.num_blocks) {
+      using E = typename TT::raw;
+      const E* kn = reinterpret_cast<const E*>(a.k_new);
+      const E* vn = reinterpret_cast<const E*>(a.v_new);
+      E* kc = reinterpret_cast<E*>(const_cast<void*>(a.k_cache));
+      E* vc = reinterpret_cast<E*>(const_cast<void*>(a.v_cache));
+#pragma unroll
+      for (int r = 0; r < MAXR; ++r) {
+        const int d = lane + 64 * r;
+        if (d < D) {
+          kc[k_elem_index(blk, g, off, d, hkv, bs, D, TT::bytes)] = kn[nrow + d];
+          vc[((((int64_t)blk * hkv + g) * (bs / vs) + off / vs) * D + d) * vs + off % vs] =
+              vn[nrow + d];
+        }
       }
     }
   }
@@ -483,15 +561,18 @@ constexpr int valu_batch() {
 
 template <typename TT, int D>
 const void* valu_fn() {
-  return reinterpret_cast<const void*>(&decode_valu_kernel<TT, D, valu_batch<TT, D>()>);
+  return reinterpret_cast<const void*>(&decode_valu_kernel<TT, D, valu_batch<TT, D>(), false>);
 }
 
 template <typename TT, int D>
 hipError_t launch_valu_d(const DecodeArgs& a, hipStream_t s) {
   dim3 grid((a.num_workers + kWaves - 1) / kWaves);
-  const size_t lds = a.split ? sizeof(int) * (3 * (size_t)a.num_seqs + 2) : 0;
-  hipLaunchKernelGGL((decode_valu_kernel<TT, D, valu_batch<TT, D>()>), grid, dim3(kThreads), lds,
-                     s, a);
+  if (a.k_new)
+    hipLaunchKernelGGL((decode_valu_kernel<TT, D, valu_batch<TT, D>(), true>), grid,
+                       dim3(kThreads), decode_split_lds(a), s, a);
+  else
+    hipLaunchKernelGGL((decode_valu_kernel<TT, D, valu_batch<TT, D>(), false>), grid,
+                       dim3(kThreads), decode_split_lds(a), s, a);
   return hipGetLastError();
 }
 

@@ -60,6 +60,15 @@ __device__ __forceinline__ float dot2(BF16, uint32_t a, uint32_t b, float c) {
                                          __builtin_bit_cast(bf162_t, b), c, false);
 }
 
+// c + the two elements of a packed pair, in fp32 (a dot product with 1, 1):
+// a row sum over exactly the rounded weights a matrix op consumes.
+__device__ __forceinline__ float psum2(F16, uint32_t w, float c) {
+  return dot2(F16{}, w, 0x3C003C00u, c);
+}
+__device__ __forceinline__ float psum2(BF16, uint32_t w, float c) {
+  return dot2(BF16{}, w, 0x3F803F80u, c);
+}
+
 // ------------------------------------------------------- lane exchanges --
 // max / sum of x and x in the lane 32 (16) apart, without LDS: one
 // v_permlane32_swap (v_permlane16_swap) of x with a copy of itself leaves,
@@ -110,6 +119,18 @@ struct DecodeArgs {
   float* ws_part;       // [slots][part_record(rows, D)]
   int32_t* ws_pre;      // [B+1] step prefix per sequence (for the merge)
   int32_t* ws_ppre;     // [B+1] partition prefix per sequence (part_steps > 0)
+  // Fused cache write (pa_decode_write), or null: sequence b's new token
+  // (position L_b - 1), K and V rows [Hkv][D] at element b * new_stride of
+  // k_new / v_new.  The split decode kernels then cover positions 0 .. L_b-2;
+  // the token's own term is added by the worker that finishes the item (MHA
+  // kernel) or, with fold_in_merge, by the merge kernel (grouped-query
+  // kernel, which then writes partials only); the merge kernel stores the
+  // token into its slot (through k_cache / v_cache).  The generic kernel
+  // does everything itself.
+  const void* k_new;
+  const void* v_new;
+  int64_t new_stride;
+  int32_t fold_in_merge;  // 1: the decode kernel leaves the token's term to the merge
 };
 
 // ----------------------------------------------------------- prefill args --
@@ -144,6 +165,9 @@ hipError_t launch_decode_generic(const DecodeArgs& a, pa_dtype dt, hipStream_t s
 // worker step of the decode kernel that ran.
 hipError_t launch_decode_merge(const DecodeArgs& a, pa_dtype dt, int items_per_seq,
                                hipStream_t s);
+// pa_decode_write with an unsplit decode: store the new tokens first (the
+// decode then reads them from the pool).
+hipError_t launch_store_new_tokens(const DecodeArgs& a, pa_dtype dt, hipStream_t s);
 bool decode_valu_supported(pa_dtype dt, int head_dim, int block_size);
 // Resident wavefronts per CU of the kernel a call with these arguments runs.
 int decode_valu_waves_per_cu(pa_dtype dt, int head_dim);
@@ -161,6 +185,12 @@ hipError_t launch_swap_blocks(const void* src_k, const void* src_v, void* dst_k,
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs,
                               int32_t num_pairs, int64_t block_bytes, int64_t num_blocks,
                               hipStream_t s);
+
+// Dynamic LDS of a split decode launch (one workgroup): the per-sequence step
+// and partition prefixes and the clamped lengths, 3 * num_seqs + 2 ints.
+__host__ __device__ inline size_t split_lds_bytes(int num_seqs) {
+  return sizeof(int) * (3 * (size_t)num_seqs + 2);
+}
 
 // Floats per partial record (see DecodeArgs::ws_part); rows <= 16.
 __host__ __device__ inline int part_record(int rows, int head_dim) { return rows * head_dim + 32; }

@@ -76,13 +76,6 @@ __device__ __forceinline__ uint32_t pack2(BF16, float lo, float hi) {
   const bf162_t h = {(__bf16)lo, (__bf16)hi};
   return __builtin_bit_cast(uint32_t, h);
 }
-// c + the two elements of a packed pair, in fp32 (a dot product with 1, 1).
-__device__ __forceinline__ float psum2(F16, uint32_t w, float c) {
-  return dot2(F16{}, w, 0x3C003C00u, c);
-}
-__device__ __forceinline__ float psum2(BF16, uint32_t w, float c) {
-  return dot2(BF16{}, w, 0x3F803F80u, c);
-}
 
 // Lane i holds the physical id of logical block base + i (0 for entries past
 // the row or outside the pool: such blocks only feed masked keys).
@@ -261,7 +254,7 @@ __global__ __launch_bounds__(64 * WV) void prefill_mfma_kernel(PrefillArgs a) {
     for (int s = 0; s < QN; ++s)
       qr[s] = qrow < nrows ? ld16(qp + (WR == 16 ? 64 : 32) * s) : make_uint4(0, 0, 0, 0);
   }
-  // Scores are used as s * scl with scl = |scale * log2 e| > 0 (so the
+  // Scores are used as s * scl with scl = |scale * log2 e| >= 0 (so the
   // maximum of the raw dot products gives the maximum score, and the scale
   // folds into the exponent's fma); a negative scale flips q's sign bits
   // instead, which is exact.
@@ -464,6 +457,11 @@ __global__ __launch_bounds__(64 * WV) void prefill_mfma_kernel(PrefillArgs a) {
     float pw[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) pw[e] = __builtin_amdgcn_exp2f(fmaf(sc[e], scl, -m_run));
+    if (tok + kKeys - 1 > pos0) {  // masked keys weigh 0 also at scale 0 (-inf * 0 is NaN)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (tok + 8 * kb + e > mypos) pw[e] = 0.f;
+    }
     // P^T operand: keys 8 kb .. 8 kb + 7 of query n, all held by this lane;
     // the row sum takes the same rounded weights the matrix op does
     const uint4 pb = make_uint4(pack2(TT{}, pw[0], pw[1]), pack2(TT{}, pw[2], pw[3]),
@@ -530,6 +528,11 @@ __global__ __launch_bounds__(64 * WV) void prefill_mfma_kernel(PrefillArgs a) {
     float pw[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) pw[r] = __builtin_amdgcn_exp2f(fmaf(sc[r], scl, -m_run));
+    if (tok + kKeys - 1 > pos0) {  // masked keys weigh 0 also at scale 0 (-inf * 0 is NaN)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (tok + 8 * hh + r + (r >= 8 ? 8 : 0) > mypos) pw[r] = 0.f;
+    }
     uint4 pb[2];
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh)

@@ -39,13 +39,26 @@ def admit(alloc, seq_ids, prompts, salt: int = 0, max_blocks: int | None = None)
     BlockAllocator), reusing cached prefix blocks; all prompts are admitted
     in the given order, so a later prompt reuses blocks an earlier one of the
     same call filled (its K / V is written by this iteration's
-    pa_reshape_and_cache, before the attention reads it)."""
+    pa_reshape_and_cache, before the attention reads it).
+
+    All or nothing: if a prompt cannot be admitted (e.g. OutOfBlocks), the
+    prompts admitted before it in this call are discarded again, newest
+    first, together with the prefix-table entries they created -- their K / V
+    will never be written -- and the error is re-raised.  (Evictions made on
+    their behalf are not undone.)"""
     seq_ids = np.asarray(seq_ids, dtype=np.int64)
     B = len(seq_ids)
     lens = np.array([len(p) for p in prompts], dtype=np.int32)
     cached = np.zeros(B, dtype=np.int32)
-    for i, (s, p) in enumerate(zip(seq_ids, prompts)):
-        cached[i] = alloc.add_seq_tokens(int(s), p, salt)
+    done = 0
+    try:
+        for i, (s, p) in enumerate(zip(seq_ids, prompts)):
+            cached[i] = alloc.add_seq_tokens(int(s), p, salt)
+            done = i + 1
+    except Exception:
+        for s in reversed(seq_ids[:done]):
+            alloc.discard_seq(int(s))
+        raise
     bs = alloc.block_size
     if max_blocks is None:
         max_blocks = max(1, int(-(-lens.max(initial=0) // bs)))

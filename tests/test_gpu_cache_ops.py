@@ -237,3 +237,27 @@ def test_swap_refuses_pageable_host_memory():
                                  pairs.data_ptr(), 1, 4, 4, hkv, D, bs, 1, None)
     assert rc == -1
     assert (hk == 0).all() and (hv == 0).all()
+
+
+def test_reshape_and_cache_refuses_host_rows():
+    """Token rows in pageable host memory are refused by the binding, and by
+    the C entry point itself, before anything runs; the pools are untouched.
+    Rows that are a strided view into a larger device tensor are accepted."""
+    hkv, D, bs = 2, 128, 16
+    kc, vc = _pool(4, hkv, bs, D, "f16", 17)
+    k0, v0 = kc.clone(), vc.clone()
+    hk = torch.ones((3, hkv, D), dtype=torch.float16)
+    hv = torch.ones((3, hkv, D), dtype=torch.float16)
+    slots = torch.tensor([0, 5, 17], dtype=torch.int64, device=DEV)
+    with pytest.raises(ValueError):
+        pa.pa_reshape_and_cache(hk, hv, kc, vc, slots, bs)
+    rc = pa.lib().pa_reshape_and_cache(hk.data_ptr(), hv.data_ptr(), kc.data_ptr(), vc.data_ptr(),
+                                       slots.data_ptr(), 3, hkv * D, hkv * D, hkv, D, bs, 4, 1,
+                                       None)
+    assert rc == -1
+    torch.cuda.synchronize()
+    assert torch.equal(kc, k0) and torch.equal(vc, v0)
+    # interior device pointers (a token-strided view) pass the check
+    big = torch.randn((3, 2, hkv, D), dtype=torch.float32, device=DEV).to(torch.float16)
+    pa.pa_reshape_and_cache(big[:, 1], big[:, 0], kc, vc, slots, bs)
+    torch.cuda.synchronize()

@@ -330,14 +330,14 @@ def test_workspace_same_layout_many_calls(spec_name, part):
         assert max_err(out, oracle_decode(case)) <= TOL[spec.dtype]
 
 
-@pytest.mark.parametrize("scale", [-0.2, 0.01, 1.5])
+@pytest.mark.parametrize("scale", [0.0, -0.2, 0.01, 1.5])
 @pytest.mark.parametrize("spec_name", ["opt13b_f16_bs16", "gqa_bf16_g8_bs32",
                                        "mha_f16_d32_bs4_generic"])
 @pytest.mark.parametrize("part", [0, 512])
 def test_decode_any_scale(scale, spec_name, part, orc):
-    """Scales other than 1/sqrt(D) -- negative, small (flat weights), large
-    (sharp weights) -- on the VALU, MFMA and generic kernels, split and
-    partitioned, against the oracle at the same scale."""
+    """Scales other than 1/sqrt(D) -- zero (the mean of V), negative, small
+    (flat weights), large (sharp weights) -- on the VALU, MFMA and generic
+    kernels, split and partitioned, against the oracle at the same scale."""
     spec = SMALL[spec_name]
     log(f"[decode scale] {scale} {spec_name} partition={part}")
     c = to_dev(W.make_decode_case(spec, device=DEV, poison=True))

@@ -128,12 +128,14 @@ def test_prefill_every_workgroup_shape(rows, waves, dma, monkeypatch):
         assert err <= TOL[spec.dtype]
 
 
-@pytest.mark.parametrize("scale", [-0.2, 0.01, 1.5])
+@pytest.mark.parametrize("scale", [0.0, -0.2, 0.01, 1.5])
 @pytest.mark.parametrize("rows", [16, 32])
 def test_prefill_any_scale(scale, rows, monkeypatch):
-    """Scales other than 1/sqrt(D): negative (the kernel flips q's sign bits
-    and keeps a positive factor), small (flat weights) and large (sharp
-    weights), on both wavefront shapes, against the oracle at the same scale."""
+    """Scales other than 1/sqrt(D): zero (every visible key weighs the same,
+    and the masked keys' -inf scores must not turn into NaN), negative (the
+    kernel flips q's sign bits and keeps a positive factor), small (flat
+    weights) and large (sharp weights), on both wavefront shapes, against the
+    oracle at the same scale."""
     monkeypatch.setenv("PA_PREFILL_ROWS", str(rows))
     for name in ("mha_f16_bs16", "gqa_bf16_g8_bs32"):
         spec = SPECS[name]
