@@ -63,7 +63,8 @@ typedef enum {
   PA_ENOMEM = -3,    /* allocator: not enough free blocks (nothing changed) */
   PA_EHIP = -4,      /* a HIP runtime call or kernel launch failed */
   PA_EVALIDATE = -5, /* PA_VALIDATE=1 found a bad index in device data */
-  PA_ENOENT = -6     /* allocator: unknown sequence id, or id already used */
+  PA_ENOENT = -6,    /* allocator: unknown sequence id, or id already used */
+  PA_ESCRATCH = -7   /* pa_decode_noalloc: the call needs more than its static scratch */
 } pa_status;
 
 typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
@@ -162,6 +163,29 @@ pa_status pa_decode_write(void* out, const void* q, const void* k_new, const voi
                           int32_t max_context_len, int64_t num_blocks, pa_dtype dtype,
                           int32_t partition_size, void* workspace, size_t workspace_bytes,
                           void* stream);
+
+/* ------------------------------------------------------------------------
+ * pa_decode_noalloc -- pa_decode for callers that cannot allocate device
+ * memory: code under graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, result and checks as pa_decode, minus
+ * the workspace: the split's scratch is a static array inside libpa, one per
+ * device, of pa_decode_noalloc_scratch_bytes() bytes (32 MiB), held by every
+ * device the library runs on until the process ends.  A call whose
+ * pa_decode_workspace_bytes(...) exceeds it returns PA_ESCRATCH before any
+ * launch.  Nothing is allocated on any call.  Every call on a device shares
+ * that device's array, so calls that overlap on one device (e.g. on two
+ * streams) race and must not be issued; nothing in the array needs clearing
+ * between calls.
+ * ---------------------------------------------------------------------- */
+pa_status pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, const int32_t* context_lens,
+                            float scale, int32_t block_size, int32_t num_kv_heads,
+                            int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                            int32_t max_blocks_per_seq, int32_t max_context_len,
+                            int64_t num_blocks, pa_dtype dtype, int32_t partition_size,
+                            void* stream);
+/* Bytes of pa_decode_noalloc's static scratch (the largest workspace it serves). */
+size_t pa_decode_noalloc_scratch_bytes(void);
 
 /* Workspace bytes pa_decode needs for these sizes (0 when nothing splits).
  * Pass the same arguments as to pa_decode, on the device it will run on (the

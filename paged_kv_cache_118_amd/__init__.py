@@ -40,6 +40,9 @@ def _load():
                             i32, i32, vp, sz, vp]),
         "pa_decode_write": (i32, [vp, vp, vp, vp, i64, vp, vp, vp, vp, f32, i32, i32, i32, i32,
                                   i32, i32, i32, i64, i32, i32, vp, sz, vp]),
+        "pa_decode_noalloc": (i32, [vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, i32, i32, i32,
+                                    i32, i64, i32, i32, vp]),
+        "pa_decode_noalloc_scratch_bytes": (sz, []),
         "pa_decode_workspace_bytes": (sz, [i32, i32, i32, i32, i32, i32, i32, i32]),
         "pa_decode_partition_size": (i32, [i32, i32, i32, i32, i32, i32, i32, i32]),
         "pa_prefill": (i32, [vp, vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, i32, i32, i32, i32,
@@ -78,7 +81,8 @@ def _load():
 _lib = _load()
 
 # every symbol include/pa.h declares (checked by the CPU test suite)
-EXPORTED = ("pa_strerror", "pa_decode", "pa_decode_write", "pa_decode_workspace_bytes",
+EXPORTED = ("pa_strerror", "pa_decode", "pa_decode_write", "pa_decode_noalloc",
+            "pa_decode_noalloc_scratch_bytes", "pa_decode_workspace_bytes",
             "pa_decode_partition_size",
             "pa_prefill", "pa_swap_blocks",
             "pa_reshape_and_cache", "pa_copy_blocks", "pa_alloc_create", "pa_alloc_destroy",
@@ -226,6 +230,35 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, block
                           num_kv_heads, B, hq, D, block_tables.shape[1], int(max_context_len),
                           nb, dt, int(partition_size), ws_ptr, ws_len, _stream(stream)))
     return out
+
+
+def pa_decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
+                      num_kv_heads, max_context_len, partition_size=0, stream=None):
+    """pa_decode with the split's scratch in libpa's static per-device array
+    (nothing allocated; see pa.h).  Raises PAError with status -7 when the
+    call would need more than pa_decode_noalloc_scratch_bytes()."""
+    B, hq, D = q.shape
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q in shape and dtype")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("pools must have q's dtype")
+    nb = _check_pools(k_cache, v_cache, num_kv_heads, block_size, D)
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("block_tables and context_lens must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_tables must be [num_seqs, max_blocks], context_lens [num_seqs]")
+    _check(_lib.pa_decode_noalloc(_dev_ptr(out, "out"), _dev_ptr(q, "q"),
+                                  _dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"),
+                                  _dev_ptr(block_tables, "block_tables"),
+                                  _dev_ptr(context_lens, "context_lens"), float(scale),
+                                  block_size, num_kv_heads, B, hq, D, block_tables.shape[1],
+                                  int(max_context_len), nb, _dtype_code(q), int(partition_size),
+                                  _stream(stream)))
+    return out
+
+
+def pa_decode_noalloc_scratch_bytes() -> int:
+    return int(_lib.pa_decode_noalloc_scratch_bytes())
 
 
 def pa_decode_write(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale,

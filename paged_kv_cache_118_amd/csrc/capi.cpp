@@ -159,7 +159,7 @@ bool copy_to_host(std::vector<T>& dst, const T* src, size_t n, hipStream_t s) {
 
 }  // namespace
 
-namespace {
+namespace pa {
 
 // pa_decode and pa_decode_write: k_new / v_new null for a plain decode.
 pa_status decode_impl(void* out, const void* q, const void* k_new, const void* v_new,
@@ -293,7 +293,7 @@ pa_status decode_impl(void* out, const void* q, const void* k_new, const void* v
   return hip_status(e);
 }
 
-}  // namespace
+}  // namespace pa
 
 extern "C" {
 
@@ -306,6 +306,7 @@ const char* pa_strerror(pa_status s) {
     case PA_EHIP: return "HIP runtime or launch failure";
     case PA_EVALIDATE: return "device index data failed validation";
     case PA_ENOENT: return "unknown or duplicate sequence id";
+    case PA_ESCRATCH: return "the call needs more scratch than pa_decode_noalloc's static array";
   }
   return "unknown status";
 }

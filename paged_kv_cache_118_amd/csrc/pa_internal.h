@@ -154,6 +154,16 @@ struct PrefillArgs {
   int64_t num_blocks;
 };
 
+// pa_decode / pa_decode_write behind argument checks (capi.cpp).
+pa_status decode_impl(void* out, const void* q, const void* k_new, const void* v_new,
+                      int64_t new_stride, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* context_lens, float scale,
+                      int32_t block_size, int32_t num_kv_heads, int32_t num_seqs,
+                      int32_t num_q_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                      int32_t max_context_len, int64_t num_blocks, pa_dtype dtype,
+                      int32_t partition_size, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
 hipError_t launch_prefill(const PrefillArgs& a, pa_dtype dt, hipStream_t s);
 bool prefill_supported(pa_dtype dt, int head_dim, int block_size);
 
