@@ -45,6 +45,8 @@ def parse():
                     help="tokens per split partition (0 = library choice, -1 = never)")
     ap.add_argument("--replicas", type=int, default=0, help="0 = enough for >= 2 GB")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-gqa", action="store_true",
+                    help="leave out the GQA long-context sub-record of the default run")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
@@ -214,6 +216,7 @@ class Workload:
         self.dtype = spec.dtype
         self.part = spec.partition_size if args.partition is None else args.partition
         self.pairs_dev = None
+        self.groups = None  # (group_start, group_prefix_len) of a sharing batch
         if name == "llama13b_prefix_share":
             self._build_share()
         elif name == "opt66b_sweep":
@@ -286,18 +289,25 @@ class Workload:
                 a.fork(c, 200_000 + c)  # beam parent keeps the partial tail shared
             return a
 
+        max_members = 16 // (sp.num_q_heads // sp.num_kv_heads)
+
         def step(a):
             slots, pairs = a.append_batch(np.arange(B), np.ones(B, dtype=np.int32))
             tables, lens_now = a.block_tables(np.arange(B), maxb)
-            return slots, pairs.reshape(-1, 2), tables, lens_now
+            gs, gp = a.share_groups(np.arange(B), max_members)
+            return slots, pairs.reshape(-1, 2), tables, lens_now, gs, gp
 
-        _, (slots, pairs, tables, lens_now) = self._alloc_step(build, step)
+        _, (slots, pairs, tables, lens_now, gs, gp) = self._alloc_step(build, step)
         self.lens, self.tables, self.slots, self.nb = lens_now, tables, slots, nb
         self.pairs = pairs
+        self.groups = (gs, gp)
         self.decode_idx = None
-        uniq_tokens = groups * prefix + int(np.sum(lens_now - prefix))
+        # unique bytes: each group's shared prefix once, every sequence's own rest
+        member_prefix = np.repeat(gp, np.diff(gs))
+        uniq_tokens = int(gp.sum()) + int(np.sum(lens_now - member_prefix))
         self.unique_kv_bytes = uniq_tokens * self._tok_bytes()
         self.config = {"workload": sp.name, "num_seqs": B, "groups": groups, "prefix": prefix,
+                       "share_groups": int(len(gp)),
                        "q_heads": sp.num_q_heads, "kv_heads": sp.num_kv_heads,
                        "head_dim": sp.head_dim, "block_size": bs, "tails": [lo, hi],
                        "cow_pairs": int(len(pairs)), "pool_blocks": nb}
@@ -389,6 +399,13 @@ class Workload:
         ws = self.pa.pa_decode_workspace_bytes(B, sp.num_q_heads, sp.num_kv_heads, sp.head_dim,
                                                sp.block_size, self.max_ctx, self.part,
                                                W.TORCH_DTYPE[sp.dtype])
+        if self.groups is not None:
+            gs, gp = self.groups
+            self.gs_dev = torch.from_numpy(gs).to(dev)
+            self.gp_dev = torch.from_numpy(gp).to(dev)
+            ws = max(ws, self.pa.pa_decode_shared_workspace_bytes(
+                B, len(gp), sp.num_q_heads, sp.num_kv_heads, sp.head_dim, sp.block_size,
+                self.max_ctx, W.TORCH_DTYPE[sp.dtype]))
         self.ws = torch.zeros(max(ws, 1), dtype=torch.uint8, device=dev)
         self.config["partition"] = self.pa.pa_decode_partition_size(
             B, sp.num_q_heads, sp.num_kv_heads, sp.head_dim, sp.block_size, self.max_ctx,
@@ -443,6 +460,18 @@ class Workload:
 
     # -- the timed step ----------------------------------------------------
     def decode(self, r):
+        """The step's decode call: pa_decode_shared for a sharing batch (each
+        shared block read once per group), else pa_decode."""
+        sp = self.spec
+        if self.groups is not None:
+            self.pa.pa_decode_shared(self.out, self.q[r], self.k[r], self.v[r], self.tables_dev,
+                                     self.lens_dev, self.gs_dev, self.gp_dev, sp.scale,
+                                     sp.block_size, sp.num_kv_heads, self.max_ctx,
+                                     workspace=self.ws)
+        else:
+            self.decode_plain(r)
+
+    def decode_plain(self, r):
         sp = self.spec
         self.pa.pa_decode(self.out, self.q[r], self.k[r], self.v[r], self.tables_dev,
                           self.lens_dev, sp.scale, sp.block_size, sp.num_kv_heads, self.max_ctx,
@@ -451,8 +480,13 @@ class Workload:
     def step(self, r):
         """Copy-on-write copies (if any), then the decoding sequences' new
         tokens written and attended in one pa_decode_write launch; a mixed
-        step's prompt-chunk tokens are written by pa_reshape_and_cache first."""
+        step's prompt-chunk tokens are written by pa_reshape_and_cache first.
+        A sharing batch writes with pa_reshape_and_cache and decodes with
+        pa_decode_shared."""
         pa, sp = self.pa, self.spec
+        if self.groups is not None:  # the shared decode reads the pools as written
+            self.step_separate(r)
+            return
         if self.pairs_dev is not None:
             pa.pa_copy_blocks(self.k[r], self.v[r], self.pairs_dev, sp.block_size)
         if self.n_chunk_tokens:
@@ -629,12 +663,29 @@ def prefill_run(args, torch, wl):
         "config": {"workload": "opt66b_sweep chunk writers", "seqs": B, "query_tokens": ql,
                    "q_heads": H, "kv_heads": sp.num_kv_heads, "head_dim": D,
                    "block_size": sp.block_size, "contexts": [int(x) for x in ctx]},
-        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": None},
+        "roofline": prefill_roofline(flops, kv_bytes, ms / 1e3, peak),
+        "mfma_TFLOPs_frac": round(tflops / peak, 4),
         "kv_bytes_per_call": kv_bytes,
         "kv_GBps_if_read_once": round(kv_bytes / (ms / 1e3) / 1e9, 1),
     }
     print(json.dumps(rec), flush=True)
+
+
+def prefill_roofline(flops, kv_bytes, seconds, peak_tflops):
+    """The binding roof of a chunked-prefill call: matrix-core time of its
+    algorithmic flops or HBM time of its K/V read once, whichever is longer
+    (ridge: 2.5 PFLOP/s / 8 TB/s = 312 flop/byte)."""
+    t_flop = flops / (peak_tflops * 1e12)
+    t_byte = kv_bytes / (HBM_PEAK_GBS * 1e9)
+    if t_flop >= t_byte:
+        ach = flops / seconds / 1e12
+        return {"bound": "mfma", "achieved": round(ach, 2), "peak": peak_tflops,
+                "unit": "TFLOP/s", "frac": round(ach / peak_tflops, 4), "traffic": None,
+                "flop_per_byte": round(flops / kv_bytes, 1)}
+    ach = kv_bytes / seconds / 1e9
+    return {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+            "flop_per_byte": round(flops / kv_bytes, 1)}
 
 
 def swap_run(args, torch, wl):
@@ -776,6 +827,7 @@ def prefix_cache_run(args, torch):
 
     res = {}
     outs = {}
+    roofs = {}
     for name, cached in (("reuse", True), ("recompute", False)):
         st = setup(cached)
         for _ in range(max(1, args.warmup // 5)):
@@ -802,6 +854,9 @@ def prefix_cache_run(args, torch):
         res[name] = {"ms_per_iteration": round(ms, 4), "prefill_ms": round(pms, 4),
                      "rows_queried": st["rows"], "rows_written": st["written"],
                      "prefill_TFLOPs": round(flops / (pms / 1e3) / 1e12, 1)}
+        # each (sequence, kv head) reads its whole context once
+        roofs[name] = prefill_roofline(flops, int(L.sum()) * 2 * sp.num_kv_heads * sp.head_dim * 2,
+                                       pms / 1e3, MFMA_PEAK_TFLOPS[sp.dtype])
         outs[name] = (st["out"], st["rs"], st["rp"])
         del st
     o_r, rs_r, rp_r = outs["reuse"]
@@ -809,8 +864,6 @@ def prefix_cache_run(args, torch):
     start = np.concatenate([[0], np.cumsum(L)])
     at = torch.from_numpy(start[rs_r] + rp_r).to(dev)
     diff = float((o_r.double() - o_f[at].double()).abs().max())
-    peak = MFMA_PEAK_TFLOPS[sp.dtype]
-    tf = res["reuse"]["prefill_TFLOPs"]
     print(json.dumps({
         "metric": "prefix_cache_iteration_speedup",
         "value": round(res["recompute"]["ms_per_iteration"] / res["reuse"]["ms_per_iteration"], 3),
@@ -825,8 +878,7 @@ def prefix_cache_run(args, torch):
         "blocks_held_with_reuse": int(blocks_cached), "blocks_held_without": int(blocks_plain),
         "host_admission_us_per_prompt": round(host_us, 2),
         **res, "max_abs_diff_reuse_vs_recompute": diff,
-        "roofline": {"bound": "mfma", "achieved": tf, "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(tf / peak, 4), "traffic": None},
+        "roofline": roofs["reuse"],
     }), flush=True)
 
 
@@ -904,22 +956,14 @@ def main():
     torch.cuda.synchronize()
     ms_step_sep = (time.perf_counter() - t0) * 1e3 / args.steps
 
-    # timed region 2: K pa_decode calls back to back (the step's other calls
-    # left out), bracketed by HIP events on the stream they run on: the mean
-    # duration of one call (its decode and merge kernels) for the roofline
-    stream = torch.cuda.current_stream()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    ev0.record(stream)
-    for i in range(args.steps):
-        wl.decode(i % wl.replicas)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    dec_ms = ev0.elapsed_time(ev1) / args.steps
-
+    # timed region 2: the decode call alone (the step's other calls left
+    # out), for the roofline
+    call = time_calls(torch, wl.decode, wl.replicas)
     kv_gb = wl.kv_read_bytes / 1e9
     value = kv_gb / (ms_step / 1e3)
-    achieved = wl.decode_alg_bytes / 1e9 / (dec_ms / 1e3)
+    roof_bytes = getattr(wl, "unique_kv_bytes", wl.kv_read_bytes)
+    achieved = roof_bytes / 1e9 / (call["mean_us"] / 1e6)
+    ceiling = stream_read_ceiling(torch, wl.pa)
     rec = {
         "metric": "paged_decode_kv_read_GBps",
         "value": round(value, 2),
@@ -937,7 +981,7 @@ def main():
         "config": wl.config,
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "seq_per_s": round(wl.decode_seqs / (ms_step / 1e3), 1),
-        "decode_kernel_ms": round(dec_ms, 5),
+        "decode_call_us": call,
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 2),
@@ -946,28 +990,125 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": stored_traffic(args.workload, args.partition),
             "kernel": wl.roofline_kernel,
+            "bytes": "unique K/V (shared prefix once)" if hasattr(wl, "unique_kv_bytes")
+            else "K/V of the valid positions",
+            "frac_median_call": round(roof_bytes / 1e9 / (call["median_us"] / 1e6) /
+                                      HBM_PEAK_GBS, 4),
+            "frac_of_stream_read": round(achieved / ceiling["GBps"], 4),
         },
+        "hbm_stream_read": ceiling,
         "host_alloc_us_per_step": wl.host_alloc_us,
     }
+    if hasattr(wl, "unique_kv_bytes"):
+        plain = time_calls(torch, wl.decode_plain, wl.replicas)
+        rec["unique_kv_bytes_per_step"] = wl.unique_kv_bytes
+        rec["logical_GBps_call"] = round(wl.kv_read_bytes / 1e3 / call["mean_us"], 1)
+        rec["plain_decode_call_us"] = plain
+        rec["plain_decode_frac_unique"] = round(
+            wl.unique_kv_bytes / 1e3 / plain["mean_us"] / HBM_PEAK_GBS, 4)
     if wl.mfma_path:
-        # GQA groups run on the matrix cores: the algorithmic flops (q.k and
-        # p.v, 2 per multiply-add) and, from the stored counter record, the
-        # issued ones (the group's rows are padded to 16), against the peak
-        sp = wl.spec
-        alg = 4.0 * sp.head_dim * sp.num_q_heads * float(np.sum(wl.lens.astype(np.int64)))
-        issued = stored_mfma(args.workload, args.partition)
-        peak = MFMA_PEAK_TFLOPS[wl.dtype]
-        rec["mfma"] = {
-            "alg_tflops": round(alg / (dec_ms / 1e3) / 1e12, 2),
-            "alg_frac": round(alg / (dec_ms / 1e3) / 1e12 / peak, 4),
-            "issued_tflops": None if issued is None else round(issued / (dec_ms / 1e3) / 1e12, 2),
-            "issued_frac": None if issued is None else
-            round(issued / (dec_ms / 1e3) / 1e12 / peak, 4),
-            "peak_tflops": peak,
-        }
+        rec["mfma"] = mfma_record(wl, args, call["mean_us"] / 1e3)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = wl.cpu_baseline(args.cpu_seconds)
+    if args.workload == "opt13b_decode" and not args.no_gqa:
+        rec["gqa_long"] = gqa_subrecord(args, torch)
     print(json.dumps(rec), flush=True)
+
+
+def time_calls(torch, fn, replicas, groups=20, per=10):
+    """Mean duration of one call of fn(replica) on the current stream, from
+    HIP events around groups of `per` back-to-back calls (per-call event
+    markers would add their own cost), with the median and min over the
+    groups."""
+    for i in range(per):
+        fn(i % replicas)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(groups + 1)]
+    k = 0
+    evs[0].record(stream)
+    for g in range(groups):
+        for _ in range(per):
+            fn(k % replicas)
+            k += 1
+        evs[g + 1].record(stream)
+    torch.cuda.synchronize()
+    us = np.array([evs[g].elapsed_time(evs[g + 1]) * 1e3 / per for g in range(groups)])
+    total = evs[0].elapsed_time(evs[groups]) * 1e3 / (groups * per)
+    return {"mean_us": round(float(total), 2), "median_us": round(float(np.median(us)), 2),
+            "min_us": round(float(us.min()), 2), "calls": groups * per}
+
+
+def stream_read_ceiling(torch, pa, gib=4, reps=10):
+    """HBM read ceiling in this run: libpa's plain streaming-read kernel
+    (pa_bench_stream_read, 16-byte non-temporal loads) over a 4 GiB buffer,
+    event-timed back to back."""
+    n = gib << 30
+    buf = torch.ones(n // 4, dtype=torch.int32, device="cuda")
+    wg = 8 * torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.zeros(wg * 256, dtype=torch.int32, device="cuda")
+    for _ in range(2):
+        pa.bench_stream_read(buf, sink, wg)
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(reps):
+        pa.bench_stream_read(buf, sink, wg)
+    e1.record(s)
+    torch.cuda.synchronize()
+    gbps = n * reps / (e0.elapsed_time(e1) / 1e3) / 1e9
+    del buf
+    return {"GBps": round(gbps, 1), "bytes": n, "frac_of_peak": round(gbps / HBM_PEAK_GBS, 4),
+            "kernel": "pa_bench_stream_read"}
+
+
+def mfma_record(wl, args, call_ms):
+    """GQA groups run on the matrix cores: the algorithmic flops (q.k and p.v,
+    2 per multiply-add) and, from the stored counter record, the issued ones
+    (the group's rows are padded to 16), against the dense peak."""
+    sp = wl.spec
+    alg = 4.0 * sp.head_dim * sp.num_q_heads * float(np.sum(wl.lens.astype(np.int64)))
+    issued = stored_mfma(wl.args.workload, wl.args.partition)
+    peak = MFMA_PEAK_TFLOPS[wl.dtype]
+    t = call_ms / 1e3
+    return {
+        "alg_tflops": round(alg / t / 1e12, 2),
+        "alg_frac": round(alg / t / 1e12 / peak, 4),
+        "issued_tflops": None if issued is None else round(issued / t / 1e12, 2),
+        "issued_frac": None if issued is None else round(issued / t / 1e12 / peak, 4),
+        "peak_tflops": peak,
+    }
+
+
+def gqa_subrecord(args, torch):
+    """The second >= 70% target workload, in the same run: the GQA
+    long-context decode (64 q / 8 kv heads, bf16, contexts 16-32k, 512-token
+    partitions): its pa_decode call against the HBM roofline, its matrix-core
+    use, and the oracle on a sample."""
+    import argparse
+    a = argparse.Namespace(**vars(args))
+    a.workload, a.partition, a.replicas, a.block_size = "gqa_long", None, 0, None
+    wl = Workload(a, torch.device("cuda:0"))
+    torch.cuda.synchronize()
+    call = time_calls(torch, wl.decode, wl.replicas, groups=10, per=5)
+    achieved = wl.kv_read_bytes / 1e3 / call["mean_us"]
+    sub = {
+        "config": wl.config,
+        "decode_call_us": call,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "frac_median_call": round(wl.kv_read_bytes / 1e3 / call["median_us"] /
+                                               HBM_PEAK_GBS, 4),
+                     "traffic": stored_traffic("gqa_long", None),
+                     "kernel": wl.roofline_kernel},
+        "mfma": mfma_record(wl, a, call["mean_us"] / 1e3),
+    }
+    if not args.no_cpu_baseline:
+        sub["cpu_baseline"] = wl.cpu_baseline(args.cpu_seconds)
+    del wl
+    torch.cuda.empty_cache()
+    return sub
 
 
 if __name__ == "__main__":

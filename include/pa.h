@@ -187,6 +187,53 @@ pa_status pa_decode_noalloc(void* out, const void* q, const void* k_cache, const
 /* Bytes of pa_decode_noalloc's static scratch (the largest workspace it serves). */
 size_t pa_decode_noalloc_scratch_bytes(void);
 
+/* ------------------------------------------------------------------------
+ * pa_decode_shared -- pa_decode for a batch in which groups of sequences
+ * share their leading blocks (a beam or parallel-sampling family, prompts
+ * with a common prefix: [P5] section 二 "共享与写时复制" -- the shared blocks
+ * are held once, by reference count).  Same result as pa_decode (one softmax
+ * over all of each sequence's positions, [P5] section 二, the Z / o
+ * equations), but each shared block is read from memory once per group
+ * instead of once per member.
+ *
+ * Groups are runs of consecutive sequences: group g is sequences
+ * group_start[g] .. group_start[g+1]-1, and its first group_prefix_len[g]
+ * positions (a multiple of BS, at most every member's length) lie in the
+ * same physical blocks in every member's table.  group_start[0] = 0,
+ * group_start[num_groups] = num_seqs, every group has at least one member
+ * and members * (num_q_heads / num_kv_heads) <= 16; a prefix of 0 is allowed
+ * (a group that shares nothing).  pa_alloc_share_groups produces such groups
+ * from an allocator's tables.
+ *
+ * How: a prefix pass on the matrix cores reads each group's shared blocks
+ * once per kv head and scores them against the q rows of all its members (a
+ * small dense contraction: members x q heads per kv head), a tail pass
+ * streams each sequence from its group's prefix on, and a merge combines
+ * the two fp32 partial softmax states of every row.
+ *  group_start       [num_groups + 1] int32 (device)
+ *  group_prefix_len  [num_groups] int32 (device), tokens
+ *  workspace         at least pa_decode_shared_workspace_bytes(...) bytes
+ *  other arguments   as pa_decode (the split is the token-balanced one)
+ * The prefix pass needs f16 / bf16, head_dim 64 or 128 and block_size 8, 16
+ * or a multiple of 32; otherwise, and for num_groups = 0, the call is a plain
+ * pa_decode with partition_size 0 (the same result).  Group data is not
+ * checked on the hot path (PA_VALIDATE=1 checks all of the above, table
+ * entries included); groups that break the rules give undefined rows, never
+ * an access outside the tables, pools or workspace.
+ * ---------------------------------------------------------------------- */
+pa_status pa_decode_shared(void* out, const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_tables, const int32_t* context_lens, float scale,
+                           int32_t block_size, int32_t num_kv_heads, int32_t num_seqs,
+                           int32_t num_q_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                           int32_t max_context_len, int64_t num_blocks, pa_dtype dtype,
+                           const int32_t* group_start, const int32_t* group_prefix_len,
+                           int32_t num_groups, void* workspace, size_t workspace_bytes,
+                           void* stream);
+size_t pa_decode_shared_workspace_bytes(int32_t num_seqs, int32_t num_groups,
+                                        int32_t num_q_heads, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t block_size,
+                                        int32_t max_context_len, pa_dtype dtype);
+
 /* Workspace bytes pa_decode needs for these sizes (0 when nothing splits).
  * Pass the same arguments as to pa_decode, on the device it will run on (the
  * balanced split sizes itself by the device's CU count). */
@@ -347,6 +394,19 @@ pa_status pa_alloc_free_seq(pa_alloc* a, int64_t seq_id);
  * (those entries' blocks go to the free list).  Entries the sequence reused
  * from others are untouched. */
 pa_status pa_alloc_discard_seq(pa_alloc* a, int64_t seq_id);
+
+/* Groups for pa_decode_shared from the tables of seq_ids[0..n-1], in that
+ * order: sequence j joins the group of an earlier sequence i (the group's
+ * first member) when their tables begin with the same physical blocks, full
+ * in both, and -- for the third member on -- at least as many of them as the
+ * first two share; the group's prefix is the number of such blocks the first
+ * two share (times block_size; 0 for a group of one).  A group never has more
+ * than max_members members (pass 16 / (num_q_heads / num_kv_heads)).
+ * Writes group_start_out[0..G] and group_prefix_out[0..G-1], *num_groups_out
+ * = G; both arrays need room for n + 1 and n entries.  Host memory only. */
+pa_status pa_alloc_share_groups(const pa_alloc* a, const int64_t* seq_ids, int32_t n,
+                                int32_t max_members, int32_t* group_start_out,
+                                int32_t* group_prefix_out, int32_t* num_groups_out);
 
 /* Host rows for pa_decode: tables_out [n][max_blocks] (padded with -1) and
  * lens_out [n].  PA_EINVAL if a sequence holds more than max_blocks blocks. */

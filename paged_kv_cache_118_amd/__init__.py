@@ -59,6 +59,11 @@ def _load():
         "pa_alloc_append_batch": (i32, [vp, vp, vp, i32, vp, vp, vp, vp]),
         "pa_alloc_free_seq": (i32, [vp, i64]),
         "pa_alloc_discard_seq": (i32, [vp, i64]),
+        "pa_alloc_share_groups": (i32, [vp, vp, i32, i32, vp, vp, vp]),
+        "pa_decode_shared": (i32, [vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, i32, i32, i32,
+                                   i32, i64, i32, vp, vp, i32, vp, sz, vp]),
+        "pa_decode_shared_workspace_bytes": (sz, [i32, i32, i32, i32, i32, i32, i32, i32]),
+        "pa_bench_stream_read": (i32, [vp, sz, vp, i32, vp]),
         "pa_alloc_block_tables": (i32, [vp, vp, i32, i32, vp, vp]),
         "pa_alloc_num_free": (i64, [vp]),
         "pa_alloc_refcount": (i32, [vp, i64]),
@@ -87,7 +92,8 @@ EXPORTED = ("pa_strerror", "pa_decode", "pa_decode_write", "pa_decode_noalloc",
             "pa_prefill", "pa_swap_blocks",
             "pa_reshape_and_cache", "pa_copy_blocks", "pa_alloc_create", "pa_alloc_destroy",
             "pa_alloc_add_seq", "pa_alloc_fork", "pa_alloc_append", "pa_alloc_append_batch",
-            "pa_alloc_free_seq", "pa_alloc_discard_seq",
+            "pa_alloc_free_seq", "pa_alloc_discard_seq", "pa_alloc_share_groups",
+            "pa_decode_shared", "pa_decode_shared_workspace_bytes", "pa_bench_stream_read",
             "pa_alloc_block_tables", "pa_alloc_num_free", "pa_alloc_refcount",
             "pa_alloc_seq_len", "pa_alloc_seq_num_blocks", "pa_alloc_add_seq_tokens",
             "pa_alloc_append_tokens", "pa_alloc_num_cached", "pa_alloc_num_evictable",
@@ -259,6 +265,62 @@ def pa_decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens, scal
 
 def pa_decode_noalloc_scratch_bytes() -> int:
     return int(_lib.pa_decode_noalloc_scratch_bytes())
+
+
+def pa_decode_shared_workspace_bytes(num_seqs, num_groups, num_q_heads, num_kv_heads, head_dim,
+                                     block_size, max_context_len, dtype=torch.float16) -> int:
+    return int(_lib.pa_decode_shared_workspace_bytes(num_seqs, num_groups, num_q_heads,
+                                                     num_kv_heads, head_dim, block_size,
+                                                     max_context_len, _DTYPE[dtype]))
+
+
+def pa_decode_shared(out, q, k_cache, v_cache, block_tables, context_lens, group_start,
+                     group_prefix_len, scale, block_size, num_kv_heads, max_context_len,
+                     workspace=None, stream=None):
+    """pa_decode for groups of consecutive sequences sharing their leading
+    blocks (see pa.h): group_start int32 [G+1], group_prefix_len int32 [G]
+    (device tensors, e.g. from BlockAllocator.share_groups)."""
+    B, hq, D = q.shape
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q in shape and dtype")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("pools must have q's dtype")
+    nb = _check_pools(k_cache, v_cache, num_kv_heads, block_size, D)
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("block_tables and context_lens must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_tables must be [num_seqs, max_blocks], context_lens [num_seqs]")
+    G = group_prefix_len.shape[0]
+    if group_start.dtype != torch.int32 or group_prefix_len.dtype != torch.int32 or \
+            tuple(group_start.shape) != (G + 1,):
+        raise ValueError("group_start must be int32 [G+1], group_prefix_len int32 [G]")
+    dt = _dtype_code(q)
+    ws_bytes = int(_lib.pa_decode_shared_workspace_bytes(B, G, hq, num_kv_heads, D, block_size,
+                                                         max_context_len, dt))
+    if ws_bytes and workspace is None:
+        workspace = _scratch(ws_bytes, q.device, stream)
+    ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_lib.pa_decode_shared(_dev_ptr(out, "out"), _dev_ptr(q, "q"),
+                                 _dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"),
+                                 _dev_ptr(block_tables, "block_tables"),
+                                 _dev_ptr(context_lens, "context_lens"), float(scale), block_size,
+                                 num_kv_heads, B, hq, D, block_tables.shape[1],
+                                 int(max_context_len), nb, dt,
+                                 _dev_ptr(group_start, "group_start"),
+                                 _dev_ptr(group_prefix_len, "group_prefix_len"), G, ws_ptr,
+                                 ws_len, _stream(stream)))
+    return out
+
+
+def bench_stream_read(buf, sink, workgroups, stream=None):
+    """Measurement helper (include/pa_bench.h): read every byte of the device
+    tensor ``buf`` once with 16-byte non-temporal loads; ``sink`` a uint32
+    device tensor of workgroups * 256 entries."""
+    if sink.numel() < workgroups * 256 or sink.dtype != torch.int32 and sink.dtype != torch.uint32:
+        raise ValueError("sink must hold workgroups * 256 32-bit entries")
+    _check(_lib.pa_bench_stream_read(_dev_ptr(buf, "buf"), buf.numel() * buf.element_size(),
+                                     _dev_ptr(sink, "sink"), int(workgroups), _stream(stream)))
 
 
 def pa_decode_write(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale,
@@ -460,6 +522,18 @@ class BlockAllocator:
         """free_seq for a sequence whose slots were never written: the prefix
         table entries it created are dropped first (pa_alloc_discard_seq)."""
         _check(_lib.pa_alloc_discard_seq(self._h, seq_id))
+
+    def share_groups(self, seq_ids, max_members: int = 16):
+        """Groups for pa_decode_shared (pa_alloc_share_groups): returns
+        (group_start int32[G+1], group_prefix_len int32[G])."""
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        gs = np.empty(len(ids) + 1, dtype=np.int32)
+        gp = np.empty(max(len(ids), 1), dtype=np.int32)
+        ng = ctypes.c_int32(0)
+        _check(_lib.pa_alloc_share_groups(self._h, ids.ctypes.data_as(ctypes.c_void_p), len(ids),
+                                          max_members, gs.ctypes.data_as(ctypes.c_void_p),
+                                          gp.ctypes.data_as(ctypes.c_void_p), ctypes.byref(ng)))
+        return gs[:ng.value + 1].copy(), gp[:ng.value].copy()
 
     def block_tables(self, seq_ids, max_blocks: int):
         ids = np.ascontiguousarray(seq_ids, dtype=np.int64)

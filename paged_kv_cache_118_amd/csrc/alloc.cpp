@@ -457,6 +457,46 @@ pa_status pa_alloc_discard_seq(pa_alloc* a, int64_t seq_id) {
   return pa_alloc_free_seq(a, seq_id);
 }
 
+pa_status pa_alloc_share_groups(const pa_alloc* a, const int64_t* seq_ids, int32_t n,
+                                int32_t max_members, int32_t* group_start_out,
+                                int32_t* group_prefix_out, int32_t* num_groups_out) {
+  if (!a || n < 0 || max_members < 1 || !num_groups_out || !group_start_out ||
+      (n > 0 && (!seq_ids || !group_prefix_out)))
+    return PA_EINVAL;
+  std::vector<const pa_alloc::Seq*> seqs((size_t)n);
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = a->seqs.find(seq_ids[i]);
+    if (it == a->seqs.end()) return PA_ENOENT;
+    seqs[(size_t)i] = &it->second;
+  }
+  const int32_t bs = a->block_size;
+  // leading blocks two sequences hold in common and that are full in both
+  auto common = [bs](const pa_alloc::Seq& x, const pa_alloc::Seq& y) {
+    const size_t full = (size_t)(std::min(x.len, y.len) / bs);
+    size_t j = 0;
+    while (j < full && x.blocks[j] == y.blocks[j]) ++j;
+    return (int32_t)j;
+  };
+  int32_t g = 0;
+  for (int32_t i = 0; i < n;) {
+    // group g starts at i; a later sequence joins while it shares the
+    // group's whole prefix with the first member (the first joiner sets it)
+    group_start_out[g] = i;
+    int32_t prefix = 0, j = i + 1;
+    for (; j < n && j - i < max_members; ++j) {
+      const int32_t c = common(*seqs[(size_t)i], *seqs[(size_t)j]);
+      if (c == 0 || (j > i + 1 && c < prefix)) break;
+      if (j == i + 1) prefix = c;
+    }
+    group_prefix_out[g] = prefix * bs;
+    ++g;
+    i = j;
+  }
+  group_start_out[g] = n;
+  *num_groups_out = g;
+  return PA_OK;
+}
+
 pa_status pa_alloc_block_tables(const pa_alloc* a, const int64_t* seq_ids, int32_t n,
                                 int32_t max_blocks, int32_t* tables_out, int32_t* lens_out) {
   if (!a || n < 0 || max_blocks < 0 || (n > 0 && (!seq_ids || !lens_out))) return PA_EINVAL;

@@ -40,7 +40,7 @@ int device_lds_per_cu() {
   return v;
 }
 
-int waves_per_cu(bool mfma, pa_dtype dt, int head_dim, int num_seqs) {
+int waves_per_cu(bool mfma, pa_dtype dt, int head_dim, size_t lds_bytes) {
   static int cache[2][3][5] = {};
   int dsel = head_dim == 64 ? 0 : head_dim == 128 ? 1 : head_dim == 256 ? 2 : 3;
   if (dsel > 2) dsel = 3;
@@ -50,7 +50,7 @@ int waves_per_cu(bool mfma, pa_dtype dt, int head_dim, int num_seqs) {
              : std::min(kValuWorkersPerCu, decode_valu_waves_per_cu(dt, head_dim));
   // resident workgroups are also bounded by the LDS the split keeps per workgroup
   static const int lds_cu = device_lds_per_cu();
-  const int by_lds = (int)(lds_cu / split_lds_bytes(num_seqs)) * kWavesPerWorkgroup;
+  const int by_lds = (int)(lds_cu / std::max<size_t>(lds_bytes, 1)) * kWavesPerWorkgroup;
   return std::max(kWavesPerWorkgroup, std::min(x, by_lds));
 }
 
@@ -125,12 +125,58 @@ Plan make_plan(int num_seqs, int hq, int hkv, int head_dim, int block_size, int 
     return p;
   }
   p.part_steps = partition_size > 0 ? std::max(1, partition_size / p.step) : 0;
-  p.num_workers = device_cus() * waves_per_cu(p.path == Path::kMfma, dt, head_dim, num_seqs);
+  p.num_workers =
+      device_cus() * waves_per_cu(p.path == Path::kMfma, dt, head_dim, split_lds_bytes(num_seqs));
   const size_t slots = (size_t)(items + p.num_workers);  // partial of item i by worker w: i + w
   p.pre_off = round_up(slots * part_record(p.rows_per_item, head_dim) * 4, 256);
   p.ppre_off = p.pre_off + round_up(((size_t)num_seqs + 1) * 4, 256);
   p.ws_bytes = p.ppre_off + round_up(((size_t)num_seqs + 1) * 4, 256);
   return p;
+}
+
+// ----------------------------------------------------- shared-prefix plan --
+// pa_decode_shared: the tail pass uses the token-balanced split of a plain
+// decode (with the larger LDS of its scan), the prefix pass its own split
+// over (group, kv head) items with 16-row records; the workspace holds the
+// tail split's, then the prefix records, the prefix step prefixes and the
+// group of each sequence.
+struct CascadePlan {
+  bool ok;  // false: the plain decode runs instead
+  Plan tail;
+  int p_workers;
+  size_t p_off, p_pre_off, grp_off, ws_bytes;
+};
+
+bool prefix_pass_supported(pa_dtype dt, int head_dim, int block_size, int group) {
+  return (dt == PA_F16 || dt == PA_BF16) && (head_dim == 64 || head_dim == 128) &&
+         (block_size == 8 || block_size == 16 || block_size % 32 == 0) && group <= kPrefixRows;
+}
+
+CascadePlan make_cascade_plan(int num_seqs, int num_groups, int hq, int hkv, int head_dim,
+                              int block_size, int len_cap, pa_dtype dt) {
+  CascadePlan c{};
+  c.tail = make_plan(num_seqs, hq, hkv, head_dim, block_size, len_cap, 0, dt);
+  c.ok = num_groups > 0 && c.tail.split && num_groups <= num_seqs &&
+         prefix_pass_supported(dt, head_dim, block_size, hq / hkv);
+  if (!c.ok) {
+    c.ws_bytes = c.tail.ws_bytes;
+    return c;
+  }
+  // the tail pass's workers, sized with its larger LDS
+  c.tail.num_workers = device_cus() * waves_per_cu(c.tail.path == Path::kMfma, dt, head_dim,
+                                                   cascade_lds_bytes(num_seqs, num_groups));
+  const size_t slots = (size_t)num_seqs * c.tail.items_per_seq + c.tail.num_workers;
+  c.tail.pre_off = round_up(slots * part_record(c.tail.rows_per_item, head_dim) * 4, 256);
+  c.tail.ppre_off = c.tail.pre_off + round_up(((size_t)num_seqs + 1) * 4, 256);
+  c.tail.ws_bytes = c.tail.ppre_off + round_up(((size_t)num_seqs + 1) * 4, 256);
+  const size_t p_lds = split_lds_bytes(num_groups) + sizeof(int) * (2 * (size_t)num_groups + 1);
+  c.p_workers = device_cus() * waves_per_cu(true, dt, head_dim, p_lds);
+  const size_t p_slots = (size_t)num_groups * hkv + c.p_workers;
+  c.p_off = c.tail.ws_bytes;
+  c.p_pre_off = c.p_off + round_up(p_slots * part_record(kPrefixRows, head_dim) * 4, 256);
+  c.grp_off = c.p_pre_off + round_up(((size_t)num_groups + 1) * 4, 256);
+  c.ws_bytes = c.grp_off + round_up((size_t)num_seqs * 4, 256);
+  return c;
 }
 
 // True when a kernel may dereference p: device memory, or pinned host memory
@@ -358,6 +404,125 @@ pa_status pa_decode_write(void* out, const void* q, const void* k_new, const voi
                      context_lens, scale, block_size, num_kv_heads, num_seqs, num_q_heads,
                      head_dim, max_blocks_per_seq, max_context_len, num_blocks, dtype,
                      partition_size, workspace, workspace_bytes, stream);
+}
+
+size_t pa_decode_shared_workspace_bytes(int32_t num_seqs, int32_t num_groups,
+                                        int32_t num_q_heads, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t block_size,
+                                        int32_t max_context_len, pa_dtype dtype) {
+  if (num_seqs <= 0 || num_groups < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      head_dim <= 0 || max_context_len <= 0)
+    return 0;
+  return make_cascade_plan(num_seqs, num_groups, num_q_heads, num_kv_heads, head_dim, block_size,
+                           max_context_len, dtype)
+      .ws_bytes;
+}
+
+pa_status pa_decode_shared(void* out, const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_tables, const int32_t* context_lens, float scale,
+                           int32_t block_size, int32_t num_kv_heads, int32_t num_seqs,
+                           int32_t num_q_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                           int32_t max_context_len, int64_t num_blocks, pa_dtype dtype,
+                           const int32_t* group_start, const int32_t* group_prefix_len,
+                           int32_t num_groups, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  if (num_groups < 0 || num_seqs < 0 || num_kv_heads <= 0 || num_q_heads <= 0 ||
+      block_size <= 0 || max_blocks_per_seq < 0 || max_context_len < 0)
+    return PA_EINVAL;
+  if (num_groups > 0 && (!group_start || !group_prefix_len)) return PA_EINVAL;
+  const int len_cap = (int)std::min<int64_t>((int64_t)max_context_len,
+                                             (int64_t)max_blocks_per_seq * block_size);
+  const CascadePlan sized =
+      make_cascade_plan(std::max(num_seqs, 1), num_groups, num_q_heads, num_kv_heads, head_dim,
+                        block_size, max_context_len, dtype);
+  const CascadePlan c = make_cascade_plan(std::max(num_seqs, 1), num_groups, num_q_heads,
+                                          num_kv_heads, head_dim, block_size, len_cap, dtype);
+  if (num_seqs == 0 || !c.ok || num_groups > num_seqs)  // no prefix pass: a plain decode
+    return pa::decode_impl(out, q, nullptr, nullptr, 0, k_cache, v_cache, block_tables,
+                           context_lens, scale, block_size, num_kv_heads, num_seqs, num_q_heads,
+                           head_dim, max_blocks_per_seq, max_context_len, num_blocks, dtype, 0,
+                           workspace, workspace_bytes, stream);
+  // the checks of pa_decode, then the groups'
+  if (!dtype_ok(dtype)) return PA_ENOTSUP;
+  if (num_q_heads % num_kv_heads != 0 || !std::isfinite(scale) || num_blocks <= 0)
+    return PA_EINVAL;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_EINVAL;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    return PA_EINVAL;
+  if (c.ws_bytes > sized.ws_bytes) return PA_EINVAL;  // cannot happen: len_cap <= max
+  if (!workspace || workspace_bytes < c.ws_bytes || !aligned16(workspace)) return PA_EINVAL;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int group = num_q_heads / num_kv_heads;
+  if (validate_enabled()) {
+    std::vector<int32_t> lens, tab, gs, gp;
+    if (!copy_to_host(lens, context_lens, (size_t)num_seqs, s) ||
+        !copy_to_host(tab, block_tables, (size_t)num_seqs * max_blocks_per_seq, s) ||
+        !copy_to_host(gs, group_start, (size_t)num_groups + 1, s) ||
+        !copy_to_host(gp, group_prefix_len, (size_t)num_groups, s))
+      return PA_EHIP;
+    for (int b = 0; b < num_seqs; ++b) {
+      if (lens[b] < 0 || lens[b] > len_cap) return PA_EVALIDATE;
+      const int nb = (lens[b] + block_size - 1) / block_size;
+      for (int j = 0; j < nb; ++j) {
+        const int32_t e = tab[(size_t)b * max_blocks_per_seq + j];
+        if (e < 0 || e >= num_blocks) return PA_EVALIDATE;
+      }
+    }
+    if (gs[0] != 0 || gs[num_groups] != num_seqs) return PA_EVALIDATE;
+    for (int g = 0; g < num_groups; ++g) {
+      const int m = gs[g + 1] - gs[g];
+      if (m < 1 || m * group > kPrefixRows) return PA_EVALIDATE;
+      if (gp[g] < 0 || gp[g] % block_size != 0) return PA_EVALIDATE;
+      const int nb = gp[g] / block_size;
+      for (int b = gs[g]; b < gs[g + 1]; ++b) {
+        if (lens[b] < gp[g]) return PA_EVALIDATE;
+        for (int j = 0; j < nb; ++j)
+          if (tab[(size_t)b * max_blocks_per_seq + j] != tab[(size_t)gs[g] * max_blocks_per_seq + j])
+            return PA_EVALIDATE;
+      }
+    }
+  }
+  DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.scale_log2e = scale * 1.4426950408889634f;
+  a.block_size = block_size;
+  a.num_kv_heads = num_kv_heads;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.head_dim = head_dim;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.len_cap = len_cap;
+  a.num_blocks = num_blocks;
+  a.split = 1;
+  a.part_steps = 0;
+  a.num_workers = c.tail.num_workers;
+  char* base = static_cast<char*>(workspace);
+  a.ws_part = reinterpret_cast<float*>(base);
+  a.ws_pre = reinterpret_cast<int32_t*>(base + c.tail.pre_off);
+  a.ws_ppre = reinterpret_cast<int32_t*>(base + c.tail.ppre_off);
+  a.group_start = group_start;
+  a.group_prefix = group_prefix_len;
+  a.num_groups = num_groups;
+  a.ws_grp = reinterpret_cast<int32_t*>(base + c.grp_off);
+  a.pws_part = reinterpret_cast<float*>(base + c.p_off);
+  a.pws_pre = reinterpret_cast<int32_t*>(base + c.p_pre_off);
+  a.p_num_workers = c.p_workers;
+  // prefix pass: its own split and records
+  DecodeArgs pa_ = a;
+  pa_.num_workers = c.p_workers;
+  pa_.ws_part = a.pws_part;
+  pa_.ws_pre = a.pws_pre;
+  pa_.ws_ppre = a.pws_pre;  // unused (no partitions)
+  hipError_t e = launch_decode_prefix(pa_, dtype, s);
+  if (e != hipSuccess) return PA_EHIP;
+  e = c.tail.path == Path::kMfma ? launch_decode_mfma(a, dtype, s) : launch_decode_valu(a, dtype, s);
+  if (e != hipSuccess) return PA_EHIP;
+  return hip_status(launch_cascade_merge(a, dtype, c.tail.items_per_seq, s));
 }
 
 pa_status pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,

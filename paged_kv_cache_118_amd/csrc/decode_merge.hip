@@ -73,6 +73,44 @@ __device__ __forceinline__ float merge_output(const DecodeArgs& a, SlotOf slot_o
   return acc / Lt;
 }
 
+// Running (max, sum, output) of one output element while pieces are folded in.
+struct MergeState {
+  float M, Lt, acc;
+};
+
+// Folds K pieces into st: piece k is the record at slot_of(k) of `part`, with
+// records of RR rows; this element is row r, dim d.
+template <typename SlotOf>
+__device__ __forceinline__ void fold_pieces(MergeState& st, const float* part, SlotOf slot_of,
+                                            int K, int RR, int r, int d, int D) {
+  const int od = ((d >> 4) * 4 + ((d & 15) >> 2)) * RR * 4 + r * 4 + (d & 3);
+  const int RS = part_record(RR, D);
+  for (int k0 = 0; k0 < K; k0 += kBatch) {
+    float m[kBatch], l[kBatch], o[kBatch];
+#pragma unroll
+    for (int w = 0; w < kBatch; ++w) {
+      const bool ok = k0 + w < K;
+      const float* rec = part + (int64_t)slot_of(ok ? k0 + w : k0) * RS;
+      m[w] = ok ? rec[RR * D + r] : -INFINITY;
+      l[w] = ok ? rec[RR * D + 16 + r] : 0.f;
+      o[w] = ok ? rec[od] : 0.f;
+    }
+    float Mn = st.M;
+#pragma unroll
+    for (int w = 0; w < kBatch; ++w) Mn = fmaxf(Mn, m[w]);
+    const float sc = st.M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st.M - Mn);
+    st.Lt *= sc;
+    st.acc *= sc;
+#pragma unroll
+    for (int w = 0; w < kBatch; ++w) {
+      const float f = m[w] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[w] - Mn);
+      st.Lt += f * l[w];
+      st.acc += f * o[w];
+    }
+    st.M = Mn;
+  }
+}
+
 template <typename TT>
 __device__ __forceinline__ float elem(const void* base, int64_t i) {
   if constexpr (TT::bytes == 4)
@@ -193,6 +231,61 @@ __global__ __launch_bounds__(1024) void decode_merge_kernel(DecodeArgs a, int H,
   store_token();
 }
 
+// pa_decode_shared: one workgroup per output item (b, h) of the tail pass,
+// one thread per output (row r, dim d).  The row's pieces are the tail
+// pass's partials of the item (its workers F .. F+K-1), and, when b's group
+// has a shared prefix, the prefix pass's partials of item (group, kv head)
+// at row (b - first member) * G + q head % G of their 16-row records; all
+// share one denominator after rescaling to the common maximum (the Z / o
+// equations of wq-win.github.io "079 | vLLM 与 PagedAttention", section 二).
+template <typename TT>
+__global__ __launch_bounds__(1024) void cascade_merge_kernel(DecodeArgs a, int H, int R) {
+  const int D = a.head_dim, B = a.num_seqs, NG = a.num_groups;
+  const int item = blockIdx.x;
+  const int b = item / H, h = item - b * H;
+  const int Gq = a.num_q_heads / a.num_kv_heads;
+  const int kvh = R == 1 ? h / Gq : h;
+  const int* pre = a.ws_pre;
+  const int* ppre = a.pws_pre;
+  const int n = (pre[b + 1] - pre[b]) / H;  // tail steps of the item
+  const int g = min(max(a.ws_grp[b], 0), NG - 1);
+  const int first = min(max(a.group_start[g], 0), B - 1);
+  const int np = (ppre[g + 1] - ppre[g]) / a.num_kv_heads;  // prefix steps per kv head
+  const int64_t orow0 = ((int64_t)b * a.num_q_heads + (int64_t)h * R) * D;
+  const int total = R * D;
+  if (n == 0 && np == 0) {  // empty sequence: zero rows
+    for (int t = threadIdx.x; t < total; t += blockDim.x) store_out<TT>(a.out, orow0 + t, 0.f);
+    return;
+  }
+  int F = 0, K = 0;
+  if (n > 0) {
+    const Split sp = make_split(a.num_workers, pre[B], 0, H, B, pre, nullptr);
+    const int64_t S = pre[b] + (int64_t)h * n, E = S + n;
+    F = sp.worker_of(S);
+    const int Lw = sp.worker_of(E - 1);
+    if (np == 0 && F == Lw) return;  // no prefix, one piece: the tail pass wrote the row
+    K = Lw - F + 1;
+  }
+  int Fp = 0, Kp = 0;
+  if (np > 0) {
+    const Split pp = make_split(a.p_num_workers, ppre[NG], 0, a.num_kv_heads, NG, ppre, nullptr);
+    const int64_t S = ppre[g] + (int64_t)kvh * np, E = S + np;
+    Fp = pp.worker_of(S);
+    Kp = pp.worker_of(E - 1) - Fp + 1;
+  }
+  const int base = item + F, pbase = g * a.num_kv_heads + kvh + Fp;
+  for (int t = threadIdx.x; t < total; t += blockDim.x) {
+    const int r = t / D, d = t - r * D;
+    MergeState st{-INFINITY, 0.f, 0.f};
+    fold_pieces(st, a.ws_part, [base](int k) { return base + k; }, K, R, r, d, D);
+    const int rp = (b - first) * Gq + (R == 1 ? h % Gq : r);  // row in the prefix records
+    if (rp >= 0 && rp < kPrefixRows)
+      fold_pieces(st, a.pws_part, [pbase](int k) { return pbase + k; }, Kp, kPrefixRows, rp, d,
+                  D);
+    store_out<TT>(a.out, orow0 + t, st.acc / st.Lt);
+  }
+}
+
 // The store alone, for a pa_decode_write whose decode runs unsplit (the
 // plain kernel then reads the token from the pool): one workgroup per
 // (sequence, kv head), one thread per element.
@@ -249,6 +342,28 @@ hipError_t launch_decode_merge(const DecodeArgs& a, pa_dtype dt, int items_per_s
       else
         hipLaunchKernelGGL((decode_merge_kernel<BF16, false>), grid, dim3(threads), 0, s, a,
                            items_per_seq, R);
+      break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_cascade_merge(const DecodeArgs& a, pa_dtype dt, int items_per_seq,
+                                hipStream_t s) {
+  if (a.num_seqs == 0) return hipSuccess;
+  const int R = a.num_q_heads / items_per_seq;
+  const int outputs = R * a.head_dim;
+  const int threads = outputs >= 1024 ? 1024 : (outputs + 63) / 64 * 64;
+  dim3 grid(a.num_seqs * items_per_seq);
+  switch (dt) {
+    case PA_F32:
+      hipLaunchKernelGGL(cascade_merge_kernel<F32>, grid, dim3(threads), 0, s, a, items_per_seq, R);
+      break;
+    case PA_F16:
+      hipLaunchKernelGGL(cascade_merge_kernel<F16>, grid, dim3(threads), 0, s, a, items_per_seq, R);
+      break;
+    case PA_BF16:
+      hipLaunchKernelGGL(cascade_merge_kernel<BF16>, grid, dim3(threads), 0, s, a, items_per_seq,
+                         R);
       break;
   }
   return hipGetLastError();

@@ -93,7 +93,15 @@ struct TableWindow {
 // left out here -- the stream covers positions 0 .. L-2 -- and every segment
 // is written as a partial, which the merge kernel combines with the new
 // token's own term (fold_in_merge).
-template <typename TT, int D, bool FOLD>
+//
+// CASC (pa_decode_shared): 1 = tail pass, as in decode_valu.hip (each
+// sequence's steps start after its group's shared prefix; such sequences end
+// in partials); 2 = prefix pass: items are (group, kv head), the group's
+// shared prefix is the context, and the item's rows are the members' q heads
+// of that kv head -- member m, q head h*G + i is row m*G + i (at most 16
+// rows) -- so each shared block is read once for all of them; every segment
+// ends in a 16-row partial for the merge.
+template <typename TT, int D, bool FOLD, int CASC>
 __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int VS = 8;       // V slab width (tokens)
   constexpr int EB = 2;
@@ -105,7 +113,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeArgs a) 
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int worker = blockIdx.x * kWaves + wv;
   const int n = lane & 15, kb = lane >> 4;
-  const int H = a.num_kv_heads, B = a.num_seqs;
+  // the items' first index runs over sequences, or over groups (prefix pass)
+  const int H = a.num_kv_heads, B = CASC == 2 ? a.num_groups : a.num_seqs;
   const int G = a.num_q_heads / a.num_kv_heads;
   const int bs = a.block_size;
   const int64_t hkv = a.num_kv_heads;
@@ -113,29 +122,51 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeArgs a) 
   int* s_pre = smem;
   int* s_len = smem + B + 1;
   int* s_ppre = smem + 2 * B + 1;
+  // CASC 1: first position and group of each sequence; both passes: group
+  // starts and prefix lengths
+  int* s_st = smem + 3 * B + 2;
+  int* s_grp = s_st + B;
+  int* s_gs = CASC == 2 ? smem + 3 * B + 2 : s_grp + B;
+  int* s_gp = s_gs + a.num_groups + 1;
+  constexpr int RR = CASC == 2 ? kPrefixRows : 0;  // record rows (0: the group G)
 
   Cursor c0;
   int count;
   Split sp{};
   int64_t x0 = 0;  // split 1: first stream step of this worker
   if (a.split) {
-    if (wv == 0)
-      wave_scan_steps(a.context_lens, B, H, a.len_cap, FOLD ? 1 : 0, kGroup, C, s_pre, s_len,
-                      s_ppre);
+    if constexpr (CASC != 0) {
+      if (wv == 0) load_groups(a, s_gs, s_gp);
+      __syncthreads();
+    }
+    if (wv == 0) {
+      if constexpr (CASC == 1)
+        wave_scan_tail(a, s_gs, s_gp, H, kGroup, s_pre, s_len, s_st, s_grp);
+      else if constexpr (CASC == 2)  // the groups' prefixes are the contexts
+        wave_scan_steps(s_gp, B, H, a.len_cap, 0, kGroup, 0, s_pre, s_len, s_ppre);
+      else
+        wave_scan_steps(a.context_lens, B, H, a.len_cap, FOLD ? 1 : 0, kGroup, C, s_pre, s_len,
+                        s_ppre);
+    }
     __syncthreads();
-    if (blockIdx.x == 0 && wv == 0) export_prefixes(s_pre, s_ppre, B, C, a.ws_pre, a.ws_ppre);
+    if (blockIdx.x == 0 && wv == 0) {
+      export_prefixes(s_pre, s_ppre, B, C, a.ws_pre, a.ws_ppre);
+      if constexpr (CASC == 1)
+        for (int j = lane; j < B; j += 64) a.ws_grp[j] = s_grp[j];
+    }
     const int N = s_pre[B];  // empty sequences get their zero rows from the merge
     if (N == 0) return;
     sp = make_split(a.num_workers, N, C, H, B, s_pre, s_ppre);
     if (worker >= sp.W) return;
     x0 = sp.start(worker);
     count = (int)(sp.start(worker + 1) - x0);
-    c0 = locate(s_pre, s_len, B, H, kGroup, (int)x0);
+    c0 = locate(s_pre, s_len, CASC == 1 ? s_st : nullptr, B, H, kGroup, (int)x0);
   } else {
     if (worker >= B * H) return;
     c0.b = worker / H;
     c0.h = worker % H;
     c0.k = 0;
+    c0.s = 0;
     c0.L = clamp_len(a.context_lens[c0.b], a.len_cap);
     c0.n = (c0.L + kGroup - 1) / kGroup;
     count = c0.n;
@@ -151,6 +182,30 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeArgs a) 
     x.k = __builtin_amdgcn_readfirstlane(x.k);
     x.n = __builtin_amdgcn_readfirstlane(x.n);
     x.L = __builtin_amdgcn_readfirstlane(x.L);
+    x.s = __builtin_amdgcn_readfirstlane(x.s);
+  };
+  // The sequence whose table and q rows an item uses (the group's first
+  // member in the prefix pass), the q head of its row r, and its rows.
+  // (Group starts are clamped to [0, num_seqs]; the first member to a real
+  // sequence, so that malformed groups still read inside q and the tables.)
+  auto seq_of = [&](const Cursor& cu) -> int {
+    if constexpr (CASC == 2)
+      return min(s_gs[cu.b], a.num_seqs - 1);
+    else
+      return cu.b;
+  };
+  auto row_head = [&](const Cursor& cu, int r) -> int64_t {
+    if constexpr (CASC == 2)
+      return (int64_t)min(seq_of(cu) + r / G, a.num_seqs - 1) * a.num_q_heads +
+             (int64_t)cu.h * G + r % G;
+    else
+      return (int64_t)cu.b * a.num_q_heads + (int64_t)cu.h * G + r;
+  };
+  auto rows_of = [&](const Cursor& cu) -> int {
+    if constexpr (CASC == 2)
+      return min(kPrefixRows, max(s_gs[cu.b + 1] - s_gs[cu.b], 0) * G);
+    else
+      return G;
   };
   uniform(c0);
 
@@ -175,21 +230,20 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeArgs a) 
   // tile, or the item's first q row), so they cost no HBM traffic while the
   // number of loads, and so every wait count, stays fixed.
   auto cached_addr = [&](const Cursor& cu) {
-    const int64_t head0 = (int64_t)cu.b * a.num_q_heads + (int64_t)cu.h * G;
-    return qbase + head0 * D * EB + ((lane * 16) & (D * EB - 1));
+    return qbase + row_head(cu, 0) * D * EB + ((lane * 16) & (D * EB - 1));
   };
   auto issue_k = [&](const Cursor& cu, uint4 (&kr)[2][KN], uint4 (&qr)[KN], int& qitem,
                      bool live) {
     const int item = cu.item(H);
     if (qitem != item) {
       qitem = item;
-      const int64_t head = (int64_t)cu.b * a.num_q_heads + (int64_t)cu.h * G + n;
-      const char* qp = qbase + (head * D + kb * 8) * EB;
+      const bool row = n < rows_of(cu);
+      const char* qp = qbase + (row_head(cu, row ? n : 0) * D + kb * 8) * EB;
 #pragma unroll
-      for (int s = 0; s < KN; ++s) qr[s] = n < G ? ld16(qp + 64 * s) : make_uint4(0, 0, 0, 0);
+      for (int s = 0; s < KN; ++s) qr[s] = row ? ld16(qp + 64 * s) : make_uint4(0, 0, 0, 0);
     }
-    const int32_t* trow = a.block_tables + (int64_t)cu.b * a.max_blocks_per_seq;
-    const int tok = cu.k * kGroup;
+    const int32_t* trow = a.block_tables + (int64_t)seq_of(cu) * a.max_blocks_per_seq;
+    const int tok = cu.tok(kGroup);
     const int lb0 = tok / bs;
     if (tw_b != cu.b) {
       tw_b = cu.b;
@@ -215,7 +269,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeArgs a) 
   // The V token run of k-group kb (8 tokens of one slab row per d tile).  Its
   // group's K was issued earlier, so the table window already covers it.
   auto issue_v = [&](const Cursor& cu, uint4 (&vr)[MT], bool live) {
-    const int tok = cu.k * kGroup;
+    const int tok = cu.tok(kGroup);
     const int lb0 = tok / bs;
     const bool run = live && kb * 8 < cu.L - tok;  // this k-group's 8 tokens hold data
     const int t = tok + kb * 8;
@@ -248,7 +302,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeArgs a) 
       for (int mt = 0; mt < MT; ++mt) acc[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
       seg_k0 = cu.k;
     }
-    nvalid = min(kGroup, cu.L - cu.k * kGroup);
+    nvalid = min(kGroup, cu.L - cu.tok(kGroup));
     float4_t st[2];
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) {
@@ -326,7 +380,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeArgs a) 
       float l_tot = l_lane + __shfl_xor(l_lane, 16);
       l_tot += __shfl_xor(l_tot, 32);
       const int64_t orow0 = (int64_t)cu.b * a.num_q_heads + (int64_t)cu.h * G;
-      if (!FOLD && seg_k0 == 0 && cu.k == cu.n - 1) {  // the whole item: final rows
+      if (!FOLD && CASC != 2 && (CASC == 0 || cu.s == 0) && seg_k0 == 0 &&
+          cu.k == cu.n - 1) {  // the whole item: final rows
         if (n < G) {
           const int64_t orow = (orow0 + n) * D;
           const float inv = 1.f / l_tot;
@@ -341,20 +396,21 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeArgs a) 
         // write one contiguous run of 64 G bytes; then the 128-byte m / l
         // line, written whole (lanes kb = 2, 3 write its zero half).
         const int64_t slot = (int64_t)cu.item(H) + worker;
-        float* rec = a.ws_part + slot * part_record(G, D);
-        if (n < G) {
-          float* o = rec + (kb * G + n) * 4;
+        const int rr = RR ? RR : G, nr = rows_of(cu);
+        float* rec = a.ws_part + slot * part_record(rr, D);
+        if (n < nr) {
+          float* o = rec + (kb * rr + n) * 4;
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt) *reinterpret_cast<float4_t*>(o + mt * 16 * G) = acc[mt];
+          for (int mt = 0; mt < MT; ++mt) *reinterpret_cast<float4_t*>(o + mt * 16 * rr) = acc[mt];
         }
-        if (lane < 32) rec[G * D + lane] = (lane & 15) < G ? (lane < 16 ? m_run : l_tot) : 0.f;
+        if (lane < 32) rec[rr * D + lane] = (lane & 15) < nr ? (lane < 16 ? m_run : l_tot) : 0.f;
       }
     }
   };
 
   auto next = [&](Cursor& c, int idx) {  // cursor of group idx, given idx-1's
     if (idx < count) {
-      advance(c, s_pre, s_len, H, kGroup);
+      advance(c, s_pre, s_len, CASC == 1 ? s_st : nullptr, H, kGroup);
       uniform(c);
     }
   };
@@ -402,18 +458,31 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeArgs a) 
 
 template <typename TT, int D>
 const void* mfma_fn() {
-  return reinterpret_cast<const void*>(&decode_mfma_kernel<TT, D, false>);
+  return reinterpret_cast<const void*>(&decode_mfma_kernel<TT, D, false, 0>);
 }
 
 template <typename TT, int D>
 hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
   dim3 grid((a.num_workers + kWaves - 1) / kWaves);
-  if (a.k_new)
-    hipLaunchKernelGGL((decode_mfma_kernel<TT, D, true>), grid, dim3(kThreads),
+  if (a.num_groups > 0)
+    hipLaunchKernelGGL((decode_mfma_kernel<TT, D, false, 1>), grid, dim3(kThreads),
+                       decode_split_lds(a), s, a);
+  else if (a.k_new)
+    hipLaunchKernelGGL((decode_mfma_kernel<TT, D, true, 0>), grid, dim3(kThreads),
                        decode_split_lds(a), s, a);
   else
-    hipLaunchKernelGGL((decode_mfma_kernel<TT, D, false>), grid, dim3(kThreads),
+    hipLaunchKernelGGL((decode_mfma_kernel<TT, D, false, 0>), grid, dim3(kThreads),
                        decode_split_lds(a), s, a);
+  return hipGetLastError();
+}
+
+// The prefix pass of a shared-prefix decode: a.num_workers, a.ws_part and
+// a.ws_pre are the pass's own (the caller swaps them in).
+template <typename TT, int D>
+hipError_t launch_prefix_d(const DecodeArgs& a, hipStream_t s) {
+  dim3 grid((a.num_workers + kWaves - 1) / kWaves);
+  const size_t lds = split_lds_bytes(a.num_groups) + sizeof(int) * (2 * (size_t)a.num_groups + 1);
+  hipLaunchKernelGGL((decode_mfma_kernel<TT, D, false, 2>), grid, dim3(kThreads), lds, s, a);
   return hipGetLastError();
 }
 
@@ -443,6 +512,15 @@ int decode_mfma_waves_per_cu(pa_dtype dt, int head_dim) {
       blocks <= 0)
     return kWaves;
   return blocks * kWaves;
+}
+
+hipError_t launch_decode_prefix(const DecodeArgs& a, pa_dtype dt, hipStream_t s) {
+  if (a.num_groups == 0) return hipSuccess;
+  if (dt == PA_F16) return a.head_dim == 64 ? launch_prefix_d<F16, 64>(a, s)
+                                            : launch_prefix_d<F16, 128>(a, s);
+  if (dt == PA_BF16) return a.head_dim == 64 ? launch_prefix_d<BF16, 64>(a, s)
+                                             : launch_prefix_d<BF16, 128>(a, s);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, pa_dtype dt, hipStream_t s) {

@@ -38,9 +38,12 @@ __device__ __forceinline__ int clamp_len(int L, int cap) { return L < 0 ? 0 : (L
 // encoding).
 constexpr int kVmcntZero = 0x0F70;
 
-// Dynamic LDS a decode launch with these arguments needs.
+// Dynamic LDS a decode launch with these arguments needs (the prefix pass of
+// a shared-prefix decode sizes its own: its sequences are the groups).
 inline size_t decode_split_lds(const DecodeArgs& a) {
-  return a.split ? split_lds_bytes(a.num_seqs) : 0;
+  if (!a.split) return 0;
+  return a.num_groups > 0 ? cascade_lds_bytes(a.num_seqs, a.num_groups)
+                          : split_lds_bytes(a.num_seqs);
 }
 
 // Exclusive prefixes over sequences of H * n_b (LDS s_pre[0..B]) and, when
@@ -159,15 +162,20 @@ __device__ __forceinline__ Split make_split(int num_workers, int N, int C = 0, i
   return s;
 }
 
-// Position in the step stream: sequence b, head h, step k of n, length L.
+// Position in the step stream: sequence b, head h, step k of n, length L;
+// the item's steps cover positions s .. L-1 (s > 0 only for the tail pass of
+// a shared-prefix decode, where positions below s are the group's prefix),
+// step k starting at position s + k * STEP.
 struct Cursor {
-  int b, h, k, n, L;
+  int b, h, k, n, L, s;
   __device__ __forceinline__ int item(int H) const { return b * H + h; }
+  __device__ __forceinline__ int tok(int step) const { return s + k * step; }
 };
 
 // Cursor of stream step x: the sequence with s_pre[b] <= x < s_pre[b+1].
-__device__ __forceinline__ Cursor locate(const int* s_pre, const int* s_len, int B, int H,
-                                         int step, int x) {
+// s_st: the first position of each sequence's steps (null: 0).
+__device__ __forceinline__ Cursor locate(const int* s_pre, const int* s_len, const int* s_st,
+                                         int B, int H, int step, int x) {
   int lo = 0, hi = B;  // first index with s_pre[idx] > x, searched in [0, B]
   while (lo < hi) {
     const int mid = (lo + hi) >> 1;
@@ -176,7 +184,8 @@ __device__ __forceinline__ Cursor locate(const int* s_pre, const int* s_len, int
   Cursor c;
   c.b = lo - 1;
   c.L = s_len[c.b];
-  c.n = (c.L + step - 1) / step;
+  c.s = s_st ? s_st[c.b] : 0;
+  c.n = (c.L - c.s + step - 1) / step;
   const int r = x - s_pre[c.b];
   c.h = r / c.n;
   c.k = r - c.h * c.n;
@@ -184,8 +193,8 @@ __device__ __forceinline__ Cursor locate(const int* s_pre, const int* s_len, int
 }
 
 // Next step of the stream (skips empty sequences).
-__device__ __forceinline__ void advance(Cursor& c, const int* s_pre, const int* s_len, int H,
-                                        int step) {
+__device__ __forceinline__ void advance(Cursor& c, const int* s_pre, const int* s_len,
+                                        const int* s_st, int H, int step) {
   if (++c.k < c.n) return;
   c.k = 0;
   if (++c.h < H) return;
@@ -194,7 +203,74 @@ __device__ __forceinline__ void advance(Cursor& c, const int* s_pre, const int* 
     ++c.b;
   } while (s_pre[c.b + 1] == s_pre[c.b]);
   c.L = s_len[c.b];
-  c.n = (c.L + step - 1) / step;
+  c.s = s_st ? s_st[c.b] : 0;
+  c.n = (c.L - c.s + step - 1) / step;
+}
+
+// ----------------------------------------------------------- shared prefix --
+// pa_decode_shared: groups of consecutive sequences, group g = sequences
+// gs[g] .. gs[g+1]-1, whose first gp[g] positions (whole blocks) are the same
+// physical blocks in every member's table.  The prefix pass reads those
+// blocks once per (group, kv head) for all the members' q rows; the tail pass
+// streams each sequence from its group's prefix length on; the merge joins
+// the two partials of every row.
+
+// The prefix length a group's passes use: a whole number of blocks, no more
+// than its first member's length (the caller guarantees every member's; the
+// kernels only keep every access inside the tables).
+__device__ __forceinline__ int group_prefix(const DecodeArgs& a, int g, int L_first) {
+  const int P = clamp_len(a.group_prefix[g], L_first);
+  return P - P % a.block_size;
+}
+
+// Group starts s_gs[0..G] (clamped to [0, B]) and prefix lengths s_gp[0..G-1]
+// into LDS, by one wavefront (the caller publishes them with a barrier).
+__device__ inline void load_groups(const DecodeArgs& a, int* s_gs, int* s_gp) {
+  const int G = a.num_groups, B = a.num_seqs;
+  for (int i = threadIdx.x & 63; i <= G; i += 64) {
+    const int s0 = min(max(a.group_start[i], 0), B);
+    s_gs[i] = s0;
+    if (i < G) s_gp[i] = group_prefix(a, i, clamp_len(a.context_lens[min(s0, B - 1)], a.len_cap));
+  }
+}
+
+// Tail pass scan: as wave_scan_steps (no partitions, no dropped position),
+// with each sequence's first position s_st[b] = its group's prefix length
+// and its group s_grp[b].  s_gs / s_gp as load_groups left them.
+__device__ inline int wave_scan_tail(const DecodeArgs& a, const int* s_gs, const int* s_gp, int H,
+                                     int step, int* s_pre, int* s_len, int* s_st, int* s_grp) {
+  const int B = a.num_seqs, G = a.num_groups;
+  const int lane = threadIdx.x & 63;
+  const int per = (B + 63) / 64;
+  const int j0 = min(lane * per, B), j1 = min(j0 + per, B);
+  int g = 0, hi = G;  // last group with s_gs[g] <= j0
+  while (g < hi) {
+    const int mid = (g + hi + 1) >> 1;
+    if (mid < G && s_gs[mid] <= j0) g = mid; else hi = mid - 1;
+  }
+  int local = 0;
+  for (int j = j0; j < j1; ++j) {
+    while (g + 1 < G && s_gs[g + 1] <= j) ++g;
+    const int L = clamp_len(a.context_lens[j], a.len_cap);
+    const int st = min(s_gp[g], L);
+    s_len[j] = L;
+    s_st[j] = st;
+    s_grp[j] = g;
+    local += H * ((L - st + step - 1) / step);
+  }
+  int incl = local;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  int run = incl - local;
+  for (int j = j0; j < j1; ++j) {
+    s_pre[j] = run;
+    run += H * ((s_len[j] - s_st[j] + step - 1) / step);
+  }
+  if (lane == 63) s_pre[B] = incl;
+  return __shfl(incl, 63);
 }
 
 // The step ends a segment of a worker whose last stream step has index

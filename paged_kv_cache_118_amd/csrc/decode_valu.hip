@@ -195,7 +195,12 @@ struct TableWindow {
 // segment's end (one more online-softmax step of a single key), so a whole
 // item still ends as its final row and a split one as partials that already
 // hold the token.  The merge kernel stores the token into its slot.
-template <typename TT, int D, int NB, bool FOLD>
+//
+// CASC (pa_decode_shared, tail pass): each sequence's steps start after its
+// group's shared prefix (the prefix pass covers that), and a segment of such
+// a sequence is always written as a partial, which the merge joins with the
+// prefix pass's partial of the same row.
+template <typename TT, int D, int NB, bool FOLD, bool CASC>
 __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
   constexpr int EB = TT::bytes;
   constexpr int NK = D * EB / 64;  // uint4 per lane per step, K and V alike
@@ -216,29 +221,44 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
   int* s_pre = smem;
   int* s_len = smem + B + 1;
   int* s_ppre = smem + 2 * B + 1;
+  // CASC: first position and group of each sequence, group starts and prefixes
+  int* s_st = smem + 3 * B + 2;
+  int* s_grp = s_st + B;
+  int* s_gs = s_grp + B;
+  int* s_gp = s_gs + a.num_groups + 1;
 
   Cursor c0;
   int count;
   Split sp{};
   int64_t x0 = 0;  // split 1: first stream step of this worker
   if (a.split) {
-    if (wv == 0)
+    if constexpr (CASC) {
+      if (wv == 0) load_groups(a, s_gs, s_gp);
+      __syncthreads();
+      if (wv == 0) wave_scan_tail(a, s_gs, s_gp, H, kStep, s_pre, s_len, s_st, s_grp);
+    } else if (wv == 0) {
       wave_scan_steps(a.context_lens, B, H, a.len_cap, FOLD ? 1 : 0, kStep, C, s_pre, s_len,
                       s_ppre);
+    }
     __syncthreads();
-    if (blockIdx.x == 0 && wv == 0) export_prefixes(s_pre, s_ppre, B, C, a.ws_pre, a.ws_ppre);
+    if (blockIdx.x == 0 && wv == 0) {
+      export_prefixes(s_pre, s_ppre, B, C, a.ws_pre, a.ws_ppre);
+      if constexpr (CASC)
+        for (int j = lane; j < B; j += 64) a.ws_grp[j] = s_grp[j];
+    }
     const int N = s_pre[B];  // empty sequences get their zero rows from the merge
     if (N == 0) return;
     sp = make_split(a.num_workers, N, C, H, B, s_pre, s_ppre);
     if (worker >= sp.W) return;
     x0 = sp.start(worker);
     count = (int)(sp.start(worker + 1) - x0);
-    c0 = locate(s_pre, s_len, B, H, kStep, (int)x0);
+    c0 = locate(s_pre, s_len, CASC ? s_st : nullptr, B, H, kStep, (int)x0);
   } else {
     if (worker >= B * H) return;
     c0.b = worker / H;
     c0.h = worker % H;
     c0.k = 0;
+    c0.s = 0;
     c0.L = clamp_len(a.context_lens[c0.b], a.len_cap);
     c0.n = (c0.L + kStep - 1) / kStep;
     count = c0.n;
@@ -255,6 +275,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
     x.k = __builtin_amdgcn_readfirstlane(x.k);
     x.n = __builtin_amdgcn_readfirstlane(x.n);
     x.L = __builtin_amdgcn_readfirstlane(x.L);
+    x.s = __builtin_amdgcn_readfirstlane(x.s);
   };
   uniform(c0);
 
@@ -305,7 +326,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
       for (int i = 0; i < NK; ++i) qr[i] = ld16(qp + 64 * i);  // chunks c + 4i
     }
     const int32_t* trow = a.block_tables + (int64_t)cu.b * a.max_blocks_per_seq;
-    const int tok = cu.k * kStep;
+    const int tok = cu.tok(kStep);
     const int lb0 = tok / bs, lb1 = (tok + 8) / bs;
     if (tw_b != cu.b) {
       tw_b = cu.b;
@@ -360,7 +381,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
       for (int r = 0; r < R; ++r) acc[r] = 0.f;
       seg_k0 = cu.k;
     }
-    const int nvalid = min(kStep, cu.L - cu.k * kStep);
+    const int nvalid = min(kStep, cu.L - cu.tok(kStep));
     float d = lane_dot(TT{}, qr, kr);
     d += dpp<0xB1>(d);  // quad_perm [1,0,3,2]
     d += dpp<0x4E>(d);  // quad_perm [2,3,0,1]
@@ -401,7 +422,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
       }
       const float l_tot = wave_sum(l_lane);
       const int item = cu.item(H);
-      if (seg_k0 == 0 && cu.k == cu.n - 1) {  // the whole item: final row
+      if (seg_k0 == 0 && cu.k == cu.n - 1 && (!CASC || cu.s == 0)) {  // whole item: final row
         const int64_t orow = (int64_t)item * D;
 #pragma unroll
         for (int r = 0; r < R; ++r) store_out<TT>(a.out, orow + lane + 64 * r, acc[r] / l_tot);
@@ -436,7 +457,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
     for (int u = 1; u < NB; ++u) {
       cs[u] = cs[u - 1];
       if (j + u < count) {
-        advance(cs[u], s_pre, s_len, H, kStep);
+        advance(cs[u], s_pre, s_len, CASC ? s_st : nullptr, H, kStep);
         uniform(cs[u]);
       }
     }
@@ -452,7 +473,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
     __builtin_amdgcn_s_waitcnt(kVmcntZero);
     cur = cs[NB - 1];
     if (j + NB < count) {
-      advance(cur, s_pre, s_len, H, kStep);
+      advance(cur, s_pre, s_len, CASC ? s_st : nullptr, H, kStep);
       uniform(cur);
     }
   }
@@ -561,18 +582,23 @@ constexpr int valu_batch() {
 
 template <typename TT, int D>
 const void* valu_fn() {
-  return reinterpret_cast<const void*>(&decode_valu_kernel<TT, D, valu_batch<TT, D>(), false>);
+  return reinterpret_cast<const void*>(
+      &decode_valu_kernel<TT, D, valu_batch<TT, D>(), false, false>);
 }
 
 template <typename TT, int D>
 hipError_t launch_valu_d(const DecodeArgs& a, hipStream_t s) {
   dim3 grid((a.num_workers + kWaves - 1) / kWaves);
-  if (a.k_new)
-    hipLaunchKernelGGL((decode_valu_kernel<TT, D, valu_batch<TT, D>(), true>), grid,
-                       dim3(kThreads), decode_split_lds(a), s, a);
+  constexpr int NB = valu_batch<TT, D>();
+  if (a.num_groups > 0)
+    hipLaunchKernelGGL((decode_valu_kernel<TT, D, NB, false, true>), grid, dim3(kThreads),
+                       decode_split_lds(a), s, a);
+  else if (a.k_new)
+    hipLaunchKernelGGL((decode_valu_kernel<TT, D, NB, true, false>), grid, dim3(kThreads),
+                       decode_split_lds(a), s, a);
   else
-    hipLaunchKernelGGL((decode_valu_kernel<TT, D, valu_batch<TT, D>(), false>), grid,
-                       dim3(kThreads), decode_split_lds(a), s, a);
+    hipLaunchKernelGGL((decode_valu_kernel<TT, D, NB, false, false>), grid, dim3(kThreads),
+                       decode_split_lds(a), s, a);
   return hipGetLastError();
 }
 

@@ -131,7 +131,24 @@ struct DecodeArgs {
   const void* v_new;
   int64_t new_stride;
   int32_t fold_in_merge;  // 1: the decode kernel leaves the token's term to the merge
+  // Shared-prefix decode (pa_decode_shared), or num_groups = 0: groups of
+  // consecutive sequences, gs[g] .. gs[g+1]-1, whose first group_prefix[g]
+  // positions are the same physical blocks.  The tail pass streams every
+  // sequence from its group's prefix on and exports each sequence's group
+  // (ws_grp); the prefix pass (its own split: pws_part, pws_pre,
+  // p_num_workers; records of 16 rows) reads each shared block once for the
+  // members' q rows; the merge joins both passes' partials of every row.
+  const int32_t* group_start;
+  const int32_t* group_prefix;
+  int32_t num_groups;
+  int32_t* ws_grp;
+  float* pws_part;
+  int32_t* pws_pre;
+  int32_t p_num_workers;
 };
+
+// Rows of a prefix-pass partial record (members x q heads per kv head).
+constexpr int kPrefixRows = 16;
 
 // ----------------------------------------------------------- prefill args --
 struct PrefillArgs {
@@ -175,6 +192,11 @@ hipError_t launch_decode_generic(const DecodeArgs& a, pa_dtype dt, hipStream_t s
 // worker step of the decode kernel that ran.
 hipError_t launch_decode_merge(const DecodeArgs& a, pa_dtype dt, int items_per_seq,
                                hipStream_t s);
+// pa_decode_shared: the prefix pass (matrix cores; a.num_workers / ws_part /
+// ws_pre must be the pass's own) and the merge of both passes' partials.
+hipError_t launch_decode_prefix(const DecodeArgs& a, pa_dtype dt, hipStream_t s);
+hipError_t launch_cascade_merge(const DecodeArgs& a, pa_dtype dt, int items_per_seq,
+                                hipStream_t s);
 // pa_decode_write with an unsplit decode: store the new tokens first (the
 // decode then reads them from the pool).
 hipError_t launch_store_new_tokens(const DecodeArgs& a, pa_dtype dt, hipStream_t s);
@@ -200,6 +222,11 @@ hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs
 // and partition prefixes and the clamped lengths, 3 * num_seqs + 2 ints.
 __host__ __device__ inline size_t split_lds_bytes(int num_seqs) {
   return sizeof(int) * (3 * (size_t)num_seqs + 2);
+}
+// ... and of a shared-prefix pass: the tail pass adds each sequence's first
+// position and group, both passes the group starts and prefix lengths.
+__host__ __device__ inline size_t cascade_lds_bytes(int num_seqs, int num_groups) {
+  return split_lds_bytes(num_seqs) + sizeof(int) * (2 * (size_t)num_seqs + 2 * (size_t)num_groups + 1);
 }
 
 // Floats per partial record (see DecodeArgs::ws_part); rows <= 16.

@@ -143,6 +143,62 @@ def contiguous_tables(lens, block_size, max_blocks=None):
     return tables, max(1, cursor)
 
 
+def shared_prefix_tables(group_sizes, prefix_blocks, tail_lens, block_size, rng,
+                         pool_factor=1.25):
+    """Tables of consecutive groups of sequences that share leading blocks:
+    group g's members (group_sizes[g] of them, in order) all start with the
+    same prefix_blocks[g] physical blocks (full), then each has its own
+    blocks for its tail_lens[i] further positions.  Physical ids come from a
+    seeded shuffle of a pool of pool_factor x the distinct blocks needed.
+    Returns (tables int32 [B][max_blocks] -1 padded, lens int32 [B],
+    num_blocks, group_start int32 [G+1], group_prefix_len int32 [G])."""
+    group_sizes = [int(x) for x in group_sizes]
+    B = sum(group_sizes)
+    tail_lens = [int(x) for x in tail_lens]
+    assert len(tail_lens) == B and len(prefix_blocks) == len(group_sizes)
+    need = sum(int(p) for p in prefix_blocks) + sum(blocks_needed(t, block_size) for t in tail_lens)
+    num_blocks = max(1, int(math.ceil(pool_factor * need)))
+    perm = list(rng.permutation(num_blocks))
+    lens = np.zeros(B, dtype=np.int32)
+    rows = []
+    b = 0
+    starts = [0]
+    for g, m in enumerate(group_sizes):
+        pre = [int(perm.pop()) for _ in range(int(prefix_blocks[g]))]
+        for _ in range(m):
+            own = [int(perm.pop()) for _ in range(blocks_needed(tail_lens[b], block_size))]
+            rows.append(pre + own)
+            lens[b] = int(prefix_blocks[g]) * block_size + tail_lens[b]
+            b += 1
+        starts.append(b)
+    maxb = max(1, max(len(r) for r in rows))
+    tables = np.full((B, maxb), -1, dtype=np.int32)
+    for i, r in enumerate(rows):
+        tables[i, :len(r)] = r
+    return (tables, lens, num_blocks, np.array(starts, dtype=np.int32),
+            np.array([int(p) * block_size for p in prefix_blocks], dtype=np.int32))
+
+
+def make_shared_case(spec: Spec, group_sizes, prefix_blocks, tail_lens, device="cpu",
+                     poison=True, seed=None):
+    """A decode case on shared_prefix_tables: q, K, V ~ N(0, 1) drawn as in
+    make_decode_case.  The groups travel in extra["group_start"] and
+    extra["group_prefix_len"]."""
+    seed = spec.seed if seed is None else seed
+    rng = np.random.default_rng(seed)
+    tables, lens, nb, gs, gp = shared_prefix_tables(group_sizes, prefix_blocks, tail_lens,
+                                                    spec.block_size, rng, spec.pool_factor)
+    gen = make_generator(seed, device)
+    hq, hkv, D, bs = spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.block_size
+    q = randn((len(lens), hq, D), spec.dtype, gen, device)
+    k = randn(k_pool_shape(nb, hkv, bs, D, spec.dtype), spec.dtype, gen, device)
+    v = randn(v_pool_shape(nb, hkv, bs, D), spec.dtype, gen, device)
+    if poison:
+        poison_unused(k, v, tables, lens, bs)
+    return DecodeCase(spec, lens, tables, nb, q, k, v,
+                      {"group_start": gs, "group_prefix_len": gp})
+
+
 def slots_for_positions(tables: np.ndarray, seq_pos, block_size: int) -> np.ndarray:
     """Slot of each (seq, position) pair: physical block * BS + offset."""
     out = np.empty(len(seq_pos), dtype=np.int64)
