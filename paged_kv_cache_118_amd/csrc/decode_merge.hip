@@ -34,44 +34,11 @@ __device__ __forceinline__ void store_out(void* out, int64_t idx, float x) {
 }
 
 // Partials folded per memory round trip: each thread loads (m, l, o) of up to
-// kBatch pieces back to back, then folds them in with one rescale.
+// NB pieces back to back, then folds them in with one rescale.  Items of a
+// few pieces (the common case: an item split once or twice) take the short
+// batch, so no thread issues loads for pieces that do not exist.
+constexpr int kBatchShort = 4;
 constexpr int kBatch = 16;
-
-// slot_of(k) = slot of the item's k-th piece, k < K.  (m0, l0, o0) is a piece
-// already in hand (the new token's term, or nothing: -inf, 0, 0).
-template <typename SlotOf>
-__device__ __forceinline__ float merge_output(const DecodeArgs& a, SlotOf slot_of, int K, int R,
-                                              int r, int d, float m0, float l0, float o0) {
-  const int D = a.head_dim;
-  const int od = ((d >> 4) * 4 + ((d & 15) >> 2)) * R * 4 + r * 4 + (d & 3);  // within a record
-  const int RS = part_record(R, D);
-  float M = m0, Lt = l0, acc = o0;
-  for (int k0 = 0; k0 < K; k0 += kBatch) {
-    float m[kBatch], l[kBatch], o[kBatch];
-#pragma unroll
-    for (int w = 0; w < kBatch; ++w) {
-      const bool ok = k0 + w < K;
-      const float* rec = a.ws_part + (int64_t)slot_of(ok ? k0 + w : k0) * RS;
-      m[w] = ok ? rec[R * D + r] : -INFINITY;
-      l[w] = ok ? rec[R * D + 16 + r] : 0.f;
-      o[w] = ok ? rec[od] : 0.f;
-    }
-    float Mn = M;
-#pragma unroll
-    for (int w = 0; w < kBatch; ++w) Mn = fmaxf(Mn, m[w]);
-    const float sc = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
-    Lt *= sc;
-    acc *= sc;
-#pragma unroll
-    for (int w = 0; w < kBatch; ++w) {
-      const float f = m[w] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[w] - Mn);
-      Lt += f * l[w];
-      acc += f * o[w];
-    }
-    M = Mn;
-  }
-  return acc / Lt;
-}
 
 // Running (max, sum, output) of one output element while pieces are folded in.
 struct MergeState {
@@ -80,15 +47,15 @@ struct MergeState {
 
 // Folds K pieces into st: piece k is the record at slot_of(k) of `part`, with
 // records of RR rows; this element is row r, dim d.
-template <typename SlotOf>
-__device__ __forceinline__ void fold_pieces(MergeState& st, const float* part, SlotOf slot_of,
-                                            int K, int RR, int r, int d, int D) {
+template <int NB, typename SlotOf>
+__device__ __forceinline__ void fold_batches(MergeState& st, const float* part, SlotOf slot_of,
+                                             int K, int RR, int r, int d, int D) {
   const int od = ((d >> 4) * 4 + ((d & 15) >> 2)) * RR * 4 + r * 4 + (d & 3);
   const int RS = part_record(RR, D);
-  for (int k0 = 0; k0 < K; k0 += kBatch) {
-    float m[kBatch], l[kBatch], o[kBatch];
+  for (int k0 = 0; k0 < K; k0 += NB) {
+    float m[NB], l[NB], o[NB];
 #pragma unroll
-    for (int w = 0; w < kBatch; ++w) {
+    for (int w = 0; w < NB; ++w) {
       const bool ok = k0 + w < K;
       const float* rec = part + (int64_t)slot_of(ok ? k0 + w : k0) * RS;
       m[w] = ok ? rec[RR * D + r] : -INFINITY;
@@ -97,18 +64,36 @@ __device__ __forceinline__ void fold_pieces(MergeState& st, const float* part, S
     }
     float Mn = st.M;
 #pragma unroll
-    for (int w = 0; w < kBatch; ++w) Mn = fmaxf(Mn, m[w]);
+    for (int w = 0; w < NB; ++w) Mn = fmaxf(Mn, m[w]);
     const float sc = st.M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st.M - Mn);
     st.Lt *= sc;
     st.acc *= sc;
 #pragma unroll
-    for (int w = 0; w < kBatch; ++w) {
+    for (int w = 0; w < NB; ++w) {
       const float f = m[w] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[w] - Mn);
       st.Lt += f * l[w];
       st.acc += f * o[w];
     }
     st.M = Mn;
   }
+}
+template <typename SlotOf>
+__device__ __forceinline__ void fold_pieces(MergeState& st, const float* part, SlotOf slot_of,
+                                            int K, int RR, int r, int d, int D) {
+  if (K <= kBatchShort)
+    fold_batches<kBatchShort>(st, part, slot_of, K, RR, r, d, D);
+  else
+    fold_batches<kBatch>(st, part, slot_of, K, RR, r, d, D);
+}
+
+// slot_of(k) = slot of the item's k-th piece, k < K.  (m0, l0, o0) is a piece
+// already in hand (the new token's term, or nothing: -inf, 0, 0).
+template <typename SlotOf>
+__device__ __forceinline__ float merge_output(const DecodeArgs& a, SlotOf slot_of, int K, int R,
+                                              int r, int d, float m0, float l0, float o0) {
+  MergeState st{m0, l0, o0};
+  fold_pieces(st, a.ws_part, slot_of, K, R, r, d, a.head_dim);
+  return st.acc / st.Lt;
 }
 
 template <typename TT>
@@ -144,11 +129,16 @@ __device__ __forceinline__ NewSlot new_slot(const DecodeArgs& a, int32_t blk, in
 // sequences with no earlier position (L = 1: the row is v_new) need a row
 // here.  In both, the item that owns the kv head's first q row stores the
 // token into its slot.
+// Several items share a workgroup (ipw of them, `per` threads each), except
+// when the merge adds the new token's term (it synchronises the workgroup).
 template <typename TT, bool FOLD>
-__global__ __launch_bounds__(1024) void decode_merge_kernel(DecodeArgs a, int H, int R) {
+__global__ __launch_bounds__(1024) void decode_merge_kernel(DecodeArgs a, int H, int R, int ipw) {
   using E = typename TT::raw;
   const int D = a.head_dim, B = a.num_seqs;
-  const int item = blockIdx.x;
+  const int per = blockDim.x / ipw;  // threads per item
+  const int item = blockIdx.x * ipw + threadIdx.x / per;
+  const int tid = threadIdx.x - (threadIdx.x / per) * per;
+  if (item >= B * H) return;
   const int b = item / H, h = item - b * H;
   const int* pre = a.ws_pre;
   const int64_t orow0 = ((int64_t)b * a.num_q_heads + (int64_t)h * R) * D;
@@ -162,22 +152,22 @@ __global__ __launch_bounds__(1024) void decode_merge_kernel(DecodeArgs a, int H,
   const int n = (pre[b + 1] - pre[b]) / H;
   const int L = FOLD ? clamp_len(a.context_lens[b], a.len_cap) : 0;
   E kx = 0, vx = 0;
-  const int td = threadIdx.x < D ? threadIdx.x : 0;
+  const int td = tid < D ? tid : 0;
   if constexpr (FOLD) {
     kx = reinterpret_cast<const E*>(a.k_new)[nrow + td];
     vx = reinterpret_cast<const E*>(a.v_new)[nrow + td];
   }
   if (FOLD ? L == 0 : n == 0) {  // empty sequence: zero rows
-    for (int t = threadIdx.x; t < total; t += blockDim.x) store_out<TT>(a.out, orow0 + t, 0.f);
+    for (int t = tid; t < total; t += per) store_out<TT>(a.out, orow0 + t, 0.f);
     return;
   }
   // second round: the new token's block, and the partials (below)
-  const bool stores = FOLD && (R > 1 || h % G == 0) && threadIdx.x < D;
+  const bool stores = FOLD && (R > 1 || h % G == 0) && tid < D;
   const int32_t blk =
       stores ? a.block_tables[(int64_t)b * a.max_blocks_per_seq + (L - 1) / a.block_size] : -1;
   auto store_token = [&]() {
     if (!stores) return;
-    const NewSlot ns = new_slot(a, blk, g, L, threadIdx.x, TT::bytes);
+    const NewSlot ns = new_slot(a, blk, g, L, tid, TT::bytes);
     if (ns.k < 0) return;
     // non-temporal: these scattered pieces of lines are not read again here
     // (measured: the step's token stores 6 us cheaper than plain stores)
@@ -203,7 +193,7 @@ __global__ __launch_bounds__(1024) void decode_merge_kernel(DecodeArgs a, int H,
     // the pieces hold every position; a sequence of one (FOLD, n = 0) is
     // its new token alone: weight 1, row v_new
     const bool only_new = FOLD && n == 0;
-    for (int t = threadIdx.x; t < total; t += blockDim.x) {
+    for (int t = tid; t < total; t += per) {
       const int r = t / D, d = t - r * D;
       store_out<TT>(a.out, orow0 + t,
                     merge_output(a, slot_of, K, R, r, d, only_new ? 0.f : -INFINITY,
@@ -239,9 +229,13 @@ __global__ __launch_bounds__(1024) void decode_merge_kernel(DecodeArgs a, int H,
 // share one denominator after rescaling to the common maximum (the Z / o
 // equations of wq-win.github.io "079 | vLLM 与 PagedAttention", section 二).
 template <typename TT>
-__global__ __launch_bounds__(1024) void cascade_merge_kernel(DecodeArgs a, int H, int R) {
+__global__ __launch_bounds__(1024) void cascade_merge_kernel(DecodeArgs a, int H, int R,
+                                                             int ipw) {
   const int D = a.head_dim, B = a.num_seqs, NG = a.num_groups;
-  const int item = blockIdx.x;
+  const int per = blockDim.x / ipw;  // threads per item
+  const int item = blockIdx.x * ipw + threadIdx.x / per;
+  const int tid = threadIdx.x - (threadIdx.x / per) * per;
+  if (item >= B * H) return;
   const int b = item / H, h = item - b * H;
   const int Gq = a.num_q_heads / a.num_kv_heads;
   const int kvh = R == 1 ? h / Gq : h;
@@ -254,7 +248,7 @@ __global__ __launch_bounds__(1024) void cascade_merge_kernel(DecodeArgs a, int H
   const int64_t orow0 = ((int64_t)b * a.num_q_heads + (int64_t)h * R) * D;
   const int total = R * D;
   if (n == 0 && np == 0) {  // empty sequence: zero rows
-    for (int t = threadIdx.x; t < total; t += blockDim.x) store_out<TT>(a.out, orow0 + t, 0.f);
+    for (int t = tid; t < total; t += per) store_out<TT>(a.out, orow0 + t, 0.f);
     return;
   }
   int F = 0, K = 0;
@@ -274,7 +268,7 @@ __global__ __launch_bounds__(1024) void cascade_merge_kernel(DecodeArgs a, int H
     Kp = pp.worker_of(E - 1) - Fp + 1;
   }
   const int base = item + F, pbase = g * a.num_kv_heads + kvh + Fp;
-  for (int t = threadIdx.x; t < total; t += blockDim.x) {
+  for (int t = tid; t < total; t += per) {
     const int r = t / D, d = t - r * D;
     MergeState st{-INFINITY, 0.f, 0.f};
     fold_pieces(st, a.ws_part, [base](int k) { return base + k; }, K, R, r, d, D);
@@ -310,38 +304,48 @@ __global__ __launch_bounds__(256) void store_new_tokens_kernel(DecodeArgs a) {
 
 }  // namespace
 
+namespace {
+// Threads per item (a multiple of 64, at most 1024) and items per workgroup
+// (up to 512 threads per workgroup; one item where the workgroup syncs).
+void merge_shape(int outputs, bool single, int* per, int* ipw) {
+  *per = outputs >= 1024 ? 1024 : (outputs + 63) / 64 * 64;
+  *ipw = single ? 1 : (*per <= 256 ? 512 / *per : 1);
+}
+}  // namespace
+
 hipError_t launch_decode_merge(const DecodeArgs& a, pa_dtype dt, int items_per_seq,
                                hipStream_t s) {
   if (a.num_seqs == 0 || !a.split) return hipSuccess;
   const int R = a.num_q_heads / items_per_seq;
-  const int outputs = R * a.head_dim;
-  const int threads = outputs >= 1024 ? 1024 : (outputs + 63) / 64 * 64;
-  dim3 grid(a.num_seqs * items_per_seq);
   const bool fold = a.k_new != nullptr;
+  int per, ipw;
+  merge_shape(R * a.head_dim, fold && a.fold_in_merge, &per, &ipw);
+  const int items = a.num_seqs * items_per_seq;
+  dim3 grid((items + ipw - 1) / ipw), block(per * ipw);
   switch (dt) {
     case PA_F32:
       if (fold)
-        hipLaunchKernelGGL((decode_merge_kernel<F32, true>), grid, dim3(threads), 0, s, a,
-                           items_per_seq, R);
+        hipLaunchKernelGGL((decode_merge_kernel<F32, true>), grid, block, 0, s, a, items_per_seq,
+                           R, ipw);
       else
-        hipLaunchKernelGGL((decode_merge_kernel<F32, false>), grid, dim3(threads), 0, s, a,
-                           items_per_seq, R);
+        hipLaunchKernelGGL((decode_merge_kernel<F32, false>), grid, block, 0, s, a, items_per_seq,
+                           R, ipw);
       break;
     case PA_F16:
       if (fold)
-        hipLaunchKernelGGL((decode_merge_kernel<F16, true>), grid, dim3(threads), 0, s, a,
-                           items_per_seq, R);
+        hipLaunchKernelGGL((decode_merge_kernel<F16, true>), grid, block, 0, s, a, items_per_seq,
+                           R, ipw);
       else
-        hipLaunchKernelGGL((decode_merge_kernel<F16, false>), grid, dim3(threads), 0, s, a,
-                           items_per_seq, R);
+        hipLaunchKernelGGL((decode_merge_kernel<F16, false>), grid, block, 0, s, a, items_per_seq,
+                           R, ipw);
       break;
     case PA_BF16:
       if (fold)
-        hipLaunchKernelGGL((decode_merge_kernel<BF16, true>), grid, dim3(threads), 0, s, a,
-                           items_per_seq, R);
+        hipLaunchKernelGGL((decode_merge_kernel<BF16, true>), grid, block, 0, s, a,
+                           items_per_seq, R, ipw);
       else
-        hipLaunchKernelGGL((decode_merge_kernel<BF16, false>), grid, dim3(threads), 0, s, a,
-                           items_per_seq, R);
+        hipLaunchKernelGGL((decode_merge_kernel<BF16, false>), grid, block, 0, s, a,
+                           items_per_seq, R, ipw);
       break;
   }
   return hipGetLastError();
@@ -351,19 +355,19 @@ hipError_t launch_cascade_merge(const DecodeArgs& a, pa_dtype dt, int items_per_
                                 hipStream_t s) {
   if (a.num_seqs == 0) return hipSuccess;
   const int R = a.num_q_heads / items_per_seq;
-  const int outputs = R * a.head_dim;
-  const int threads = outputs >= 1024 ? 1024 : (outputs + 63) / 64 * 64;
-  dim3 grid(a.num_seqs * items_per_seq);
+  int per, ipw;
+  merge_shape(R * a.head_dim, false, &per, &ipw);
+  const int items = a.num_seqs * items_per_seq;
+  dim3 grid((items + ipw - 1) / ipw), block(per * ipw);
   switch (dt) {
     case PA_F32:
-      hipLaunchKernelGGL(cascade_merge_kernel<F32>, grid, dim3(threads), 0, s, a, items_per_seq, R);
+      hipLaunchKernelGGL(cascade_merge_kernel<F32>, grid, block, 0, s, a, items_per_seq, R, ipw);
       break;
     case PA_F16:
-      hipLaunchKernelGGL(cascade_merge_kernel<F16>, grid, dim3(threads), 0, s, a, items_per_seq, R);
+      hipLaunchKernelGGL(cascade_merge_kernel<F16>, grid, block, 0, s, a, items_per_seq, R, ipw);
       break;
     case PA_BF16:
-      hipLaunchKernelGGL(cascade_merge_kernel<BF16>, grid, dim3(threads), 0, s, a, items_per_seq,
-                         R);
+      hipLaunchKernelGGL(cascade_merge_kernel<BF16>, grid, block, 0, s, a, items_per_seq, R, ipw);
       break;
   }
   return hipGetLastError();

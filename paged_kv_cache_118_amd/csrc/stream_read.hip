@@ -12,21 +12,27 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kUnroll = 8;
 
+// Workgroup w reads chunks w, w + gridDim.x, ... of kThreads * kUnroll
+// 16-byte pieces each: within a chunk, load u of all threads is one
+// contiguous 4 KiB run, so every wavefront instruction reads whole lines and
+// a workgroup walks 32 KiB of consecutive memory per iteration.
 __global__ __launch_bounds__(kThreads) void stream_read_kernel(const uint4* __restrict__ buf,
                                                                int64_t n16, uint32_t* sink) {
   typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  constexpr int64_t kChunk = (int64_t)kThreads * kUnroll;
   uint32_t acc = 0;
-  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  for (; i + (kUnroll - 1) * stride < n16; i += kUnroll * stride) {
+  const int64_t chunks = n16 / kChunk;
+  for (int64_t c = blockIdx.x; c < chunks; c += gridDim.x) {
+    const uint4* p = buf + c * kChunk + threadIdx.x;
     u32x4_t v[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u)
-      v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(buf + i + u * stride));
+      v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p + u * kThreads));
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
-  for (; i < n16; i += stride) {
+  for (int64_t i = chunks * kChunk + (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n16;
+       i += (int64_t)gridDim.x * kThreads) {
     const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(buf + i));
     acc ^= v.x ^ v.y ^ v.z ^ v.w;
   }
