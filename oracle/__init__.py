@@ -73,15 +73,23 @@ LIB_PATH = os.path.join(_HERE, "libpa_oracle.so")
 DTYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2}
 
 
-def build(mutant: int = 0, out_path: str | None = None) -> str:
+SAN_LIB_PATH = os.path.join(_HERE, "san", "libpa_oracle_san.so")
+
+
+def build(mutant: int = 0, out_path: str | None = None, sanitize: bool = False) -> str:
     """Compile the oracle with gcc.  ``mutant > 0`` plants one known mistake
-    (mutation tests only) and must go to a separate ``out_path``."""
+    (mutation tests only) and must go to a separate ``out_path``.
+    ``sanitize`` builds under AddressSanitizer and UndefinedBehaviorSanitizer
+    (to SAN_LIB_PATH; load it with PA_ORACLE_LIB and gcc's libasan preloaded)."""
     if out_path is None:
         if mutant:
             raise ValueError("a mutant build needs its own output path")
-        out_path = LIB_PATH
+        out_path = SAN_LIB_PATH if sanitize else LIB_PATH
+    os.makedirs(os.path.dirname(out_path), exist_ok=True)
     tmp = out_path + f".tmp{os.getpid()}"
-    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
+    san = ["-fsanitize=address,undefined", "-fno-omit-frame-pointer",
+           "-fno-sanitize-recover=all", "-g"] if sanitize else []
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread", *san,
            f"-DORACLE_MUTANT={int(mutant)}", _SRC, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out_path)
@@ -224,12 +232,14 @@ _default: Oracle | None = None
 
 
 def get() -> Oracle:
-    """The oracle build; compiled with gcc if nothing is built yet."""
+    """The oracle build (PA_ORACLE_LIB, e.g. the sanitizer build, if set);
+    compiled with gcc if nothing is built yet."""
     global _default
     if _default is None:
-        if not os.path.exists(LIB_PATH):
+        path = os.environ.get("PA_ORACLE_LIB") or LIB_PATH
+        if path == LIB_PATH and not os.path.exists(LIB_PATH):
             build()
-        _default = Oracle(LIB_PATH)
+        _default = Oracle(path)
     return _default
 
 

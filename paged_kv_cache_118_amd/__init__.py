@@ -76,10 +76,16 @@ def _load():
         "pa_alloc_reset_prefix_cache": (i32, [vp]),
         "pa_prefix_block_hash": (i32, [vp, ctypes.c_uint64, vp, i32, vp]),
     }
+    # PA_ALLOC_LIB: the host allocator from another build of alloc.cpp (the
+    # sanitizer build of build.py), for CPU test runs; everything else stays
+    alloc_lib = ctypes.CDLL(os.environ["PA_ALLOC_LIB"]) if os.environ.get("PA_ALLOC_LIB") else lib
     for name, (res, args) in sig.items():
-        fn = getattr(lib, name)
+        src = alloc_lib if name.startswith(("pa_alloc_", "pa_prefix_block_hash")) else lib
+        fn = getattr(src, name)
         fn.restype = res
         fn.argtypes = args
+        if src is not lib:
+            setattr(lib, name, fn)
     return lib
 
 

@@ -67,5 +67,30 @@ def build_library(jobs: int | None = None) -> str:
     return LIB
 
 
+# Host allocator alone (alloc.cpp with sha256.h), built with g++ under
+# AddressSanitizer and UndefinedBehaviorSanitizer, for running the CPU test
+# suites against it: PA_ALLOC_LIB=<this .so> routes the binding's pa_alloc_*
+# and pa_prefix_block_hash there; the process needs gcc's libasan preloaded
+# (LD_PRELOAD=$(gcc -print-file-name=libasan.so)).  CPU only.
+SAN_LIB = os.path.join(BUILD, "san", "libpa_alloc_san.so")
+SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-omit-frame-pointer", "-fno-sanitize-recover=all",
+             "-g", "-O1"]
+
+
+def build_sanitized_alloc() -> str:
+    os.makedirs(os.path.dirname(SAN_LIB), exist_ok=True)
+    tmp = SAN_LIB + f".tmp{os.getpid()}"
+    cmd = ["g++", "-std=c++17", "-shared", "-fPIC", *SAN_FLAGS, "-I", os.path.join(ROOT, "include"),
+           "-I", CSRC, os.path.join(CSRC, "alloc.cpp"), "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"sanitizer build failed: {' '.join(cmd)}\n{r.stderr}")
+    os.replace(tmp, SAN_LIB)
+    return SAN_LIB
+
+
 if __name__ == "__main__":
-    print(build_library())
+    if "--sanitize" in sys.argv[1:]:
+        print(build_sanitized_alloc())
+    else:
+        print(build_library())
