@@ -17,8 +17,11 @@ using namespace pa;
 namespace {
 
 constexpr int kPartGranule = 256;  // fixed chunks are a multiple of this many tokens
-// A GQA group this large or larger goes to the matrix cores.
-constexpr int kMfmaMinGroup = 4;
+// Every GQA group (G >= 2) goes to the matrix cores where they support the
+// shape: the MFMA kernel reads each K/V token once per kv head, the VALU
+// kernel once per q head, and at G = 2 and 3 the MFMA kernel ran 1.9-2.8x
+// faster (bf16, D 128, block sizes 16 and 32, contexts 1-8K).
+constexpr int kMfmaMinGroup = 2;
 // The token-balanced split keeps per-sequence prefix sums in LDS.
 constexpr int kMaxSplitSeqs = 8192;
 // Workers per CU: the decode kernel's occupancy with the launch's dynamic LDS

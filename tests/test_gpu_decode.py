@@ -43,6 +43,12 @@ SMALL = {
                                               lengths=("uniform", 1, 300)),
     "gqa_g2_f16": W.GQA_LONG.with_(dtype="f16", num_seqs=3, num_q_heads=4, num_kv_heads=2,
                                    block_size=16, lengths=("uniform", 1, 1200)),
+    "gqa_g3_bf16": W.GQA_LONG.with_(num_seqs=3, num_q_heads=6, num_kv_heads=2,
+                                    lengths=("uniform", 1, 1500)),
+    # D 256 has no MFMA kernel: a GQA group on the VALU path
+    "gqa_g2_bf16_d256_valu": W.OPT13B.with_(dtype="bf16", num_seqs=4, num_q_heads=4,
+                                            num_kv_heads=2, head_dim=256,
+                                            lengths=("uniform", 1, 900)),
 }
 
 

@@ -24,7 +24,7 @@ SPECS = {  # (spec, members per group at most)
     "mha_bf16_bs16": (BASE.with_(num_q_heads=8, num_kv_heads=8), 16),
     "mha_f16_bs8": (BASE.with_(dtype="f16", num_q_heads=4, num_kv_heads=4, block_size=8), 16),
     "mha_bf16_bs32": (BASE.with_(num_q_heads=4, num_kv_heads=4, block_size=32), 16),
-    "gqa_g2_f16_valu_tail": (BASE.with_(dtype="f16", num_q_heads=8, num_kv_heads=4), 8),
+    "gqa_g2_f16_mfma_tail": (BASE.with_(dtype="f16", num_q_heads=8, num_kv_heads=4), 8),
     "gqa_g8_bf16_mfma_tail": (BASE.with_(num_q_heads=16, num_kv_heads=2, block_size=32), 2),
     "gqa_g4_bf16_d64": (BASE.with_(num_q_heads=8, num_kv_heads=2, head_dim=64), 4),
     "mha_f32_fallback": (BASE.with_(dtype="f32", num_q_heads=4, num_kv_heads=4), 16),
@@ -89,7 +89,7 @@ def test_shared_edge_lengths():
 
 
 def test_shared_deterministic_and_workspace_reuse():
-    spec, mm = SPECS["gqa_g2_f16_valu_tail"]
+    spec, mm = SPECS["gqa_g2_f16_mfma_tail"]
     sizes, pblocks, tails = layout(mm, np.random.default_rng(3))
     case = to_dev(W.make_shared_case(spec, sizes, pblocks, tails, device=DEV))
     need = pa.pa_decode_shared_workspace_bytes(len(case.lens), len(sizes), spec.num_q_heads,
