@@ -14,10 +14,40 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// Large writes (prompt chunks): one workgroup = TT = 32 consecutive tokens of
-// one kv head, 8*TT threads.  The K and V rows of the TT tokens are first
-// staged in LDS by 16-byte loads
-// running along each row (so a wavefront reads whole cache lines), then:
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// Stores that go around the L2's normal allocation: every written byte is
+// new to the pool and the kernel never reads it back.
+__device__ inline void store16_nt(char* dst, const char* lds_src) {
+  const uint4 x = *reinterpret_cast<const uint4*>(lds_src);
+  __builtin_nontemporal_store(u32x4_t{x.x, x.y, x.z, x.w}, reinterpret_cast<u32x4_t*>(dst));
+}
+
+// Large writes (prompt chunks): one workgroup = about TT consecutive tokens
+// of one kv head, 8*TT threads.  Workgroups go through the kv heads fastest
+// and through the token blocks from the last one back: neighbouring
+// workgroups read neighbouring pieces of the same token rows and write
+// neighbouring parts of the same pool blocks, and the batch's last tokens --
+// in a mixed batch the scattered decode tokens, whose one-token V slabs are
+// written element by element and take longest -- start first instead of
+// forming the kernel's tail.  (On the OPT-66B-shaped chunk write, 64 tokens
+// per workgroup in this order took 55-56 us against 65-68 us for 32 tokens
+// in token-block-major order.)
+//
+// Boundaries.  Workgroup boundary i sits at token i*TT, moved forward (at most
+// 7 tokens) past tokens whose slot continues the previous token's slot inside
+// one 8-slot run.  With a block size that is a multiple of 8, slots 8k .. 8k+7
+// of a block are one 128-byte line of each K piece run and one V slab, so a
+// run of consecutive slots is never split between two workgroups (which, on
+// different XCDs, would each write part of the same lines).  Any placement
+// would be correct; this one only saves partial-line writes.  So that no
+// load waits for the boundaries, a workgroup loads its whole window -- the
+// TT + 7 tokens from i*TT, and the slot before it -- at once and finds both
+// boundaries in LDS; rows past its end are read twice (the next workgroup
+// owns them), at most 7 of TT + 7.
+//
+// The K and V rows are staged in LDS by 16-byte loads running along each row
+// (a wavefront reads whole cache lines), then:
 //  K: the pool stores 16-byte pieces [D/X][BS][X]; piece c of a token row is
 //     one 16-byte store, threads taking tokens fastest, so consecutive slots
 //     of one block fill one contiguous run per piece.
@@ -27,6 +57,8 @@ constexpr int kThreads = 256;
 //     gathered from LDS and written as whole 16-byte pieces; the tokens of
 //     partly written slabs store their elements one by one, lanes taking
 //     tokens fastest.
+// The 16-byte stores are non-temporal: every byte is new to the pool and
+// the kernel never reads it back.
 template <int ES, int TT>
 __global__ __launch_bounds__(8 * TT) void reshape_and_cache_kernel(
     const char* __restrict__ k, const char* __restrict__ v, char* __restrict__ k_cache,
@@ -34,28 +66,32 @@ __global__ __launch_bounds__(8 * TT) void reshape_and_cache_kernel(
     int64_t k_stride, int64_t v_stride, int32_t hkv, int32_t D, int32_t bs, int64_t num_blocks) {
   using E = typename std::conditional<ES == 4, uint32_t, uint16_t>::type;
   constexpr int NT = 8 * TT;
+  constexpr int TW = TT + 7;  // window: the tokens a workgroup may own
+  static_assert(TW < NT && (NT & (NT - 1)) == 0, "a thread per window token");
   extern __shared__ __align__(16) char smem[];
   const int row_bytes = D * ES;            // a multiple of 16
   const int pitch = row_bytes + 16;        // LDS row pitch (16-byte aligned, skewed banks)
   char* sk = smem;
-  char* sv = smem + TT * pitch;
-  int64_t* sslot = reinterpret_cast<int64_t*>(smem + 2 * TT * pitch);
-  int* slead = reinterpret_cast<int*>(sslot + TT);  // token leads a fully written slab
-  int* scov = slead + TT;                          // token lies in such a slab
-  __shared__ int s_leaders[TT / 8 + 1];
-  __shared__ int s_nlead;
-  const int h = blockIdx.y;
-  const int t0 = blockIdx.x * TT;
-  const int nt = min(TT, num_tokens - t0);
+  char* sv = smem + TW * pitch;
+  int64_t* swin = reinterpret_cast<int64_t*>(smem + 2 * TW * pitch);  // slots w0-1 .. w0+TW-1
+  int* slead = reinterpret_cast<int*>(swin + TW + 1);  // token leads a fully written slab
+  int* scov = slead + TW;                              // token lies in such a slab
+  __shared__ int s_leaders[TW / 8 + 1];
+  __shared__ int s_nlead, s_t0, s_t1;
+  const int h = blockIdx.x % hkv;
+  const int w0 = ((int)gridDim.x / hkv - 1 - (int)blockIdx.x / hkv) * TT;
+  const int wn = min(TW, num_tokens - w0);  // window tokens present
   const int64_t max_slot = num_blocks * (int64_t)bs;
   const int vs = v_slab(bs);
   const int chunks = row_bytes / 16;
 
-  if (threadIdx.x < nt) sslot[threadIdx.x] = slots[t0 + threadIdx.x];
-  if (threadIdx.x == 0) s_nlead = 0;
-  for (int i = threadIdx.x; i < nt * chunks; i += NT) {  // lanes along a row
+  if (threadIdx.x <= TW) {
+    const int t = w0 - 1 + (int)threadIdx.x;
+    swin[threadIdx.x] = (t >= 0 && t < num_tokens) ? slots[t] : -1;
+  }
+  for (int i = threadIdx.x; i < wn * chunks; i += NT) {  // lanes along a row
     const int tt = i / chunks, c = i - tt * chunks;
-    const int64_t t = t0 + tt;
+    const int64_t t = w0 + tt;
     const uint4 kv = *reinterpret_cast<const uint4*>(k + (t * k_stride + (int64_t)h * D) * ES +
                                                       c * 16);
     const uint4 vv = *reinterpret_cast<const uint4*>(v + (t * v_stride + (int64_t)h * D) * ES +
@@ -64,6 +100,28 @@ __global__ __launch_bounds__(8 * TT) void reshape_and_cache_kernel(
     *reinterpret_cast<uint4*>(sv + tt * pitch + c * 16) = vv;
   }
   __syncthreads();
+  if (threadIdx.x < 64) {  // both boundaries: lanes 0-6 after w0, 8-14 after w0 + TT
+    const int lane = threadIdx.x;
+    const int j = lane & 7;
+    const int base = (lane >> 3) == 1 ? min(TT, num_tokens - w0) : 0;  // relative to w0
+    bool cont = false;
+    if (lane < 16 && j < 7 && w0 + base + j > 0 && base + j < wn) {
+      const int64_t cur = swin[base + j + 1];
+      cont = cur > 0 && cur == swin[base + j] + 1 && (cur & 7) != 0;
+    }
+    const uint64_t m = __ballot(cont);
+    if (lane == 0) {
+      s_t0 = __builtin_ctzll(~(m & 0x7f));
+      s_t1 = min(TT, num_tokens - w0) + __builtin_ctzll(~((m >> 8) & 0x7f));
+      s_nlead = 0;
+    }
+  }
+  __syncthreads();
+  const int r0 = s_t0;              // first owned window row
+  const int nt = s_t1 - r0;         // owned tokens
+  const int64_t* sslot = swin + 1 + r0;
+  const char* kr = sk + r0 * pitch;
+  const char* vr = sv + r0 * pitch;
   if (threadIdx.x < nt) {
     const int tt = threadIdx.x;
     const int64_t s0 = sslot[tt];
@@ -87,8 +145,7 @@ __global__ __launch_bounds__(8 * TT) void reshape_and_cache_kernel(
     if (slot >= 0 && slot < max_slot) {
       const int64_t blk = slot / bs;
       const int off = (int)(slot - blk * bs);
-      *reinterpret_cast<uint4*>(k_cache + (((blk * hkv + h) * chunks + c) * bs + off) * 16) =
-          *reinterpret_cast<const uint4*>(sk + tt * pitch + c * 16);
+      store16_nt(k_cache + (((blk * hkv + h) * chunks + c) * bs + off) * 16, kr + tt * pitch + c * 16);
     }
   }
   __syncthreads();
@@ -104,26 +161,28 @@ __global__ __launch_bounds__(8 * TT) void reshape_and_cache_kernel(
     const int64_t slot = sslot[tt];
     const int64_t blk = slot / bs;
     const int off = (int)(slot - blk * bs);
-    E e[16 / ES];
+    __align__(16) E e[16 / ES];
 #pragma unroll
     for (int u = 0; u < 16 / ES; ++u)
-      e[u] = *reinterpret_cast<const E*>(sv + (tt + half * (16 / ES) + u) * pitch + d * ES);
-    char* dst = v_cache + ((((blk * hkv + h) * (bs / 8) + off / 8) * D + d) * 8) * ES + half * 16;
-    *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(e);
+      e[u] = *reinterpret_cast<const E*>(vr + (tt + half * (16 / ES) + u) * pitch + d * ES);
+    store16_nt(v_cache + ((((blk * hkv + h) * (bs / 8) + off / 8) * D + d) * 8) * ES + half * 16,
+               reinterpret_cast<const char*>(e));
   }
 
-  // V, tokens of partly written slabs: element by element, tokens fastest.
-  const int tt = threadIdx.x % TT;
-  const int dgrp = threadIdx.x / TT;
+  // V, tokens of partly written slabs: element by element, lanes taking
+  // tokens (groups of TL >= nt lanes, a power of two), the NT / TL groups
+  // taking every (NT / TL)-th element.
+  const int lg = nt <= 1 ? 0 : 32 - __builtin_clz(nt - 1);  // log2 TL
+  const int tt = threadIdx.x & ((1 << lg) - 1);
   if (tt >= nt || scov[tt]) return;
   const int64_t slot = sslot[tt];
   if (slot < 0 || slot >= max_slot) return;
   const int64_t blk = slot / bs;
   const int off = (int)(slot - blk * bs);
-  E* vdst = reinterpret_cast<E*>(v_cache) + ((blk * hkv + h) * (bs / vs) + off / vs) * (int64_t)D * vs +
-            off % vs;
-  const E* src = reinterpret_cast<const E*>(sv + tt * pitch);
-  for (int d = dgrp; d < D; d += NT / TT) vdst[(int64_t)d * vs] = src[d];
+  E* vdst = reinterpret_cast<E*>(v_cache) +
+            ((blk * hkv + h) * (bs / vs) + off / vs) * (int64_t)D * vs + off % vs;
+  const E* src = reinterpret_cast<const E*>(vr + tt * pitch);
+  for (int d = threadIdx.x >> lg; d < D; d += NT >> lg) vdst[(int64_t)d * vs] = src[d];
 }
 
 // Decode-sized writes (a token or a few per sequence, scattered slots, no
@@ -165,7 +224,6 @@ __global__ __launch_bounds__(64) void reshape_and_cache_small_kernel(
     if (slot >= 0 && slot < max_slot) {
       const int64_t blk = slot / bs;
       const int off = (int)(slot - blk * bs);
-      typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
       __builtin_nontemporal_store(u32x4_t{kv.x, kv.y, kv.z, kv.w},
           reinterpret_cast<u32x4_t*>(k_cache + (((blk * hkv + h) * chunks + c) * bs + off) * 16));
     }
@@ -231,13 +289,28 @@ __global__ __launch_bounds__(kThreads) void swap_blocks_kernel(
   }
 }
 
+// LDS of one large-write workgroup: K and V rows, slots (and the one
+// before), two flags per window token.
+size_t rc_lds_bytes(int tt, int D, int es) {
+  return (size_t)(tt + 7) * (2 * (D * es + 16) + 8 + 8) + 8;
+}
+
+// The largest LDS one workgroup may take on the current device.
+size_t max_lds_per_workgroup() {
+  int dev = 0, v = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
+      v <= 0)
+    return 64 * 1024;
+  return (size_t)v;
+}
+
 template <int TT>
 void launch_rc(const void* k, const void* v, void* k_cache, void* v_cache, const int64_t* slots,
                int32_t num_tokens, int64_t k_stride, int64_t v_stride, int32_t hkv, int32_t D,
                int32_t bs, int64_t num_blocks, int es, hipStream_t s) {
-  dim3 grid((num_tokens + TT - 1) / TT, hkv);
-  // K and V rows, slots, two flags per token
-  const size_t lds = (size_t)TT * (2 * (D * es + 16) + 8 + 8);
+  dim3 grid((num_tokens + TT - 1) / TT * hkv);
+  const size_t lds = rc_lds_bytes(TT, D, es);
   if (es == 4)
     hipLaunchKernelGGL((reshape_and_cache_kernel<4, TT>), grid, dim3(8 * TT), lds, s,
                        (const char*)k, (const char*)v, (char*)k_cache, (char*)v_cache, slots,
@@ -257,8 +330,18 @@ hipError_t launch_reshape_and_cache(const void* k, const void* v, void* k_cache,
                                     hipStream_t s) {
   if (num_tokens == 0) return hipSuccess;
   if (num_tokens >= 1024) {
-    launch_rc<32>(k, v, k_cache, v_cache, slots, num_tokens, k_stride, v_stride, num_kv_heads,
-                  head_dim, block_size, num_blocks, elem_bytes, s);
+    // 64 tokens per workgroup where the LDS allows (16-bit rows, and fp32 up
+    // to D 128), else fewer
+    const size_t cap = max_lds_per_workgroup();
+    if (rc_lds_bytes(64, head_dim, elem_bytes) <= cap)
+      launch_rc<64>(k, v, k_cache, v_cache, slots, num_tokens, k_stride, v_stride, num_kv_heads,
+                    head_dim, block_size, num_blocks, elem_bytes, s);
+    else if (rc_lds_bytes(32, head_dim, elem_bytes) <= cap)
+      launch_rc<32>(k, v, k_cache, v_cache, slots, num_tokens, k_stride, v_stride, num_kv_heads,
+                    head_dim, block_size, num_blocks, elem_bytes, s);
+    else
+      launch_rc<16>(k, v, k_cache, v_cache, slots, num_tokens, k_stride, v_stride, num_kv_heads,
+                    head_dim, block_size, num_blocks, elem_bytes, s);
   } else {
     dim3 grid((num_tokens + 7) / 8, num_kv_heads);
     const size_t lds = (size_t)8 * (head_dim * elem_bytes + 4);
