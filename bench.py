@@ -74,6 +74,9 @@ def parse():
                          "SQ_INSTS_VALU_MFMA_MOPS_<dtype>, SQ_VALU_MFMA_BUSY_CYCLES and "
                          "GRBM_GUI_ACTIVE of this workload into the MFMA record stored under "
                          "profiles/")
+    ap.add_argument("--only", choices=["decode", "step"], default=None,
+                    help="only run the workload's decode call (or its whole step) warmup + "
+                         "steps times, untimed: the program that counter runs profile")
     ap.add_argument("--counters-summary", nargs=4, metavar=("FETCH", "WRITE", "CFETCH", "CWRITE"),
                     help="only summarise four rocprofv3 --pmc output folders (FETCH_SIZE and "
                          "WRITE_SIZE of this workload, then of --calib-copy-mb 1024) into the "
@@ -102,7 +105,8 @@ def kernel_sources_sha() -> str:
 
 
 def _pmc_medians(folder: str) -> dict:
-    """Median counter value per pa kernel (and the copy kernels) of one run."""
+    """Median counter value per pa kernel instance (name with its template
+    arguments; the copy kernel of the calibration run as "copy") of one run."""
     import csv
     import glob
     import re
@@ -111,25 +115,37 @@ def _pmc_medians(folder: str) -> dict:
         with open(path) as f:
             for r in csv.DictReader(f):
                 n = r["Kernel_Name"]
-                m = re.search(r"pa::\(anonymous namespace\)::(\w+)", n)
-                key = m.group(1) if m else ("copy" if "copy" in n.lower() else None)
+                m = re.search(r"pa::\(anonymous namespace\)::([^(]+)", n)
+                key = m.group(1).strip() if m else ("copy" if "copy" in n.lower() else None)
                 if key:
                     vals.setdefault(key, []).append(float(r["Counter_Value"]))
     return {k: float(np.median(v)) for k, v in vals.items()}
 
 
+def _is_decode_kernel(name: str) -> bool:
+    return name.startswith("decode_") or name.startswith("cascade_merge")
+
+
 def counters_summary(args) -> dict:
+    """Traffic record of one workload's pa_decode (pa_decode_shared for a
+    sharing batch) call, from counter runs of ``--only decode``: every decode
+    kernel instance of the run belongs to that call.  Other pa kernels of
+    the runs (a ``--only step`` run's cache writes) are listed apart."""
     fetch, write, cfetch, cwrite = (_pmc_medians(d) for d in args.counters_summary)
     copy_kib = 1024 * 1024  # --calib-copy-mb 1024: 1 GiB read and 1 GiB written
     f_scale = copy_kib / cfetch["copy"]
     w_scale = copy_kib / cwrite["copy"]
-    kernels = [k for k in fetch if k.startswith("decode_")]
-    per = {k: {"fetch_bytes": round(fetch[k] * f_scale * 1024),
-               "write_bytes": round(write.get(k, 0.0) * w_scale * 1024)} for k in kernels}
+
+    def scaled(k):
+        return {"fetch_bytes": round(fetch.get(k, 0.0) * f_scale * 1024),
+                "write_bytes": round(write.get(k, 0.0) * w_scale * 1024)}
+    names = sorted(set(fetch) | set(write))
+    per = {k: scaled(k) for k in names if _is_decode_kernel(k)}
+    other = {k: scaled(k) for k in names if k != "copy" and not _is_decode_kernel(k)}
     return {"workload": args.workload, "partition": args.partition,
             "sources_sha256": kernel_sources_sha(),
             "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
-            "kernels": per,
+            "kernels": per, "other_kernels": other,
             "bytes_per_call": sum(v["fetch_bytes"] + v["write_bytes"] for v in per.values())}
 
 
@@ -367,7 +383,9 @@ class Workload:
         self.decode_alg_bytes = (self.kv_read_bytes + 2 * q_bytes + self.tables.nbytes +
                                  self.lens.nbytes)
         self.decode_seqs = B
-        self.roofline_kernel = "pa_decode call (decode kernel + merge kernel)"
+        self.roofline_kernel = ("pa_decode_shared call (tail pass + prefix pass + cascade merge)"
+                                if self.groups is not None else
+                                "pa_decode call (decode kernel + merge kernel)")
         per_step = self.kv_read_bytes + 2 * T * self._tok_bytes()
         self.replicas = self.args.replicas or max(1, int(math.ceil(2e9 / per_step)))
         gen = W.make_generator(sp.seed, dev)
@@ -924,6 +942,14 @@ def main():
     dev = torch.device("cuda:0")
     wl = build_workload(args, dev)
     torch.cuda.synchronize()
+    if args.only:
+        fn = wl.decode if args.only == "decode" else wl.step
+        for i in range(args.warmup + args.steps):
+            fn(i % wl.replicas)
+        torch.cuda.synchronize()
+        print(json.dumps({"only": args.only, "workload": args.workload,
+                          "calls": args.warmup + args.steps}), flush=True)
+        return
     if args.swap:
         swap_run(args, torch, wl)
         return
