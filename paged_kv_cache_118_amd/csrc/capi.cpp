@@ -14,6 +14,15 @@
 
 using namespace pa;
 
+int pa::device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    return 256;
+  return cus;
+}
+
 namespace {
 
 constexpr int kPartGranule = 256;  // fixed chunks are a multiple of this many tokens
@@ -74,15 +83,6 @@ bool validate_enabled() {
     v = (e && e[0] && e[0] != '0') ? 1 : 0;
   }
   return v == 1;
-}
-
-int device_cus() {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 256;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      cus <= 0)
-    return 256;
-  return cus;
 }
 
 enum class Path { kValu, kMfma, kGeneric };
@@ -178,7 +178,7 @@ CascadePlan make_cascade_plan(int num_seqs, int num_groups, int hq, int hkv, int
   c.p_off = c.tail.ws_bytes;
   c.p_pre_off = c.p_off + round_up(p_slots * part_record(kPrefixRows, head_dim) * 4, 256);
   c.grp_off = c.p_pre_off + round_up(((size_t)num_groups + 1) * 4, 256);
-  c.ws_bytes = c.grp_off + round_up((size_t)num_seqs * 4, 256);
+  c.ws_bytes = c.grp_off + round_up((size_t)num_seqs * 16, 256);  // int4 per sequence
   return c;
 }
 

@@ -152,7 +152,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeArgs a) 
     if (blockIdx.x == 0 && wv == 0) {
       export_prefixes(s_pre, s_ppre, B, C, a.ws_pre, a.ws_ppre);
       if constexpr (CASC == 1)
-        for (int j = lane; j < B; j += 64) a.ws_grp[j] = s_grp[j];
+        export_groups(a, s_grp, s_gs, B);
     }
     const int N = s_pre[B];  // empty sequences get their zero rows from the merge
     if (N == 0) return;

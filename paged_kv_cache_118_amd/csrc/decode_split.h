@@ -282,6 +282,20 @@ __device__ __forceinline__ bool segment_starts(const Cursor& c, int j) {
   return j == 0 || c.k == 0;
 }
 
+// For the cascade merge, per sequence j four ints at ws_grp + 4 j: its group
+// g, the group's first member, and the group's range [pws_pre[g],
+// pws_pre[g + 1]) of prefix-pass steps (exported by the prefix pass, which
+// runs before the tail pass).  One wavefront; s_grp / s_gs as the tail scan
+// and load_groups left them.
+__device__ inline void export_groups(const DecodeArgs& a, const int* s_grp, const int* s_gs,
+                                     int B) {
+  for (int j = threadIdx.x & 63; j < B; j += 64) {
+    const int g = s_grp[j];
+    *reinterpret_cast<int4*>(a.ws_grp + 4 * j) =
+        make_int4(g, min(s_gs[g], B - 1), a.pws_pre[g], a.pws_pre[g + 1]);
+  }
+}
+
 // Copies the scan's prefixes to global memory for the merge kernel:
 // pre[0..B] = s_pre, ppre[0..B] = s_ppre (C > 0).  Called by one wavefront
 // after the barrier that published them.

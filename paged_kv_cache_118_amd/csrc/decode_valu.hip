@@ -244,7 +244,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
     if (blockIdx.x == 0 && wv == 0) {
       export_prefixes(s_pre, s_ppre, B, C, a.ws_pre, a.ws_ppre);
       if constexpr (CASC)
-        for (int j = lane; j < B; j += 64) a.ws_grp[j] = s_grp[j];
+        export_groups(a, s_grp, s_gs, B);
     }
     const int N = s_pre[B];  // empty sequences get their zero rows from the merge
     if (N == 0) return;

@@ -135,9 +135,10 @@ struct DecodeArgs {
   // consecutive sequences, gs[g] .. gs[g+1]-1, whose first group_prefix[g]
   // positions are the same physical blocks.  The tail pass streams every
   // sequence from its group's prefix on and exports each sequence's group
-  // (ws_grp); the prefix pass (its own split: pws_part, pws_pre,
-  // p_num_workers; records of 16 rows) reads each shared block once for the
-  // members' q rows; the merge joins both passes' partials of every row.
+  // facts (ws_grp, four ints per sequence: export_groups); the prefix pass
+  // (its own split: pws_part, pws_pre, p_num_workers; records of 16 rows)
+  // reads each shared block once for the members' q rows; the merge joins
+  // both passes' partials of every row.
   const int32_t* group_start;
   const int32_t* group_prefix;
   int32_t num_groups;
@@ -146,6 +147,9 @@ struct DecodeArgs {
   int32_t* pws_pre;
   int32_t p_num_workers;
 };
+
+// Compute units of the current device (256 if the query fails).
+int device_cus();
 
 // Rows of a prefix-pass partial record (members x q heads per kv head).
 constexpr int kPrefixRows = 16;
