@@ -67,6 +67,10 @@ def parse():
                     help="automatic prefix caching on the LLaMA-13B prefix-sharing prompts: "
                          "host admission cost, and one iteration's K/V writes + chunked "
                          "prefill with reuse vs recomputing every prompt")
+    ap.add_argument("--group-sweep", action="store_true",
+                    help="only time pa_decode over the q-head group size G = Hq / Hkv (8 kv "
+                         "heads, bf16, D 128, block size 32, 32 sequences of 4-8K tokens): "
+                         "one JSON line per G")
     ap.add_argument("--stream-probe", action="store_true",
                     help="only measure plain device read / copy bandwidth (context for peak)")
     ap.add_argument("--mfma-summary", metavar="FOLDER",
@@ -560,6 +564,46 @@ def stream_probe(torch, gib=4, reps=10):
     return res
 
 
+def group_sweep(args, torch):
+    """pa_decode of one batch shape at q-head group sizes G = 1, 2, 3, 4, 8
+    (Hkv = 8): K/V bytes per call and the back-to-back call time.  G = 1
+    runs the vector-ALU kernel, G >= 2 the matrix-core one, which reads each
+    K/V token once per kv head whatever G is, so the rate should not fall
+    with G.  Two seeded replicas alternate so that a call never rereads what
+    the previous one left in the last-level cache."""
+    import paged_kv_cache_118_amd as pa
+    import workloads as W
+    dev = torch.device("cuda:0")
+    hkv, B, lo, hi, bs = 8, 32, 4096, 8192, 32
+    for G in (1, 2, 3, 4, 8):
+        sp = W.GQA_LONG.with_(num_q_heads=G * hkv, num_kv_heads=hkv, num_seqs=B, block_size=bs,
+                              lengths=("uniform", lo, hi), partition_size=0)
+        cases = [W.make_decode_case(sp, device=dev, poison=False, seed=sp.seed + 7 * r)
+                 for r in range(2)]
+        ws = torch.empty(max(1, pa.pa_decode_workspace_bytes(B, sp.num_q_heads, hkv, sp.head_dim,
+                                                             bs, hi, 0, torch.bfloat16)),
+                         dtype=torch.uint8, device=dev)
+        out = torch.empty_like(cases[0].q)
+        tabs = [torch.from_numpy(c.tables).to(dev) for c in cases]
+        lens = [torch.from_numpy(c.lens).to(dev) for c in cases]
+
+        def call(r):
+            c = cases[r]
+            pa.pa_decode(out, c.q, c.k_cache, c.v_cache, tabs[r], lens[r], sp.scale, bs, hkv, hi,
+                         partition_size=0, workspace=ws)
+        t = time_calls(torch, call, 2)
+        kv = float(np.mean([int(c.lens.astype(np.int64).sum()) for c in cases])) * 2 * hkv * \
+            sp.head_dim * 2
+        print(json.dumps({"group": G, "q_heads": G * hkv, "kv_heads": hkv,
+                          "kernel": "decode_valu" if G == 1 else "decode_mfma",
+                          "kv_bytes_per_call": int(kv), "call_us": t,
+                          "kv_GBps": round(kv / 1e3 / t["mean_us"], 1),
+                          "frac_of_8TBps": round(kv / 1e3 / t["mean_us"] / HBM_PEAK_GBS, 4)}),
+              flush=True)
+        del cases, ws, out, tabs, lens
+        torch.cuda.empty_cache()
+
+
 def overhead_sweep(args, torch):
     """Cost of paging: the same decode (OPT-13B heads, fp16, 64 sequences of
     equal length L) over a pool where every sequence's blocks are one
@@ -933,6 +977,10 @@ def main():
 
     if args.overhead_sweep:
         overhead_sweep(args, torch)
+        return
+
+    if args.group_sweep:
+        group_sweep(args, torch)
         return
 
     if args.prefix_cache:
