@@ -1084,6 +1084,9 @@ def main():
         rec["mfma"] = mfma_record(wl, args, call["mean_us"] / 1e3)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = wl.cpu_baseline(args.cpu_seconds)
+        # the same run's decode call over the oracle, on the same bytes measure
+        rec["cpu_baseline"]["gpu_call_over_oracle"] = round(
+            wl.kv_read_bytes / 1e3 / call["mean_us"] / rec["cpu_baseline"]["value"], 1)
     if args.workload == "opt13b_decode" and not args.no_gqa:
         rec["gqa_long"] = gqa_subrecord(args, torch)
     print(json.dumps(rec), flush=True)
@@ -1180,6 +1183,7 @@ def gqa_subrecord(args, torch):
     }
     if not args.no_cpu_baseline:
         sub["cpu_baseline"] = wl.cpu_baseline(args.cpu_seconds)
+        sub["cpu_baseline"]["gpu_call_over_oracle"] = round(achieved / sub["cpu_baseline"]["value"], 1)
     del wl
     torch.cuda.empty_cache()
     return sub
