@@ -356,6 +356,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeArgs a) 
   };
 
   // Phase 2: O^T += V^T P^T, and the segment's output at its end.
+  bool seg_end = false;  // pv ended a segment; finish stores its result
   auto pv = [&](const Cursor& cu, uint4 (&vr)[MT], const uint4& pb, int nvalid, int j) {
     if (nvalid < kGroup) {  // zero V of masked tokens (their bits may be NaN)
       const int keep = min(max(nvalid - kb * 8, 0), 8);  // valid tokens of this k-group
@@ -376,7 +377,15 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeArgs a) 
     }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma(TT{}, vr[mt], pb, acc[mt]);
-    if (segment_ends(cu, j, count - 1)) {
+    seg_end = segment_ends(cu, j, count - 1);
+  };
+  // The result of a segment that pv ended -- the item's final rows or its
+  // partial record -- stored once the next group's K loads are issued: on
+  // this GPU a wavefront's stores and loads share one wait counter, and a
+  // store issued before a load has to complete before that load can be
+  // waited on.  acc and the softmax state hold until the next step begins.
+  auto finish = [&](const Cursor& cu) {
+    {
       float l_tot = l_lane + __shfl_xor(l_lane, 16);
       l_tot += __shfl_xor(l_tot, 32);
       const int64_t orow0 = (int64_t)cu.b * a.num_q_heads + (int64_t)cu.h * G;
@@ -436,6 +445,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeArgs a) 
       issue_v(c1, vB, j + 1 < count);
       pv(c0, vA, pb, nv, j);
       issue_k(c2, kA, qA, qia, j + 2 < count);
+      if (seg_end) finish(c0);
     }
     if (++j >= count) break;
     c0 = c1;
@@ -449,6 +459,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeArgs a) 
       issue_v(c1, vA, j + 1 < count);
       pv(c0, vB, pb, nv, j);
       issue_k(c2, kB, qB, qib, j + 2 < count);
+      if (seg_end) finish(c0);
     }
     if (++j >= count) break;
     c0 = c1;
