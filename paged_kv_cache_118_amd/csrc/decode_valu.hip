@@ -613,31 +613,36 @@ __global__ __launch_bounds__(64) void decode_generic_kernel(DecodeArgs a) {
 
 // Steps per batch: two while a lane's K / V / q registers of a step fit in
 // 48 VGPRs (16-bit data up to D = 128, fp32 up to D = 64), else one, so
-// that the kernel keeps at least two wavefronts per SIMD.
-template <typename TT, int D>
+// that the kernel keeps at least two wavefronts per SIMD.  The plain
+// decode of 16-bit data up to D = 128 takes three (186 VGPRs, still two
+// wavefronts per SIMD): 107.0-107.3 against 108.0 us per OPT-13B-shaped
+// call and 2636 against 2655 us on the OPT-66B-shaped batch; with the fused
+// write (242 VGPRs) and in the shared decode's tail pass three were no
+// faster.
+template <typename TT, int D, bool FOLD, bool CASC>
 constexpr int valu_batch() {
-  return D * TT::bytes <= 256 ? 2 : 1;
+  return D * TT::bytes > 256 ? 1 : (TT::bytes == 2 && !FOLD && !CASC) ? 3 : 2;
 }
 
 template <typename TT, int D>
 const void* valu_fn() {
   return reinterpret_cast<const void*>(
-      &decode_valu_kernel<TT, D, valu_batch<TT, D>(), false, false>);
+      &decode_valu_kernel<TT, D, valu_batch<TT, D, false, false>(), false, false>);
 }
 
 template <typename TT, int D>
 hipError_t launch_valu_d(const DecodeArgs& a, hipStream_t s) {
   dim3 grid((a.num_workers + kWaves - 1) / kWaves);
-  constexpr int NB = valu_batch<TT, D>();
   if (a.num_groups > 0)
-    hipLaunchKernelGGL((decode_valu_kernel<TT, D, NB, false, true>), grid, dim3(kThreads),
-                       decode_split_lds(a), s, a);
+    hipLaunchKernelGGL((decode_valu_kernel<TT, D, valu_batch<TT, D, false, true>(), false, true>),
+                       grid, dim3(kThreads), decode_split_lds(a), s, a);
   else if (a.k_new)
-    hipLaunchKernelGGL((decode_valu_kernel<TT, D, NB, true, false>), grid, dim3(kThreads),
-                       decode_split_lds(a), s, a);
+    hipLaunchKernelGGL((decode_valu_kernel<TT, D, valu_batch<TT, D, true, false>(), true, false>),
+                       grid, dim3(kThreads), decode_split_lds(a), s, a);
   else
-    hipLaunchKernelGGL((decode_valu_kernel<TT, D, NB, false, false>), grid, dim3(kThreads),
-                       decode_split_lds(a), s, a);
+    hipLaunchKernelGGL(
+        (decode_valu_kernel<TT, D, valu_batch<TT, D, false, false>(), false, false>), grid,
+        dim3(kThreads), decode_split_lds(a), s, a);
   return hipGetLastError();
 }
 
