@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gqa", action="store_true",
                     help="leave out the GQA long-context sub-record of the default run")
+    ap.add_argument("--no-share", action="store_true",
+                    help="leave out the prefix-sharing sub-record of the default run")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
@@ -1115,6 +1117,8 @@ def main():
             wl.kv_read_bytes / 1e3 / call["mean_us"] / rec["cpu_baseline"]["value"], 1)
     if args.workload == "opt13b_decode" and not args.no_gqa:
         rec["gqa_long"] = gqa_subrecord(args, torch)
+    if args.workload == "opt13b_decode" and not args.no_share:
+        rec["prefix_share"] = share_subrecord(args, torch)
     print(json.dumps(rec), flush=True)
 
 
@@ -1210,6 +1214,43 @@ def gqa_subrecord(args, torch):
     if not args.no_cpu_baseline:
         sub["cpu_baseline"] = wl.cpu_baseline(args.cpu_seconds)
         sub["cpu_baseline"]["gpu_call_over_oracle"] = round(achieved / sub["cpu_baseline"]["value"], 1)
+    del wl
+    torch.cuda.empty_cache()
+    return sub
+
+
+def share_subrecord(args, torch):
+    """The copy-on-write sharing batch in the same run (LLaMA-13B heads,
+    bf16, 256 beams in 32 groups sharing 512-token prefixes): the
+    pa_decode_shared call against the HBM roofline on the unique K/V (each
+    shared block once), beside the plain pa_decode of the same batch, and
+    the oracle on a sample."""
+    import argparse
+    a = argparse.Namespace(**vars(args))
+    a.workload, a.partition, a.replicas, a.block_size = "llama13b_prefix_share", None, 0, None
+    wl = Workload(a, torch.device("cuda:0"))
+    torch.cuda.synchronize()
+    call = time_calls(torch, wl.decode, wl.replicas, groups=10, per=5)
+    plain = time_calls(torch, wl.decode_plain, wl.replicas, groups=10, per=5)
+    achieved = wl.unique_kv_bytes / 1e3 / call["mean_us"]
+    sub = {
+        "config": wl.config,
+        "decode_call_us": call,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "frac_median_call": round(wl.unique_kv_bytes / 1e3 / call["median_us"] /
+                                               HBM_PEAK_GBS, 4),
+                     "traffic": stored_traffic("llama13b_prefix_share", None),
+                     "kernel": wl.roofline_kernel,
+                     "bytes": "unique K/V (shared prefix once)"},
+        "unique_kv_bytes_per_step": wl.unique_kv_bytes,
+        "logical_GBps_call": round(wl.kv_read_bytes / 1e3 / call["mean_us"], 1),
+        "plain_decode_call_us": plain,
+        "plain_decode_frac_unique": round(wl.unique_kv_bytes / 1e3 / plain["mean_us"] /
+                                          HBM_PEAK_GBS, 4),
+    }
+    if not args.no_cpu_baseline:
+        sub["cpu_baseline"] = wl.cpu_baseline(args.cpu_seconds)
     del wl
     torch.cuda.empty_cache()
     return sub
