@@ -49,6 +49,8 @@ def parse():
                     help="leave out the GQA long-context sub-record of the default run")
     ap.add_argument("--no-share", action="store_true",
                     help="leave out the prefix-sharing sub-record of the default run")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="leave out the chunked-prefill sub-record of the default run")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
@@ -682,6 +684,10 @@ def overhead_sweep(args, torch):
 
 
 def prefill_run(args, torch, wl):
+    print(json.dumps(prefill_record(args, torch, wl)), flush=True)
+
+
+def prefill_record(args, torch, wl):
     """Chunked-prefill attention of the 66B sweep's chunk writers: 16
     sequences x 256 query tokens, each causal over its whole context, timed as
     back-to-back pa_prefill calls on the stream (pools replicated as for the
@@ -758,7 +764,7 @@ def prefill_run(args, torch, wl):
             "how": "each call timed by HIP events right after one decode step of the "
                    "workload (its cache write and the 112 sequences' decode)"},
     }
-    print(json.dumps(rec), flush=True)
+    return rec
 
 
 def prefill_roofline(flops, kv_bytes, seconds, peak_tflops):
@@ -1119,6 +1125,8 @@ def main():
         rec["gqa_long"] = gqa_subrecord(args, torch)
     if args.workload == "opt13b_decode" and not args.no_share:
         rec["prefix_share"] = share_subrecord(args, torch)
+    if args.workload == "opt13b_decode" and not args.no_prefill:
+        rec["chunked_prefill"] = prefill_subrecord(args, torch)
     print(json.dumps(rec), flush=True)
 
 
@@ -1214,6 +1222,25 @@ def gqa_subrecord(args, torch):
     if not args.no_cpu_baseline:
         sub["cpu_baseline"] = wl.cpu_baseline(args.cpu_seconds)
         sub["cpu_baseline"]["gpu_call_over_oracle"] = round(achieved / sub["cpu_baseline"]["value"], 1)
+    del wl
+    torch.cuda.empty_cache()
+    return sub
+
+
+def prefill_subrecord(args, torch):
+    """Chunked-prefill attention of the OPT-66B-shaped chunk writers in the
+    same run (16 sequences x 256 query tokens, fp16, 72 heads, block size 16,
+    contexts up to 8K): back to back and inside the mixed step, against the
+    binding roofline (HBM at 249 flop per unique K/V byte)."""
+    import argparse
+    a = argparse.Namespace(**vars(args))
+    a.workload, a.partition, a.replicas, a.block_size = "opt66b_sweep", None, 0, None
+    a.steps, a.warmup, a.no_cpu_baseline = 20, 5, True
+    wl = Workload(a, torch.device("cuda:0"))
+    torch.cuda.synchronize()
+    rec = prefill_record(a, torch, wl)
+    sub = {k: rec[k] for k in ("value", "unit", "ms_per_call", "config", "roofline",
+                               "mfma_TFLOPs_frac", "in_mixed_step")}
     del wl
     torch.cuda.empty_cache()
     return sub
