@@ -48,3 +48,39 @@ def test_counters_summary(tmp_path):
     assert set(rec["other_kernels"]) == {"reshape_and_cache_small_kernel<2>"}
     want = (200 + 50 + 10) * 512 + (4 + 6 + 8) * 2048
     assert rec["bytes_per_call"] == want
+
+
+def test_prefill_roofline_picks_the_binding_roof():
+    """The roof of a chunked-prefill call is the longer of its matrix-core
+    time and its HBM time; the ridge is 2.5 PFLOP/s over 8 TB/s = 312.5
+    flop per byte.  The 66B chunk writers (651.6 GFLOP over 2.62 GB of K/V,
+    249 flop per byte) sit below it, so HBM binds."""
+    flops, kv, sec = 651.6e9, 2.62e9, 0.86e-3
+    r = bench.prefill_roofline(flops, kv, sec, 2500.0)
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["peak"] == 8000.0
+    assert abs(r["achieved"] - kv / sec / 1e9) < 0.01
+    assert abs(r["frac"] - kv / sec / 8e12) < 1e-4
+    # ten times the flops on the same bytes: above the ridge, the matrix cores bind
+    r = bench.prefill_roofline(10 * flops, kv, sec, 2500.0)
+    assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s" and r["peak"] == 2500.0
+    assert abs(r["frac"] - 10 * flops / sec / 2.5e15) < 1e-4
+    # exactly at the ridge both times are equal: reported against the matrix peak
+    assert bench.prefill_roofline(312.5 * kv, kv, sec, 2500.0)["bound"] == "mfma"
+
+
+def test_stored_records_follow_the_kernel_sources(tmp_path, monkeypatch):
+    """The traffic and MFMA records under profiles/ were taken with the
+    kernel sources as committed (bench.py reports them only then), and a
+    record of other sources is ignored."""
+    for wl in ("opt13b_decode", "gqa_long", "llama13b_prefix_share", "opt66b_sweep"):
+        got = bench.stored_traffic(wl, None)
+        assert isinstance(got, int) and got > 0, wl
+    assert bench.stored_mfma("gqa_long", None) > 0
+    rec = {"workload": "opt13b_decode", "partition": None, "sources_sha256": "0" * 16,
+           "bytes_per_call": 1}
+    (tmp_path / "old.md").write_text(bench.RECORD_TAG + " " + bench.json.dumps(rec) + "\n")
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    assert bench.stored_traffic("opt13b_decode", None) is None
+    rec["sources_sha256"] = bench.kernel_sources_sha()
+    (tmp_path / "old.md").write_text("`" + bench.RECORD_TAG + " " + bench.json.dumps(rec) + "`\n")
+    assert bench.stored_traffic("opt13b_decode", None) == 1
