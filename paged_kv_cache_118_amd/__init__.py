@@ -139,12 +139,26 @@ def _dev_ptr(t: torch.Tensor, name: str):
     return ctypes.c_void_p(t.data_ptr())
 
 
-def _stream(stream) -> ctypes.c_void_p:
+def _stream(stream, device=None) -> ctypes.c_void_p:
     if stream is None:
-        stream = torch.cuda.current_stream()
+        stream = torch.cuda.current_stream(device)
     if isinstance(stream, torch.cuda.Stream):
+        if device is not None and stream.device != device:
+            raise ValueError(f"stream is on {stream.device}, the tensors on {device}")
         return ctypes.c_void_p(stream.cuda_stream)
     return ctypes.c_void_p(int(stream))
+
+
+def _on_device(device, **tensors) -> None:
+    """Every given tensor lives on ``device``: libpa's kernels run there (the
+    call makes it current) and dereference these pointers there."""
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if t.device != device:
+            raise ValueError(f"{name} is on {t.device}, the call's tensors on {device}")
 
 
 def _scratch(nbytes: int, device, stream) -> torch.Tensor:
@@ -230,17 +244,23 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, block
     if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
         raise ValueError("block_tables must be [num_seqs, max_blocks], context_lens [num_seqs]")
     dt = _dtype_code(q)
+    dev = q.device
+    _on_device(dev, q=q, out=out, k_cache=k_cache, v_cache=v_cache, block_tables=block_tables,
+               context_lens=context_lens, workspace=workspace)
     ws_bytes = int(_lib.pa_decode_workspace_bytes(B, hq, num_kv_heads, D, block_size,
                                                   max_context_len, partition_size, dt))
     if ws_bytes and workspace is None:
-        workspace = _scratch(ws_bytes, q.device, stream)
+        workspace = _scratch(ws_bytes, dev, stream)
     ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(_lib.pa_decode(_dev_ptr(out, "out"), _dev_ptr(q, "q"), _dev_ptr(k_cache, "k_cache"),
-                          _dev_ptr(v_cache, "v_cache"), _dev_ptr(block_tables, "block_tables"),
-                          _dev_ptr(context_lens, "context_lens"), float(scale), block_size,
-                          num_kv_heads, B, hq, D, block_tables.shape[1], int(max_context_len),
-                          nb, dt, int(partition_size), ws_ptr, ws_len, _stream(stream)))
+    with torch.cuda.device(dev):
+        _check(_lib.pa_decode(_dev_ptr(out, "out"), _dev_ptr(q, "q"),
+                              _dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"),
+                              _dev_ptr(block_tables, "block_tables"),
+                              _dev_ptr(context_lens, "context_lens"), float(scale), block_size,
+                              num_kv_heads, B, hq, D, block_tables.shape[1],
+                              int(max_context_len), nb, dt, int(partition_size), ws_ptr, ws_len,
+                              _stream(stream, dev)))
     return out
 
 
@@ -259,13 +279,17 @@ def pa_decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens, scal
         raise ValueError("block_tables and context_lens must be int32")
     if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
         raise ValueError("block_tables must be [num_seqs, max_blocks], context_lens [num_seqs]")
-    _check(_lib.pa_decode_noalloc(_dev_ptr(out, "out"), _dev_ptr(q, "q"),
-                                  _dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"),
-                                  _dev_ptr(block_tables, "block_tables"),
-                                  _dev_ptr(context_lens, "context_lens"), float(scale),
-                                  block_size, num_kv_heads, B, hq, D, block_tables.shape[1],
-                                  int(max_context_len), nb, _dtype_code(q), int(partition_size),
-                                  _stream(stream)))
+    dev = q.device
+    _on_device(dev, q=q, out=out, k_cache=k_cache, v_cache=v_cache, block_tables=block_tables,
+               context_lens=context_lens)
+    with torch.cuda.device(dev):
+        _check(_lib.pa_decode_noalloc(_dev_ptr(out, "out"), _dev_ptr(q, "q"),
+                                      _dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"),
+                                      _dev_ptr(block_tables, "block_tables"),
+                                      _dev_ptr(context_lens, "context_lens"), float(scale),
+                                      block_size, num_kv_heads, B, hq, D, block_tables.shape[1],
+                                      int(max_context_len), nb, _dtype_code(q),
+                                      int(partition_size), _stream(stream, dev)))
     return out
 
 
@@ -301,21 +325,26 @@ def pa_decode_shared(out, q, k_cache, v_cache, block_tables, context_lens, group
             tuple(group_start.shape) != (G + 1,):
         raise ValueError("group_start must be int32 [G+1], group_prefix_len int32 [G]")
     dt = _dtype_code(q)
+    dev = q.device
+    _on_device(dev, q=q, out=out, k_cache=k_cache, v_cache=v_cache, block_tables=block_tables,
+               context_lens=context_lens, group_start=group_start,
+               group_prefix_len=group_prefix_len, workspace=workspace)
     ws_bytes = int(_lib.pa_decode_shared_workspace_bytes(B, G, hq, num_kv_heads, D, block_size,
                                                          max_context_len, dt))
     if ws_bytes and workspace is None:
-        workspace = _scratch(ws_bytes, q.device, stream)
+        workspace = _scratch(ws_bytes, dev, stream)
     ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(_lib.pa_decode_shared(_dev_ptr(out, "out"), _dev_ptr(q, "q"),
-                                 _dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"),
-                                 _dev_ptr(block_tables, "block_tables"),
-                                 _dev_ptr(context_lens, "context_lens"), float(scale), block_size,
-                                 num_kv_heads, B, hq, D, block_tables.shape[1],
-                                 int(max_context_len), nb, dt,
-                                 _dev_ptr(group_start, "group_start"),
-                                 _dev_ptr(group_prefix_len, "group_prefix_len"), G, ws_ptr,
-                                 ws_len, _stream(stream)))
+    with torch.cuda.device(dev):
+        _check(_lib.pa_decode_shared(_dev_ptr(out, "out"), _dev_ptr(q, "q"),
+                                     _dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"),
+                                     _dev_ptr(block_tables, "block_tables"),
+                                     _dev_ptr(context_lens, "context_lens"), float(scale),
+                                     block_size, num_kv_heads, B, hq, D, block_tables.shape[1],
+                                     int(max_context_len), nb, dt,
+                                     _dev_ptr(group_start, "group_start"),
+                                     _dev_ptr(group_prefix_len, "group_prefix_len"), G, ws_ptr,
+                                     ws_len, _stream(stream, dev)))
     return out
 
 
@@ -325,8 +354,12 @@ def bench_stream_read(buf, sink, workgroups, stream=None):
     device tensor of workgroups * 256 entries."""
     if sink.numel() < workgroups * 256 or sink.dtype != torch.int32 and sink.dtype != torch.uint32:
         raise ValueError("sink must hold workgroups * 256 32-bit entries")
-    _check(_lib.pa_bench_stream_read(_dev_ptr(buf, "buf"), buf.numel() * buf.element_size(),
-                                     _dev_ptr(sink, "sink"), int(workgroups), _stream(stream)))
+    dev = buf.device
+    _on_device(dev, buf=buf, sink=sink)
+    with torch.cuda.device(dev):
+        _check(_lib.pa_bench_stream_read(_dev_ptr(buf, "buf"), buf.numel() * buf.element_size(),
+                                         _dev_ptr(sink, "sink"), int(workgroups),
+                                         _stream(stream, dev)))
 
 
 def pa_decode_write(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale,
@@ -356,21 +389,25 @@ def pa_decode_write(out, q, k_new, v_new, k_cache, v_cache, block_tables, contex
     if k_new.stride(0) != v_new.stride(0):
         raise ValueError("k_new and v_new must have one sequence stride")
     dt = _dtype_code(q)
+    dev = q.device
+    _on_device(dev, q=q, out=out, k_cache=k_cache, v_cache=v_cache, block_tables=block_tables,
+               context_lens=context_lens, workspace=workspace)
     ws_bytes = int(_lib.pa_decode_workspace_bytes(B, hq, num_kv_heads, D, block_size,
                                                   max_context_len, partition_size, dt))
     if ws_bytes and workspace is None:
-        workspace = _scratch(ws_bytes, q.device, stream)
+        workspace = _scratch(ws_bytes, dev, stream)
     ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(_lib.pa_decode_write(_dev_ptr(out, "out"), _dev_ptr(q, "q"),
-                                ctypes.c_void_p(k_new.data_ptr()),
-                                ctypes.c_void_p(v_new.data_ptr()), k_new.stride(0),
-                                _dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"),
-                                _dev_ptr(block_tables, "block_tables"),
-                                _dev_ptr(context_lens, "context_lens"), float(scale), block_size,
-                                num_kv_heads, B, hq, D, block_tables.shape[1],
-                                int(max_context_len), nb, dt, int(partition_size), ws_ptr, ws_len,
-                                _stream(stream)))
+    with torch.cuda.device(dev):
+        _check(_lib.pa_decode_write(_dev_ptr(out, "out"), _dev_ptr(q, "q"),
+                                    ctypes.c_void_p(k_new.data_ptr()),
+                                    ctypes.c_void_p(v_new.data_ptr()), k_new.stride(0),
+                                    _dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"),
+                                    _dev_ptr(block_tables, "block_tables"),
+                                    _dev_ptr(context_lens, "context_lens"), float(scale),
+                                    block_size, num_kv_heads, B, hq, D, block_tables.shape[1],
+                                    int(max_context_len), nb, dt, int(partition_size), ws_ptr,
+                                    ws_len, _stream(stream, dev)))
     return out
 
 
@@ -393,12 +430,18 @@ def pa_prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start
             raise ValueError(f"{name} must be int32 of the right shape")
     if block_tables.dim() != 2 or block_tables.shape[0] != B:
         raise ValueError("block_tables must be [num_seqs, max_blocks]")
-    _check(_lib.pa_prefill(_dev_ptr(out, "out"), _dev_ptr(q, "q"), _dev_ptr(k_cache, "k_cache"),
-                           _dev_ptr(v_cache, "v_cache"), _dev_ptr(block_tables, "block_tables"),
-                           _dev_ptr(context_lens, "context_lens"),
-                           _dev_ptr(query_start, "query_start"), float(scale), block_size,
-                           num_kv_heads, B, hq, D, block_tables.shape[1], int(max_query_len),
-                           int(max_context_len), nb, _dtype_code(q), _stream(stream)))
+    dev = q.device
+    _on_device(dev, q=q, out=out, k_cache=k_cache, v_cache=v_cache, block_tables=block_tables,
+               context_lens=context_lens, query_start=query_start)
+    with torch.cuda.device(dev):
+        _check(_lib.pa_prefill(_dev_ptr(out, "out"), _dev_ptr(q, "q"),
+                               _dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"),
+                               _dev_ptr(block_tables, "block_tables"),
+                               _dev_ptr(context_lens, "context_lens"),
+                               _dev_ptr(query_start, "query_start"), float(scale), block_size,
+                               num_kv_heads, B, hq, D, block_tables.shape[1],
+                               int(max_query_len), int(max_context_len), nb, _dtype_code(q),
+                               _stream(stream, dev)))
     return out
 
 
@@ -418,12 +461,16 @@ def pa_reshape_and_cache(k, v, k_cache, v_cache, slot_mapping, block_size, strea
         if not t.is_cuda or t.device != k_cache.device:
             raise ValueError(f"{name} must be a device tensor on the pools' device")
     nb = _check_pools(k_cache, v_cache, hkv, block_size, D)
-    _check(_lib.pa_reshape_and_cache(ctypes.c_void_p(k.data_ptr()),
-                                     ctypes.c_void_p(v.data_ptr()),
-                                     _dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"),
-                                     _dev_ptr(slot_mapping, "slot_mapping"), T, k.stride(0),
-                                     v.stride(0), hkv, D, block_size, nb, _dtype_code(k_cache),
-                                     _stream(stream)))
+    dev = k_cache.device
+    _on_device(dev, k_cache=k_cache, v_cache=v_cache, slot_mapping=slot_mapping)
+    with torch.cuda.device(dev):
+        _check(_lib.pa_reshape_and_cache(ctypes.c_void_p(k.data_ptr()),
+                                         ctypes.c_void_p(v.data_ptr()),
+                                         _dev_ptr(k_cache, "k_cache"),
+                                         _dev_ptr(v_cache, "v_cache"),
+                                         _dev_ptr(slot_mapping, "slot_mapping"), T, k.stride(0),
+                                         v.stride(0), hkv, D, block_size, nb,
+                                         _dtype_code(k_cache), _stream(stream, dev)))
 
 
 def pa_copy_blocks(k_cache, v_cache, src_dst_pairs, block_size, stream=None):
@@ -435,9 +482,13 @@ def pa_copy_blocks(k_cache, v_cache, src_dst_pairs, block_size, stream=None):
         raise ValueError("v_cache must be [blocks][Hkv][BS/VS][D][VS]")
     hkv, D = v_cache.shape[1], v_cache.shape[3]
     nb = _check_pools(k_cache, v_cache, hkv, block_size, D)
-    _check(_lib.pa_copy_blocks(_dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"),
-                               _dev_ptr(src_dst_pairs, "src_dst_pairs"), src_dst_pairs.shape[0],
-                               hkv, D, block_size, nb, _dtype_code(k_cache), _stream(stream)))
+    dev = k_cache.device
+    _on_device(dev, k_cache=k_cache, v_cache=v_cache, src_dst_pairs=src_dst_pairs)
+    with torch.cuda.device(dev):
+        _check(_lib.pa_copy_blocks(_dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"),
+                                   _dev_ptr(src_dst_pairs, "src_dst_pairs"),
+                                   src_dst_pairs.shape[0], hkv, D, block_size, nb,
+                                   _dtype_code(k_cache), _stream(stream, dev)))
 
 
 def pa_swap_blocks(src_k, src_v, dst_k, dst_v, src_dst_pairs, block_size, stream=None):
@@ -458,10 +509,16 @@ def pa_swap_blocks(src_k, src_v, dst_k, dst_v, src_dst_pairs, block_size, stream
     nd = _check_pools(dst_k, dst_v, hkv, block_size, D)
     if src_k.dtype != dst_k.dtype:
         raise ValueError("source and destination pools must have one dtype")
+    # the device tensors among them share one device, where the copy runs
+    devs = {t.device for t in (src_k, src_v, dst_k, dst_v, src_dst_pairs) if t.is_cuda}
+    if len(devs) > 1:
+        raise ValueError("the device tensors must share one device")
+    dev = devs.pop() if devs else torch.device("cuda", torch.cuda.current_device())
     ptr = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
-    _check(_lib.pa_swap_blocks(ptr(src_k), ptr(src_v), ptr(dst_k), ptr(dst_v),
-                               ptr(src_dst_pairs), src_dst_pairs.shape[0], ns, nd, hkv, D,
-                               block_size, _dtype_code(src_k), _stream(stream)))
+    with torch.cuda.device(dev):
+        _check(_lib.pa_swap_blocks(ptr(src_k), ptr(src_v), ptr(dst_k), ptr(dst_v),
+                                   ptr(src_dst_pairs), src_dst_pairs.shape[0], ns, nd, hkv, D,
+                                   block_size, _dtype_code(src_k), _stream(stream, dev)))
 
 
 # ------------------------------------------------------------ allocator --

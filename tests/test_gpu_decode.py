@@ -254,6 +254,35 @@ def test_stream_argument_is_honoured():
     assert torch.equal(out, ref)
 
 
+def test_host_workspace_and_foreign_stream_refused():
+    """A workspace in host memory, or a stream of another device than the
+    tensors', is refused before anything runs (the kernels would dereference
+    the workspace on the device); the output is left untouched."""
+    import paged_kv_cache_118_amd as pa
+    spec = SMALL["opt13b_f16_bs16"]
+    case = to_dev(W.make_decode_case(spec, device=DEV))
+    sp = case.spec
+    nbytes = pa.pa_decode_workspace_bytes(len(case.lens), sp.num_q_heads, sp.num_kv_heads,
+                                          sp.head_dim, sp.block_size, case.max_context_len, 0,
+                                          case.q.dtype)
+    assert nbytes > 0
+    out = torch.full_like(case.q, 7.0)
+    args = (out, case.q, case.k_cache, case.v_cache, torch.from_numpy(case.tables).to(DEV),
+            torch.from_numpy(case.lens).to(DEV), sp.scale, sp.block_size, sp.num_kv_heads,
+            case.max_context_len)
+    with pytest.raises(ValueError):
+        pa.pa_decode(*args, workspace=torch.empty(nbytes, dtype=torch.uint8))
+
+    class OtherDeviceStream(torch.cuda.Stream):
+        @property
+        def device(self):
+            return torch.device("cuda", 1)
+    with pytest.raises(ValueError):
+        pa.pa_decode(*args, stream=OtherDeviceStream())
+    torch.cuda.synchronize()
+    assert (out == 7.0).all()
+
+
 def _decode_ws(case, part, ws):
     c = case
     sp = c.spec
