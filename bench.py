@@ -1219,6 +1219,21 @@ def gqa_subrecord(args, torch):
                      "kernel": wl.roofline_kernel},
         "mfma": mfma_record(wl, a, call["mean_us"] / 1e3),
     }
+    # the same batch with the library's default split (token-balanced shares
+    # instead of whole 512-token partitions), for comparison
+    sp = wl.spec
+    ws0 = wl.pa.pa_decode_workspace_bytes(len(wl.lens), sp.num_q_heads, sp.num_kv_heads,
+                                          sp.head_dim, sp.block_size, wl.max_ctx, 0,
+                                          wl.W.TORCH_DTYPE[sp.dtype])
+    if ws0 > wl.ws.numel():
+        wl.ws = torch.zeros(ws0, dtype=torch.uint8, device=wl.dev)
+    part, wl.part = wl.part, 0
+    call0 = time_calls(torch, wl.decode, wl.replicas, groups=10, per=5)
+    wl.part = part
+    sub["token_balanced_split"] = {
+        "decode_call_us": call0,
+        "frac": round(wl.kv_read_bytes / 1e3 / call0["mean_us"] / HBM_PEAK_GBS, 4),
+        "how": "partition_size 0: each wavefront takes an equal share of the tokens"}
     if not args.no_cpu_baseline:
         sub["cpu_baseline"] = wl.cpu_baseline(args.cpu_seconds)
         sub["cpu_baseline"]["gpu_call_over_oracle"] = round(achieved / sub["cpu_baseline"]["value"], 1)
