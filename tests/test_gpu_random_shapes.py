@@ -101,3 +101,32 @@ def test_unsupported_shapes_are_refused():
         with pytest.raises(pa.PAError) as e:
             TP.run_prefill(case, q, qs)
         assert e.value.status == -2
+
+
+def test_random_shared_prefix_groups():
+    """pa_decode_shared on seeded random group structures: 1-6 groups of up
+    to the members a 16-row prefix tile holds, prefixes of 0-40 blocks, tails
+    of 0-600 tokens (empty sequences included), every dtype and tail path;
+    against the oracle, and within 2 x TOL of the plain decode of the same
+    batch."""
+    from tests.test_gpu_shared import run_shared
+    rng = np.random.default_rng(5180)
+    for i in range(12):
+        dt, D, hkv, G, bs = _shape(rng, ["f32", "f16", "bf16"], [64, 128, 128, 256],
+                                   [8, 16, 32, 64])
+        G = min(G, 8)
+        mm = 16 // G
+        sizes = [int(rng.integers(1, mm + 1)) for _ in range(int(rng.integers(1, 7)))]
+        pblocks = [int(rng.choice([0, 1, int(rng.integers(2, 41))])) for _ in sizes]
+        tails = [0 if rng.random() < 0.1 else int(rng.integers(1, 601)) for _ in range(sum(sizes))]
+        spec = W.Spec("random", dt, hkv * G, hkv, D, bs, sum(sizes), ("fixed", ()),
+                      seed=int(rng.integers(1, 1 << 30)))
+        tag = (f"{dt} Hq {hkv * G} Hkv {hkv} D {D} BS {bs} groups {sizes} prefix blocks "
+               f"{pblocks} tails {tails}")
+        log(f"[random shared {i}] {tag}")
+        case = to_dev(W.make_shared_case(spec, sizes, pblocks, tails, device=DEV, poison=True))
+        out = run_shared(case)
+        err = max_err(out, oracle_decode(case))
+        plain = (out.double() - gpu_decode(case).double()).abs().max().item()
+        assert err <= TOL[dt], f"{tag}: max abs err {err}"
+        assert plain <= 2 * TOL[dt], f"{tag}: against pa_decode {plain}"
