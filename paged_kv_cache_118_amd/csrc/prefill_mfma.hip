@@ -112,6 +112,9 @@ constexpr float kSlack = 8.f;
 
 // Sequences up to which the workgroups take them longest context first.
 constexpr int kOrderSeqs = 64;
+// Block ids of rows up to this many blocks are staged in LDS for the direct
+// loads (4 KiB per workgroup); longer rows read them through a table window.
+constexpr int kTabBlocks = 1024;
 
 // Longest query chunk from which the 32-rows-per-wavefront kernel is used.
 constexpr int kPrefill32MinRows = 64;
@@ -170,6 +173,7 @@ __global__ __launch_bounds__(64 * WV) void prefill_mfma_kernel(PrefillArgs a) {
   // buffers in one array the compiler could not tell the operand reads of
   // one from the loads in flight into the other, and waited for the loads
   __shared__ __align__(16) char lds_b[DMA ? BUFD : 16];
+  __shared__ int s_tab[DMA && NBG <= 2 ? kTabBlocks : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -343,10 +347,13 @@ __global__ __launch_bounds__(64 * WV) void prefill_mfma_kernel(PrefillArgs a) {
   // (i < D / 16) fills pieces 2 i and 2 i + 1 (lane: piece 2 i + lane / 32,
   // key krow(lane % 32)), a V load instruction iv 64 rows of slab
   // iv / (D / 64).
-  auto dma = [&](int grp, char* buf) {
+  // TAB: the block ids come from the row staged in s_tab (no window check in
+  // the loop: 2% fewer cycles on the 66B chunk writers), else from the window
+  auto dma = [&](int grp, char* buf, auto tab) {
+    constexpr bool TAB = decltype(tab)::value;
     const int tok = grp * kKeys;
-    const int lb0 = BSC ? tok / BSC : tok / bs;
-    if (lb0 < tw.base || lb0 + NBG > tw.base + 64)
+    const int lb0 = tok / (BSC ? BSC : bs);
+    if (!TAB && (lb0 < tw.base || lb0 + NBG > tw.base + 64))
       tw.load(trow, a.max_blocks_per_seq, a.num_blocks, lb0, lane);
     const uint32_t o0 = (uint32_t)(tok - lb0 * bs);
     const uint32_t lim = (uint32_t)(last_wg - tok);
@@ -354,7 +361,7 @@ __global__ __launch_bounds__(64 * WV) void prefill_mfma_kernel(PrefillArgs a) {
     const char* vblk[NBG];
 #pragma unroll
     for (int q = 0; q < NBG; ++q) {
-      const int64_t ph = tw.get(lb0 + q);
+      const int64_t ph = TAB ? __builtin_amdgcn_readfirstlane(s_tab[lb0 + q]) : tw.get(lb0 + q);
       kblk[q] = kbase + ph * kblock + khead;
       vblk[q] = vbase + ph * vblock + vhead;
     }
@@ -581,17 +588,38 @@ __global__ __launch_bounds__(64 * WV) void prefill_mfma_kernel(PrefillArgs a) {
     // this wavefront waits for its own, the barrier for everyone's (and for
     // every wavefront to be done with group g - 1, whose buffer the loads of
     // group g + 1 then overwrite)
-    auto step = [&](int grp, char* cur, char* nxt) {
-      __builtin_amdgcn_s_waitcnt(kVmcntZero);
-      __syncthreads();
-      if (grp + 1 < ngroups) dma(grp + 1, nxt);
-      if (nrows > 0 && grp * kKeys <= last) compute32(grp, cur);
+    auto run = [&](auto tab) {
+      auto step = [&](int grp, char* cur, char* nxt) {
+        __builtin_amdgcn_s_waitcnt(kVmcntZero);
+        __syncthreads();
+        if (grp + 1 < ngroups) dma(grp + 1, nxt, tab);
+        if (nrows > 0 && grp * kKeys <= last) compute32(grp, cur);
+      };
+      dma(0, lds, tab);
+      for (int grp = 0; grp < ngroups; grp += 2) {
+        step(grp, lds, lds_b);
+        if (grp + 1 >= ngroups) break;
+        step(grp + 1, lds_b, lds);
+      }
     };
-    dma(0, lds);
-    for (int grp = 0; grp < ngroups; grp += 2) {
-      step(grp, lds, lds_b);
-      if (grp + 1 >= ngroups) break;
-      step(grp + 1, lds_b, lds);
+    // every block id a group can touch -- up to last_wg / bs, and up to
+    // NBG - 1 past it in the last group (block 0 there, as in the window)
+    // (not with four blocks per key group: the second loop took the 32-row
+    // kernel past three wavefronts' registers per SIMD)
+    const int need = last_wg / bs + 1;
+    if constexpr (NBG <= 2) {
+      if (need + NBG <= kTabBlocks) {  // the same for the whole workgroup
+        for (int j = tid; j < need + NBG; j += kThreads) {
+          const int e = (j < need && j < a.max_blocks_per_seq) ? trow[j] : 0;
+          s_tab[j] = (e < 0 || (int64_t)e >= a.num_blocks) ? 0 : e;
+        }
+        __syncthreads();
+        run(std::true_type{});
+      } else {
+        run(std::false_type{});
+      }
+    } else {
+      run(std::false_type{});
     }
   } else {
   // Group g's K/V travel HBM -> registers two groups ahead of their use

@@ -156,3 +156,19 @@ def test_prefill_any_scale(scale, rows, monkeypatch):
         bound = TOL[spec.dtype] * max(1.0, float(np.abs(want).max()))
         log(f"  max abs err {err:.3e} (bound {bound:.3e})")
         assert err <= bound
+
+
+@pytest.mark.parametrize("name,ctx", [("mha_f16_bs16", [16500, 300, 1]),
+                                      ("mha_bf16_bs32", [33000, 700])])
+def test_prefill_rows_longer_than_the_staged_table(name, ctx):
+    """Rows of more than 1,024 blocks take their block ids through the table
+    window, shorter ones from the row staged in LDS; one launch mixing both,
+    against the oracle."""
+    spec = SPECS[name]
+    ql = [40, 30, 1][:len(ctx)]
+    log(f"[prefill long rows] {name} contexts {ctx}")
+    case, q, qs = make_prefill_case(spec, ctx, ql, seed=5)
+    assert -(-max(ctx) // spec.block_size) > 1024
+    err = max_err(run_prefill(case, q, qs), oracle_prefill(case, q, qs))
+    log(f"  max abs err {err:.3e}")
+    assert err <= TOL[spec.dtype]
